@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for the addmm and conv2d workloads.
+
+This module only draws random numbers and describes workload shapes; it holds
+none of the method's arithmetic, so both the HIP path and the CPU oracle can
+be fed from it.  Everything is generated on the CPU with a
+``torch.Generator('cpu')`` seeded per case (seed 0 unless stated), in the
+draw order mat1, mat2, self (addmm) or input, weight, bias (conv), as fp32
+contiguous tensors.
+
+Distributions: ``("U", a, b)`` is uniform on [a, b) (``rand*(b-a)+a``);
+``("N", sigma)`` is normal with mean 0 (``randn*sigma``); ``("I", lo, hi)`` is
+integer-valued in [lo, hi] (used for order-independent, exact cases).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class AddmmCase:
+    name: str
+    M: int
+    K: int
+    N: int
+    mat1: tuple
+    mat2: tuple
+    self: tuple
+    self_2d: bool
+    beta: float = 1.0
+    alpha: float = 1.0
+    seed: int = 0
+    kind: str = field(default="addmm", init=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+@dataclass(frozen=True)
+class ConvCase:
+    name: str
+    B: int
+    IC: int
+    H: int
+    W: int
+    OC: int
+    KH: int
+    KW: int
+    stride: tuple
+    padding: tuple
+    dilation: tuple
+    x: tuple
+    w: tuple
+    bias: tuple | None
+    seed: int = 0
+    kind: str = field(default="conv", init=False)
+
+    def out_hw(self):
+        """Output size with floor((H + 2p - d(k-1) - 1)/s) + 1 per axis."""
+        def one(n, k, s, p, d):
+            return (n + 2 * p - d * (k - 1) - 1) // s + 1
+        return (one(self.H, self.KH, self.stride[0], self.padding[0], self.dilation[0]),
+                one(self.W, self.KW, self.stride[1], self.padding[1], self.dilation[1]))
+
+    @property
+    def gemm_mnk(self):
+        OH, OW = self.out_hw()
+        return self.OC, self.B * OH * OW, self.IC * self.KH * self.KW
+
+    @property
+    def flops(self) -> int:
+        M, N, K = self.gemm_mnk
+        return 2 * M * N * K
+
+
+U11 = ("U", -1.0, 1.0)
+U01 = ("U", 0.0, 1.0)
+
+
+def N(sigma):
+    return ("N", float(sigma))
+
+
+# The workloads: a small addmm, a transformer FFN linear (bias [N] and full
+# self [M,N]), a 7x7/s4 patch-embed stem conv, a 3x3 mid-stage conv (base,
+# dilation 2, stride 2 on 57x57) and large / ragged projection addmms.
+CASES = {c.name: c for c in [
+    AddmmCase("addmm_small_64x96x80", 64, 96, 80, U11, U11, U11, False),
+    AddmmCase("ffn_2048x768x3072_bias", 2048, 768, 3072, N(1), N(0.02), N(0.02), False),
+    AddmmCase("ffn_2048x768x3072_full_self", 2048, 768, 3072, N(1), N(0.02), N(1), True,
+              beta=0.5, alpha=2.0),
+    ConvCase("stem_conv7x7_s4_768", 1, 3, 768, 768, 128, 7, 7, (4, 4), (3, 3), (1, 1),
+             U01, N(0.05), N(0.02)),
+    ConvCase("conv3x3_56_s1", 4, 256, 56, 56, 256, 3, 3, (1, 1), (1, 1), (1, 1),
+             N(1), N(0.02), N(0.02)),
+    ConvCase("conv3x3_56_d2", 4, 256, 56, 56, 256, 3, 3, (1, 1), (2, 2), (2, 2),
+             N(1), N(0.02), N(0.02)),
+    ConvCase("conv3x3_57_s2", 4, 256, 57, 57, 256, 3, 3, (2, 2), (1, 1), (1, 1),
+             N(1), N(0.02), N(0.02)),
+    AddmmCase("up_proj_4096x1024x4096", 4096, 1024, 4096, N(1), N(0.02), N(0.02), False),
+    AddmmCase("down_proj_4096x4096x1024", 4096, 4096, 1024, N(1), N(0.02), N(0.02), False),
+    AddmmCase("ragged_577x1024x4096_full_self", 577, 1024, 4096, N(1), N(0.02), N(1), True),
+]}
+
+# Groups of cases as the workload list states them (small / FFN / stem /
+# 3x3 mid-stage / large and ragged projections).
+GROUPS = {
+    "addmm_small": ["addmm_small_64x96x80"],
+    "ffn": ["ffn_2048x768x3072_bias", "ffn_2048x768x3072_full_self"],
+    "stem": ["stem_conv7x7_s4_768"],
+    "conv3x3": ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2"],
+    "proj": ["up_proj_4096x1024x4096", "down_proj_4096x4096x1024",
+             "ragged_577x1024x4096_full_self"],
+}
+
+
+def draw(shape, dist, gen: torch.Generator) -> torch.Tensor:
+    """One fp32 CPU tensor of ``shape`` from ``dist`` using ``gen``."""
+    kind = dist[0]
+    if kind == "U":
+        lo, hi = dist[1], dist[2]
+        return torch.rand(shape, generator=gen, dtype=torch.float32) * (hi - lo) + lo
+    if kind == "N":
+        return torch.randn(shape, generator=gen, dtype=torch.float32) * dist[1]
+    if kind == "I":
+        lo, hi = int(dist[1]), int(dist[2])
+        return torch.randint(lo, hi + 1, shape, generator=gen).to(torch.float32)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def addmm_inputs(case: AddmmCase):
+    """(mat1 [M,K], mat2 [K,N], self [N] or [M,N]) as fp32 CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(case.seed)
+    mat1 = draw((case.M, case.K), case.mat1, g)
+    mat2 = draw((case.K, case.N), case.mat2, g)
+    self = draw((case.M, case.N) if case.self_2d else (case.N,), case.self, g)
+    return mat1, mat2, self
+
+
+def conv_inputs(case: ConvCase):
+    """(input [B,IC,H,W], weight [OC,IC,KH,KW], bias [OC] or None)."""
+    g = torch.Generator("cpu").manual_seed(case.seed)
+    x = draw((case.B, case.IC, case.H, case.W), case.x, g)
+    w = draw((case.OC, case.IC, case.KH, case.KW), case.w, g)
+    b = None if case.bias is None else draw((case.OC,), case.bias, g)
+    return x, w, b
+
+
+def inputs(case):
+    return addmm_inputs(case) if case.kind == "addmm" else conv_inputs(case)

@@ -1,0 +1,205 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU definition of the fp32 "bias addmm" and
+ * groups==1 conv2d-as-GEMM computations.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or helper with
+ * the HIP path.
+ *
+ * Sources (the method's definition):
+ *  - "[ExecuTorch][WebGPU] Add optimized addmm op" (pytorch/executorch PR
+ *    #20855), Solution and Implementation paragraphs: the op computes
+ *    out = beta*self + alpha*(mat1 @ mat2) with mat1 [M,K], mat2 [K,N]
+ *    row-major (mat2 read as mat2[k*N + n]), and self either broadcast from
+ *    [N] (self[c]) or a full [M,N] (self[r*N + c]).
+ *  - "et_vk conv2d: route standard (groups==1) conv through an im2col tiled
+ *    GEMM" (pytorch/executorch PR #20873), Solution and Implementation
+ *    paragraphs: groups==1 conv is a GEMM with M=OC, N=B*OH*OW, K=IC*KH*KW;
+ *    the B operand is the input sampled at ih = oh*sH - pH + kh*dH (and the
+ *    same along W), with out-of-range taps reading 0 (this is the padding);
+ *    bias is added per output channel (row) and the output is NCHW.
+ *
+ * Arithmetic: every product and sum is done in double from the fp32 inputs
+ * widened to double; the sum over k (or over the (ic,kh,kw) taps) runs in
+ * increasing index order.  Next to each result the oracle also returns
+ * sabs = sum |a*b| over the same terms, which scales the acceptance bound
+ * |out - ref| <= 4e-6 * sqrt(K) * (|alpha|*sabs + |beta*self|).
+ *
+ * Readings where the pages are silent:
+ *  - beta == 0: the self term is exactly 0 and self is not read (aten's rule
+ *    for addmm; equal to the literal formula on finite inputs).
+ *  - conv output size: OH = floor((H + 2*pH - dH*(KH-1) - 1)/sH) + 1 (same
+ *    along W); zero padding symmetric per axis; iw is the W-axis analogue of
+ *    the printed ih formula; a NULL bias means 0.
+ *  - K == 0: the sum is empty, so ref = beta*self.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* The self term of the addmm epilogue for output (i, j). */
+static double self_term(const float* self, int self_2d, float beta, int64_t i,
+                        int64_t j, int64_t N) {
+  if (beta == 0.0f) return 0.0;
+  double s = self_2d ? (double)self[i * N + j] : (double)self[j];
+  return (double)beta * s;
+}
+
+/* One addmm output element: the plain dot product over k, then the epilogue. */
+static void addmm_one(int64_t i, int64_t j, int64_t N, int64_t K,
+                      const float* mat1, const float* mat2, const float* self,
+                      int self_2d, float beta, float alpha, double* ref,
+                      double* sabs) {
+  double acc = 0.0, aabs = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double p = (double)mat1[i * K + k] * (double)mat2[k * N + j];
+    acc += p;
+    aabs += fabs(p);
+  }
+  *ref = self_term(self, self_2d, beta, i, j, N) + (double)alpha * acc;
+  *sabs = aabs;
+}
+
+/* Full addmm: ref and sabs are [M,N] row-major doubles. */
+void oracle_addmm(int64_t M, int64_t N, int64_t K, const float* mat1,
+                  const float* mat2, const float* self, int self_2d,
+                  float beta, float alpha, double* ref, double* sabs) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < N; ++j)
+      addmm_one(i, j, N, K, mat1, mat2, self, self_2d, beta, alpha,
+                &ref[i * N + j], &sabs[i * N + j]);
+}
+
+/* addmm at n sampled outputs (rows[s], cols[s]). */
+void oracle_addmm_at(int64_t M, int64_t N, int64_t K, const float* mat1,
+                     const float* mat2, const float* self, int self_2d,
+                     float beta, float alpha, int64_t n, const int64_t* rows,
+                     const int64_t* cols, double* ref, double* sabs) {
+  (void)M;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < n; ++s)
+    addmm_one(rows[s], cols[s], N, K, mat1, mat2, self, self_2d, beta, alpha,
+              &ref[s], &sabs[s]);
+}
+
+/* Output spatial size of a conv along one axis; <= 0 means no valid output. */
+int64_t oracle_conv_out_size(int64_t in, int64_t k, int64_t s, int64_t p,
+                             int64_t d) {
+  int64_t span = in + 2 * p - d * (k - 1) - 1;
+  if (span < 0 || s < 1) return 0;
+  return span / s + 1;
+}
+
+typedef struct {
+  int64_t B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
+} conv_shape;
+
+static conv_shape make_shape(int64_t B, int64_t IC, int64_t H, int64_t W,
+                             int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                             int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                             int64_t dW) {
+  conv_shape c = {B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, 0, 0};
+  c.OH = oracle_conv_out_size(H, KH, sH, pH, dH);
+  c.OW = oracle_conv_out_size(W, KW, sW, pW, dW);
+  return c;
+}
+
+/* One conv output element out[b, oc, oh, ow]: direct sum over (ic, kh, kw),
+ * taps outside the input contribute nothing (zero padding), plus bias[oc]. */
+static void conv_one(const conv_shape* c, int64_t b, int64_t oc, int64_t oh,
+                     int64_t ow, const float* x, const float* w,
+                     const float* bias, double* ref, double* sabs) {
+  double acc = 0.0, aabs = 0.0;
+  for (int64_t ic = 0; ic < c->IC; ++ic)
+    for (int64_t kh = 0; kh < c->KH; ++kh)
+      for (int64_t kw = 0; kw < c->KW; ++kw) {
+        int64_t ih = oh * c->sH - c->pH + kh * c->dH;
+        int64_t iw = ow * c->sW - c->pW + kw * c->dW;
+        if (ih < 0 || ih >= c->H || iw < 0 || iw >= c->W) continue;
+        double xv = (double)x[((b * c->IC + ic) * c->H + ih) * c->W + iw];
+        double wv = (double)w[((oc * c->IC + ic) * c->KH + kh) * c->KW + kw];
+        acc += wv * xv;
+        aabs += fabs(wv * xv);
+      }
+  *ref = (bias ? (double)bias[oc] : 0.0) + acc;
+  *sabs = aabs;
+}
+
+/* Full direct conv: ref and sabs are [B, OC, OH, OW] doubles. Returns -1 if
+ * the output would be empty. */
+int oracle_conv2d(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
+                  int64_t KH, int64_t KW, int64_t sH, int64_t sW, int64_t pH,
+                  int64_t pW, int64_t dH, int64_t dW, const float* x,
+                  const float* w, const float* bias, double* ref,
+                  double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t oc = 0; oc < OC; ++oc)
+      for (int64_t oh = 0; oh < c.OH; ++oh)
+        for (int64_t ow = 0; ow < c.OW; ++ow) {
+          int64_t o = ((b * OC + oc) * c.OH + oh) * c.OW + ow;
+          conv_one(&c, b, oc, oh, ow, x, w, bias, &ref[o], &sabs[o]);
+        }
+  return 0;
+}
+
+/* Direct conv at n sampled outputs, given as flat NCHW output indices. */
+int oracle_conv2d_at(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
+                     int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                     int64_t pH, int64_t pW, int64_t dH, int64_t dW,
+                     const float* x, const float* w, const float* bias,
+                     int64_t n, const int64_t* idx, double* ref,
+                     double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0) return -1;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < n; ++s) {
+    int64_t o = idx[s];
+    int64_t ow = o % c.OW, oh = (o / c.OW) % c.OH;
+    int64_t oc = (o / (c.OW * c.OH)) % OC, b = o / (c.OW * c.OH * OC);
+    conv_one(&c, b, oc, oh, ow, x, w, bias, &ref[s], &sabs[s]);
+  }
+  return 0;
+}
+
+/* Explicit im2col: col is [K, B*OH*OW] (double) with row kk = (ic*KH+kh)*KW+kw
+ * and column n = (b*OH+oh)*OW+ow; out-of-range taps are 0.  With this matrix
+ * the conv is W[OC,K] @ col + bias (the GEMM view of the conv page). */
+int oracle_im2col(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t KH,
+                  int64_t KW, int64_t sH, int64_t sW, int64_t pH, int64_t pW,
+                  int64_t dH, int64_t dW, const float* x, double* col) {
+  conv_shape c = make_shape(B, IC, H, W, 1, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0) return -1;
+  int64_t N = B * c.OH * c.OW;
+  for (int64_t ic = 0; ic < IC; ++ic)
+    for (int64_t kh = 0; kh < KH; ++kh)
+      for (int64_t kw = 0; kw < KW; ++kw) {
+        int64_t kk = (ic * KH + kh) * KW + kw;
+        for (int64_t b = 0; b < B; ++b)
+          for (int64_t oh = 0; oh < c.OH; ++oh)
+            for (int64_t ow = 0; ow < c.OW; ++ow) {
+              int64_t n = (b * c.OH + oh) * c.OW + ow;
+              int64_t ih = oh * sH - pH + kh * dH, iw = ow * sW - pW + kw * dW;
+              double v = 0.0;
+              if (ih >= 0 && ih < H && iw >= 0 && iw < W)
+                v = (double)x[((b * IC + ic) * H + ih) * W + iw];
+              col[kk * N + n] = v;
+            }
+      }
+  return 0;
+}

@@ -1,0 +1,414 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against facts fixed independently of its own code:
+exact rational brute force on tiny inputs, closed forms of special cases
+(identity mat2, alpha = 0, K = 1, 1x1 conv, a delta kernel), two formulations
+of the conv, linearity of the epilogue, hand-worked examples and the
+float64 CPU routines of an outside library (torch.addmm / F.conv2d).
+
+Definitions pinned:
+  addmm  -- "[ExecuTorch][WebGPU] Add optimized addmm op", Solution paragraph:
+            out = beta*self + alpha*(mat1 @ mat2), self [N] or [M,N].
+  conv2d -- "et_vk conv2d: route standard (groups==1) conv through an im2col
+            tiled GEMM", Solution/Implementation: M=OC, N=B*OH*OW,
+            K=IC*KH*KW, ih = oh*sH - pH + kh*dH, out-of-range taps read 0,
+            bias per OC, NCHW output.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from bias_addmm_im2col_amd import inputs as I
+
+U64 = 2.0 ** -53  # unit roundoff of float64
+
+
+def rand32(shape, seed, lo=-1.0, hi=1.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return (torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo).numpy()
+
+
+def int32v(shape, seed, lo=-4, hi=4):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randint(lo, hi + 1, shape, generator=g).to(torch.float32).numpy()
+
+
+# ----------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("M,K,N,self_2d,beta,alpha", [
+    (1, 1, 1, False, 1.0, 1.0),
+    (3, 5, 4, False, 1.0, 1.0),
+    (4, 7, 3, True, 0.5, 2.0),
+    (5, 2, 6, True, -1.25, 0.75),
+    (2, 8, 2, False, 0.0, 3.0),
+])
+def test_addmm_matches_exact_rationals(M, K, N, self_2d, beta, alpha):
+    """P-6: tiny addmm against exact rational arithmetic.
+
+    fp32 values are exact rationals; the true result differs from the fp64
+    oracle only by fp64 rounding: at most (K+2) roundings of size U64 times
+    the magnitude sum."""
+    a, b = rand32((M, K), 1), rand32((K, N), 2)
+    s = rand32((M, N) if self_2d else (N,), 3)
+    r = oracle.addmm(a, b, s, self_2d, beta, alpha)
+    for i in range(M):
+        for j in range(N):
+            acc = sum(Fraction(float(a[i, k])) * Fraction(float(b[k, j])) for k in range(K))
+            sv = Fraction(float(s[i, j] if self_2d else s[j]))
+            exact = Fraction(float(np.float32(beta))) * sv + Fraction(float(np.float32(alpha))) * acc
+            sabs = sum(abs(Fraction(float(a[i, k])) * Fraction(float(b[k, j]))) for k in range(K))
+            mag = abs(alpha) * float(sabs) + abs(beta * float(sv))
+            assert abs(Fraction(r.ref[i, j]) - exact) <= (K + 3) * U64 * mag + 1e-300
+            assert abs(Fraction(r.sabs[i, j]) - sabs) <= K * U64 * float(sabs) + 1e-300
+
+
+def _conv_brute(x, w, bias, stride, pad, dil):
+    """Exact conv by definition: padded input, strided/dilated taps, Fractions."""
+    B, IC, H, W = x.shape
+    OC, _, KH, KW = w.shape
+    sH, sW = stride
+    pH, pW = pad
+    dH, dW = dil
+    Hp, Wp = H + 2 * pH, W + 2 * pW
+    xp = [[[[Fraction(0)] * Wp for _ in range(Hp)] for _ in range(IC)] for _ in range(B)]
+    for b in range(B):
+        for c in range(IC):
+            for h in range(H):
+                for v in range(W):
+                    xp[b][c][h + pH][v + pW] = Fraction(float(x[b, c, h, v]))
+    OH = (Hp - dH * (KH - 1) - 1) // sH + 1
+    OW = (Wp - dW * (KW - 1) - 1) // sW + 1
+    out = {}
+    for b in range(B):
+        for o in range(OC):
+            for oh in range(OH):
+                for ow in range(OW):
+                    acc = Fraction(0) if bias is None else Fraction(float(bias[o]))
+                    for c in range(IC):
+                        for kh in range(KH):
+                            for kw in range(KW):
+                                acc += Fraction(float(w[o, c, kh, kw])) * \
+                                    xp[b][c][oh * sH + kh * dH][ow * sW + kw * dW]
+                    out[b, o, oh, ow] = acc
+    return out, (OH, OW)
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,has_bias", [
+    (1, 1, 5, 5, 1, 3, 3, (1, 1), (0, 0), (1, 1), True),
+    (2, 3, 6, 7, 2, 3, 2, (2, 1), (1, 0), (1, 2), True),
+    (1, 2, 7, 7, 3, 7, 7, (4, 4), (3, 3), (1, 1), False),
+    (1, 2, 6, 5, 2, 3, 3, (1, 2), (2, 2), (2, 2), True),
+])
+def test_conv_matches_exact_rationals(B, IC, H, W, OC, KH, KW, stride, pad, dil, has_bias):
+    """P-6: tiny direct conv against an exact computation on a zero-padded input."""
+    x = rand32((B, IC, H, W), 4)
+    w = rand32((OC, IC, KH, KW), 5)
+    bias = rand32((OC,), 6) if has_bias else None
+    r = oracle.conv2d(x, w, bias, stride, pad, dil)
+    exact, (OH, OW) = _conv_brute(x, w, bias, stride, pad, dil)
+    assert r.ref.shape == (B, OC, OH, OW)
+    K = IC * KH * KW
+    for key, e in exact.items():
+        mag = r.sabs[key] + (abs(float(bias[key[1]])) if has_bias else 0.0)
+        assert abs(Fraction(r.ref[key]) - e) <= (K + 2) * U64 * mag + 1e-300
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_identity_mat2_gives_alpha_mat1_plus_beta_self():
+    """P-1: mat2 = I (K = N) -> alpha*mat1 + beta*self, exactly in fp64."""
+    M, K = 37, 29
+    a = rand32((M, K), 7)
+    s = rand32((K,), 8)
+    eye = np.eye(K, dtype=np.float32)
+    r = oracle.addmm(a, eye, s, False, 0.5, 3.0)
+    expect = 3.0 * a.astype(np.float64) + 0.5 * s.astype(np.float64)[None, :]
+    assert np.array_equal(r.ref, expect)
+
+
+@pytest.mark.parametrize("self_2d", [False, True])
+def test_alpha_zero_gives_exactly_beta_self(self_2d):
+    """P-2: alpha = 0 -> beta*self exactly, whatever mat1 @ mat2 is."""
+    M, K, N = 9, 13, 11
+    a, b = rand32((M, K), 9), rand32((K, N), 10)
+    s = rand32((M, N) if self_2d else (N,), 11)
+    r = oracle.addmm(a, b, s, self_2d, -1.5, 0.0)
+    full = s.astype(np.float64) if self_2d else np.broadcast_to(s.astype(np.float64), (M, N))
+    assert np.array_equal(r.ref, -1.5 * full)
+
+
+def test_k1_is_outer_product():
+    """P-3: K = 1 -> beta*self + alpha * a_i * b_j (one exact product)."""
+    M, N = 17, 23
+    a, b = rand32((M, 1), 12), rand32((1, N), 13)
+    s = rand32((N,), 14)
+    r = oracle.addmm(a, b, s, False, 1.0, 2.0)
+    outer = a.astype(np.float64) * b.astype(np.float64)  # (M,1)*(1,N)
+    assert np.array_equal(r.ref, s.astype(np.float64)[None, :] + 2.0 * outer)
+    assert np.array_equal(r.sabs, np.abs(outer))
+
+
+def test_k0_is_beta_self():
+    """Empty contraction: out = beta*self, sabs = 0."""
+    s = rand32((4, 5), 15)
+    r = oracle.addmm(np.zeros((4, 0), np.float32), np.zeros((0, 5), np.float32), s, True, 2.0, 1.0)
+    assert np.array_equal(r.ref, 2.0 * s.astype(np.float64))
+    assert not r.sabs.any()
+
+
+def test_beta_zero_never_reads_self():
+    """beta = 0: the self term is exactly 0 even if self holds NaN/Inf."""
+    a, b = rand32((6, 4), 16), rand32((4, 5), 17)
+    s = np.full((5,), np.nan, np.float32)
+    s[1] = np.inf
+    r = oracle.addmm(a, b, s, False, 0.0, 1.0)
+    assert np.isfinite(r.ref).all()
+    r2 = oracle.addmm(a, b, np.zeros(5, np.float32), False, 1.0, 1.0)
+    assert np.array_equal(r.ref, r2.ref)
+
+
+def test_hand_worked_addmm():
+    """A worked example small enough to check by hand.
+
+    mat1 @ mat2 = [[1+3, 2+3], [4+6, 5+6]] = [[4, 5], [10, 11]];
+    out = [10, 20] + 2*that = [[18, 30], [30, 42]];
+    sabs = [[1+3, 2+3], [4+6, 5+6]] (all terms non-negative)."""
+    a = np.array([[1, 2, 3], [4, 5, 6]], np.float32)
+    b = np.array([[1, 0], [0, 1], [1, 1]], np.float32)
+    s = np.array([10, 20], np.float32)
+    r = oracle.addmm(a, b, s, False, 1.0, 2.0)
+    assert r.ref.tolist() == [[18.0, 30.0], [30.0, 42.0]]
+    assert r.sabs.tolist() == [[4.0, 5.0], [10.0, 11.0]]
+    r2 = oracle.addmm(a, b, np.array([[1, 2], [3, 4]], np.float32), True, -1.0, 1.0)
+    assert r2.ref.tolist() == [[3.0, 3.0], [7.0, 7.0]]
+
+
+def test_hand_worked_conv():
+    """Worked conv examples checkable by hand on x = [[1,2,3],[4,5,6],[7,8,9]].
+
+    * kernel [[1,0],[0,-1]], no padding: out[i,j] = x[i,j] - x[i+1,j+1] = -4.
+    * kernel [[1]] with padding 1 and stride 2: samples the zero-padded input
+      at rows/cols {-1, 1, 3} -> [[0,0,0],[0,5,0],[0,0,0]], plus bias 0.5.
+    * 2x2 all-ones kernel, dilation 2, padding 1: a 3x3 output whose entry
+      (oh, ow) sums the input at (oh-1 or oh+1, ow-1 or ow+1) where inside.
+    """
+    x = np.arange(1, 10, dtype=np.float32).reshape(1, 1, 3, 3)
+    k = np.array([[1, 0], [0, -1]], np.float32).reshape(1, 1, 2, 2)
+    r = oracle.conv2d(x, k, None)
+    assert r.ref.tolist() == [[[[-4.0, -4.0], [-4.0, -4.0]]]]
+    r = oracle.conv2d(x, np.ones((1, 1, 1, 1), np.float32), np.array([0.5], np.float32), 2, 1, 1)
+    assert r.ref.tolist() == [[[[0.5, 0.5, 0.5], [0.5, 5.5, 0.5], [0.5, 0.5, 0.5]]]]
+    # dilation 2, pad 1: taps at (oh-1, ow-1), (oh-1, ow+1), (oh+1, ow-1), (oh+1, ow+1)
+    # OH = (3 + 2 - 2 - 1)//1 + 1 = 3.
+    # (0,0): only (1,1) is inside -> 5.  (0,1): (1,0)=4, (1,2)=6 -> 10.
+    # (1,1): (0,0)=1,(0,2)=3,(2,0)=7,(2,2)=9 -> 20.  (2,2): (1,1) -> 5.
+    r = oracle.conv2d(x, np.ones((1, 1, 2, 2), np.float32), None, 1, 1, 2)
+    assert r.ref.tolist() == [[[[5.0, 10.0, 5.0], [10.0, 20.0, 10.0], [5.0, 10.0, 5.0]]]]
+
+
+def test_1x1_conv_is_a_matmul_per_image():
+    """P-4: a 1x1, stride-1, unpadded conv is W[OC,IC] @ x[b][IC, H*W] + bias."""
+    B, IC, H, W, OC = 3, 5, 4, 6, 7
+    x = rand32((B, IC, H, W), 18)
+    w = rand32((OC, IC, 1, 1), 19)
+    bias = rand32((OC,), 20)
+    r = oracle.conv2d(x, w, bias)
+    w2 = w.reshape(OC, IC).astype(np.float64)
+    for b in range(B):
+        mm = w2 @ x[b].reshape(IC, H * W).astype(np.float64) + bias.astype(np.float64)[:, None]
+        np.testing.assert_allclose(r.ref[b].reshape(OC, H * W), mm, rtol=1e-13, atol=1e-14)
+    # and the same numbers come out of the addmm oracle with mat1 = W, mat2 = x[b]
+    for b in range(B):
+        ra = oracle.addmm(w.reshape(OC, IC), np.ascontiguousarray(x[b].reshape(IC, H * W)),
+                          np.ascontiguousarray(np.repeat(bias[:, None], H * W, 1)), True)
+        assert np.array_equal(ra.ref, r.ref[b].reshape(OC, H * W))
+
+
+@pytest.mark.parametrize("kh0,kw0,pad,dil", [
+    (1, 1, (1, 1), (1, 1)),   # centre tap with "same" padding -> identity
+    (0, 2, (1, 1), (1, 1)),
+    (2, 0, (2, 1), (2, 1)),
+    (1, 2, (0, 3), (1, 2)),
+])
+def test_delta_kernel_shifts_input(kh0, kw0, pad, dil):
+    """P-5: W[oc,ic,kh0,kw0] = delta(oc,ic), stride 1 -> the input shifted by
+    (kh0*dH - pH, kw0*dW - pW) with zero fill, plus bias."""
+    B, C, H, W, KH, KW = 2, 3, 7, 8, 3, 3
+    x = rand32((B, C, H, W), 21)
+    w = np.zeros((C, C, KH, KW), np.float32)
+    for c in range(C):
+        w[c, c, kh0, kw0] = 1.0
+    bias = rand32((C,), 22)
+    r = oracle.conv2d(x, w, bias, 1, pad, dil)
+    OH, OW = r.ref.shape[2:]
+    dy, dx = kh0 * dil[0] - pad[0], kw0 * dil[1] - pad[1]
+    expect = np.zeros((B, C, OH, OW))
+    for oh in range(OH):
+        for ow in range(OW):
+            ih, iw = oh + dy, ow + dx
+            if 0 <= ih < H and 0 <= iw < W:
+                expect[:, :, oh, ow] = x[:, :, ih, iw]
+    expect += bias.astype(np.float64)[None, :, None, None]
+    assert np.array_equal(r.ref, expect)
+    if (kh0, kw0, pad, dil) == (1, 1, (1, 1), (1, 1)):
+        assert np.array_equal(r.ref, x.astype(np.float64) + bias.astype(np.float64)[None, :, None, None])
+
+
+@pytest.mark.parametrize("stride,pad,dil", [((1, 1), (1, 1), (1, 1)), ((2, 3), (0, 2), (2, 1)),
+                                            ((4, 4), (3, 3), (1, 1))])
+def test_direct_conv_equals_explicit_im2col_gemm(stride, pad, dil):
+    """P-8: the direct 7-loop conv == W[OC,K] @ im2col [K, B*OH*OW] + bias."""
+    B, IC, H, W, OC, KH, KW = 2, 3, 11, 10, 4, 3, 4
+    x = rand32((B, IC, H, W), 23)
+    w = rand32((OC, IC, KH, KW), 24)
+    bias = rand32((OC,), 25)
+    r = oracle.conv2d(x, w, bias, stride, pad, dil)
+    col = oracle.im2col(x, KH, KW, stride, pad, dil)
+    OH, OW = r.ref.shape[2:]
+    gemm = w.reshape(OC, -1).astype(np.float64) @ col + bias.astype(np.float64)[:, None]
+    gemm = gemm.reshape(OC, B, OH, OW).transpose(1, 0, 2, 3)
+    np.testing.assert_allclose(r.ref, gemm, rtol=1e-12, atol=1e-13)
+
+
+def test_im2col_matches_sliding_windows():
+    """The explicit im2col against numpy's sliding windows of the padded input."""
+    B, IC, H, W, KH, KW, p = 2, 3, 6, 5, 3, 2, 1
+    x = rand32((B, IC, H, W), 26)
+    col = oracle.im2col(x, KH, KW, 1, p, 1)
+    xp = np.pad(x.astype(np.float64), ((0, 0), (0, 0), (p, p), (p, p)))
+    win = np.lib.stride_tricks.sliding_window_view(xp, (KH, KW), axis=(2, 3))  # B,IC,OH,OW,KH,KW
+    expect = win.transpose(1, 4, 5, 0, 2, 3).reshape(IC * KH * KW, -1)
+    assert np.array_equal(col, expect)
+
+
+def test_epilogue_linearity():
+    """P-10: out(alpha, beta) = alpha*out(1, 0) + beta*self."""
+    M, K, N = 12, 30, 9
+    a, b, s = rand32((M, K), 27), rand32((K, N), 28), rand32((M, N), 29)
+    r10 = oracle.addmm(a, b, s, True, 0.0, 1.0)
+    r = oracle.addmm(a, b, s, True, -0.75, 2.5)
+    np.testing.assert_allclose(r.ref, 2.5 * r10.ref - 0.75 * s.astype(np.float64), rtol=1e-14, atol=1e-14)
+
+
+def test_self_broadcast_equals_repeated_rows():
+    """self [N] is the same as the full [M,N] self with every row equal."""
+    M, K, N = 8, 10, 6
+    a, b, s = rand32((M, K), 30), rand32((K, N), 31), rand32((N,), 32)
+    r1 = oracle.addmm(a, b, s, False, 0.5, 1.0)
+    r2 = oracle.addmm(a, b, np.ascontiguousarray(np.tile(s, (M, 1))), True, 0.5, 1.0)
+    assert np.array_equal(r1.ref, r2.ref)
+
+
+def test_sabs_equals_ref_for_nonnegative_terms():
+    """With non-negative operands, beta = 0, alpha = 1: ref == sabs."""
+    a = rand32((5, 40), 33, 0.0, 1.0)
+    b = rand32((40, 7), 34, 0.0, 1.0)
+    r = oracle.addmm(a, b, np.zeros(7, np.float32), False, 0.0, 1.0)
+    assert np.array_equal(r.ref, r.sabs)
+
+
+# ------------------------------------------------------- library cross-check
+
+@pytest.mark.parametrize("M,K,N,self_2d,beta,alpha", [
+    (64, 96, 80, False, 1.0, 1.0), (33, 127, 65, True, 0.5, 2.0), (1, 300, 3, False, -2.0, 0.25)])
+def test_addmm_vs_torch_float64(M, K, N, self_2d, beta, alpha):
+    """P-9: against torch.addmm in float64 on the CPU (an outside routine)."""
+    a, b = rand32((M, K), 35), rand32((K, N), 36)
+    s = rand32((M, N) if self_2d else (N,), 37)
+    r = oracle.addmm(a, b, s, self_2d, beta, alpha)
+    t = torch.addmm(torch.from_numpy(s).double(), torch.from_numpy(a).double(),
+                    torch.from_numpy(b).double(), beta=beta, alpha=alpha).numpy()
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil", [
+    (1, 3, 32, 32, 8, 7, 7, (4, 4), (3, 3), (1, 1)),
+    (2, 8, 12, 12, 6, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 8, 12, 12, 6, 3, 3, (1, 1), (2, 2), (2, 2)),
+    (2, 8, 13, 13, 6, 3, 3, (2, 2), (1, 1), (1, 1)),
+    (1, 4, 9, 11, 5, 2, 3, (3, 2), (0, 2), (2, 3)),
+])
+def test_conv_vs_torch_float64(B, IC, H, W, OC, KH, KW, stride, pad, dil):
+    """P-9: against torch.nn.functional.conv2d in float64 on the CPU."""
+    x = rand32((B, IC, H, W), 38)
+    w = rand32((OC, IC, KH, KW), 39)
+    bias = rand32((OC,), 40)
+    r = oracle.conv2d(x, w, bias, stride, pad, dil)
+    t = F.conv2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                 torch.from_numpy(bias).double(), stride, pad, dil).numpy()
+    assert r.ref.shape == t.shape
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ sampled entry
+
+def test_sampled_addmm_equals_full():
+    M, K, N = 21, 17, 19
+    a, b, s = rand32((M, K), 41), rand32((K, N), 42), rand32((M, N), 43)
+    full = oracle.addmm(a, b, s, True, 0.5, -1.0)
+    g = np.random.default_rng(0)
+    rows, cols = g.integers(0, M, 100), g.integers(0, N, 100)
+    at = oracle.addmm_at(a, b, s, True, 0.5, -1.0, rows, cols)
+    assert np.array_equal(at.ref, full.ref[rows, cols])
+    assert np.array_equal(at.sabs, full.sabs[rows, cols])
+    assert np.array_equal(at.selfabs, full.selfabs[rows, cols])
+
+
+def test_sampled_conv_equals_full():
+    x = rand32((2, 3, 9, 8), 44)
+    w = rand32((5, 3, 3, 3), 45)
+    bias = rand32((5,), 46)
+    full = oracle.conv2d(x, w, bias, (2, 1), (1, 2), (1, 2))
+    idx = np.random.default_rng(1).integers(0, full.ref.size, 200)
+    at = oracle.conv2d_at(x, w, bias, (2, 1), (1, 2), (1, 2), idx)
+    assert np.array_equal(at.ref, full.ref.reshape(-1)[idx])
+    assert np.array_equal(at.sabs, full.sabs.reshape(-1)[idx])
+
+
+# --------------------------------------------------------------- workloads
+
+def test_workload_output_sizes():
+    """The stem conv's stated output is [1,128,192,192]; the 3x3 cases give
+    56x56 (s1 p1, and d2 p2) and 29x29 (s2 p1 on 57x57)."""
+    assert oracle.conv_out_size(768, 7, 4, 3, 1) == 192
+    assert oracle.conv_out_size(56, 3, 1, 1, 1) == 56
+    assert oracle.conv_out_size(56, 3, 1, 2, 2) == 56
+    assert oracle.conv_out_size(57, 3, 2, 1, 1) == 29
+    assert oracle.conv_out_size(2, 5, 1, 0, 1) == 0  # kernel larger than input
+    for c in I.CASES.values():
+        if c.kind == "conv":
+            assert c.out_hw() == (oracle.conv_out_size(c.H, c.KH, c.stride[0], c.padding[0], c.dilation[0]),
+                                  oracle.conv_out_size(c.W, c.KW, c.stride[1], c.padding[1], c.dilation[1]))
+
+
+def test_input_generator_is_seeded_and_shaped():
+    c = I.CASES["addmm_small_64x96x80"]
+    a1, b1, s1 = I.addmm_inputs(c)
+    a2, b2, s2 = I.addmm_inputs(c)
+    assert a1.shape == (64, 96) and b1.shape == (96, 80) and s1.shape == (80,)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2) and torch.equal(s1, s2)
+    assert a1.dtype == torch.float32 and float(a1.min()) >= -1 and float(a1.max()) < 1
+    cc = I.CASES["stem_conv7x7_s4_768"]
+    x, w, b = I.conv_inputs(cc)
+    assert x.shape == (1, 3, 768, 768) and w.shape == (128, 3, 7, 7) and b.shape == (128,)
+    assert float(x.min()) >= 0.0
+
+
+def test_regression_fixture_unchanged():
+    """The stored oracle outputs (tests/golden/make_golden.py) still come out."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "oracle_regression.json")
+    g = json.load(open(path))
+    ga = g["addmm"]
+    a, b, s = (rand32(sh, sd) for sh, sd in zip([(3, 5), (5, 4), (4,)], ga["seeds"]))
+    r = oracle.addmm(a, b, s, False, ga["beta"], ga["alpha"])
+    assert r.ref.tolist() == ga["ref"] and r.sabs.tolist() == ga["sabs"]
+    gc = g["conv2d"]
+    x, w, bias = (rand32(sh, sd) for sh, sd in zip([(1, 2, 5, 5), (3, 2, 3, 3), (3,)], gc["seeds"]))
+    r = oracle.conv2d(x, w, bias, gc["stride"], gc["padding"], gc["dilation"])
+    assert r.ref.tolist() == gc["ref"] and r.sabs.tolist() == gc["sabs"]
