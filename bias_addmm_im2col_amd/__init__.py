@@ -1,0 +1,199 @@
+"""fp32 tiled GEMM with a fused epilogue for AMD MI355X (gfx950).
+
+Two operations, both computed by the hand-written HIP kernels in
+``libbaim.so`` (C ABI in include/baim.h); this package only marshals
+arguments and allocates outputs with torch:
+
+* ``addmm(self, mat1, mat2, *, beta=1, alpha=1)`` --
+  ``beta*self + alpha*(mat1 @ mat2)`` with self ``[N]`` (or ``[1,N]``) or
+  ``[M,N]`` ("[ExecuTorch][WebGPU] Add optimized addmm op", Solution).
+* ``conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1,
+  groups=1)`` -- groups==1 NCHW convolution as an implicit-im2col GEMM
+  ("et_vk conv2d: route standard (groups==1) conv through an im2col tiled
+  GEMM", Solution/Implementation).
+
+``addmm_f32`` and ``conv2d_gemm_f32`` are the same-named entry points of the
+C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
+on the same ROCm device; work is enqueued on the current torch stream.
+"""
+from __future__ import annotations
+
+from . import _capi
+
+__all__ = ["addmm", "conv2d", "addmm_f32", "conv2d_gemm_f32", "conv2d_out_hw",
+           "BaimError", "library_path"]
+
+
+class BaimError(RuntimeError):
+    """A non-OK status from libbaim.so."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_capi.STATUS_NAMES.get(status, status)}: {message}")
+
+
+class BaimValueError(BaimError, ValueError):
+    pass
+
+
+class BaimUnsupportedError(BaimError, NotImplementedError):
+    pass
+
+
+def library_path() -> str:
+    return _capi.LIB_PATH
+
+
+def _check(status: int):
+    if status == _capi.BAIM_OK:
+        return
+    msg = _capi.last_error()
+    if status == _capi.BAIM_ERR_UNSUPPORTED:
+        raise BaimUnsupportedError(status, msg)
+    if status == _capi.BAIM_ERR_LAUNCH:
+        raise BaimError(status, msg)
+    raise BaimValueError(status, msg)
+
+
+def _pair(v, name):
+    if isinstance(v, int):
+        return v, v
+    v = tuple(int(a) for a in v)
+    if len(v) != 2:
+        raise ValueError(f"{name} must be an int or a pair")
+    return v
+
+
+def _scalar(v, name) -> float:
+    # Double, Int or None accepted, None meaning 1 (the page's scalar_or).
+    if v is None:
+        return 1.0
+    if isinstance(v, bool) or not isinstance(v, (int, float)):
+        raise TypeError(f"{name} must be an int or float")
+    return float(v)
+
+
+def _dev_f32(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(dev):
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def addmm_f32(out, self, mat1, mat2, beta=1.0, alpha=1.0):
+    """out[M,N] = beta*self + alpha*(mat1 @ mat2), written into ``out``.
+
+    self is [N], [1,N] or [M,N]; it may be None when beta == 0."""
+    import torch
+    beta, alpha = _scalar(beta, "beta"), _scalar(alpha, "alpha")
+    out, mat1, mat2 = _dev_f32(out, "out"), _dev_f32(mat1, "mat1"), _dev_f32(mat2, "mat2")
+    if mat1.dim() != 2 or mat2.dim() != 2 or out.dim() != 2:
+        raise ValueError("mat1, mat2 and out must be 2-D")
+    M, K = mat1.shape
+    if mat2.shape[0] != K:
+        raise ValueError(f"mat2 must be [K={K}, N], got {list(mat2.shape)}")
+    N = mat2.shape[1]
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}], got {list(out.shape)}")
+    devs = {t.device for t in (out, mat1, mat2)}
+    self_ptr, self_2d = None, 0
+    if self is not None:
+        self = _dev_f32(self, "self")
+        devs.add(self.device)
+        if tuple(self.shape) in ((N,), (1, N)):
+            self_2d = 0
+        elif tuple(self.shape) == (M, N):
+            self_2d = 1
+        else:
+            raise ValueError(f"self must be [N], [1,N] or [M,N] with M={M}, N={N}; "
+                             f"got {list(self.shape)}")
+        self_ptr = self.data_ptr()
+    elif beta != 0.0:
+        raise ValueError("self is required unless beta == 0")
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.addmm_f32(out.data_ptr(), self_ptr, self_2d, mat1.data_ptr(),
+                             mat2.data_ptr(), M, N, K, beta, alpha, _stream(dev))
+    _check(st)
+    return out
+
+
+def addmm(self, mat1, mat2, *, beta=1, alpha=1):
+    """beta*self + alpha*(mat1 @ mat2) as a new [M,N] fp32 tensor."""
+    import torch
+    _dev_f32(mat1, "mat1")
+    _dev_f32(mat2, "mat2")
+    out = torch.empty((mat1.shape[0], mat2.shape[1]), dtype=torch.float32, device=mat1.device)
+    return addmm_f32(out, self, mat1, mat2, beta, alpha)
+
+
+def conv2d_out_hw(H, W, KH, KW, stride=1, padding=0, dilation=1):
+    (sH, sW), (pH, pW), (dH, dW) = (_pair(stride, "stride"), _pair(padding, "padding"),
+                                    _pair(dilation, "dilation"))
+    st, oh, ow = _capi.conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW)
+    _check(st)
+    return oh, ow
+
+
+def conv2d_gemm_f32(out, input, weight, bias=None, stride=1, padding=0, dilation=1, groups=1):
+    """NCHW conv2d (groups == 1) written into ``out`` [B, OC, OH, OW]."""
+    import torch
+    out, x, w = _dev_f32(out, "out"), _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4 or out.dim() != 4:
+        raise ValueError("input, weight and out must be 4-D (NCHW / OIHW)")
+    B, IC, H, W = x.shape
+    OC, ICg, KH, KW = w.shape
+    if int(groups) < 1 or ICg * int(groups) != IC:
+        raise ValueError(f"weight has {ICg} input channels per group; input has {IC}, "
+                         f"groups={groups}")
+    (sH, sW), (pH, pW), (dH, dW) = (_pair(stride, "stride"), _pair(padding, "padding"),
+                                    _pair(dilation, "dilation"))
+    bias_ptr = None
+    devs = {out.device, x.device, w.device}
+    if bias is not None:
+        bias = _dev_f32(bias, "bias")
+        if tuple(bias.shape) != (OC,):
+            raise ValueError(f"bias must be [{OC}]")
+        bias_ptr = bias.data_ptr()
+        devs.add(bias.device)
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    st, OH, OW = _capi.conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW)
+    _check(st)
+    if tuple(out.shape) != (B, OC, OH, OW):
+        raise ValueError(f"out must be [{B}, {OC}, {OH}, {OW}], got {list(out.shape)}")
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.conv2d_gemm_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
+                                   B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
+                                   int(groups), _stream(dev))
+    _check(st)
+    return out
+
+
+def conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1, groups=1):
+    """groups==1 NCHW conv2d through the implicit-im2col GEMM, new output."""
+    import torch
+    if int(groups) != 1:
+        raise BaimUnsupportedError(_capi.BAIM_ERR_UNSUPPORTED,
+                                   f"groups={groups}: only groups == 1 is routed through the GEMM")
+    x, w = _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("input and weight must be 4-D")
+    OH, OW = conv2d_out_hw(x.shape[2], x.shape[3], w.shape[2], w.shape[3], stride, padding,
+                           dilation)
+    out = torch.empty((x.shape[0], w.shape[0], OH, OW), dtype=torch.float32, device=x.device)
+    return conv2d_gemm_f32(out, x, w, bias, stride, padding, dilation, groups)

@@ -1,0 +1,79 @@
+"""ctypes view of libbaim.so: the C ABI declared in include/baim.h.
+
+Argument marshalling only.  There is no fallback: if the library is missing
+the first call raises, naming the build command.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbaim.so")
+
+BAIM_OK = 0
+BAIM_ERR_NULL = 1
+BAIM_ERR_SHAPE = 2
+BAIM_ERR_UNSUPPORTED = 3
+BAIM_ERR_TOO_LARGE = 4
+BAIM_ERR_ALIAS = 5
+BAIM_ERR_LAUNCH = 6
+
+STATUS_NAMES = {
+    0: "BAIM_OK", 1: "BAIM_ERR_NULL", 2: "BAIM_ERR_SHAPE", 3: "BAIM_ERR_UNSUPPORTED",
+    4: "BAIM_ERR_TOO_LARGE", 5: "BAIM_ERR_ALIAS", 6: "BAIM_ERR_LAUNCH",
+}
+
+# Every symbol include/baim.h declares.
+EXPORTS = ("addmm_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_last_error",
+           "baim_version")
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load libbaim.so once and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m bias_addmm_im2col_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    L = ctypes.CDLL(LIB_PATH)
+    L.addmm_f32.argtypes = [_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64,
+                            ctypes.c_float, ctypes.c_float, _vp]
+    L.addmm_f32.restype = ctypes.c_int
+    L.conv2d_gemm_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 14 + [_vp]
+    L.conv2d_gemm_f32.restype = ctypes.c_int
+    L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
+    L.baim_conv2d_out_hw.restype = ctypes.c_int
+    L.baim_last_error.argtypes = []
+    L.baim_last_error.restype = ctypes.c_char_p
+    L.baim_version.argtypes = []
+    L.baim_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().baim_last_error().decode()
+
+
+def addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream) -> int:
+    return lib().addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream)
+
+
+def conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
+                    groups, stream) -> int:
+    return lib().conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW,
+                                 dH, dW, groups, stream)
+
+
+def conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW):
+    oh, ow = _i64(0), _i64(0)
+    st = lib().baim_conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW,
+                                  ctypes.byref(oh), ctypes.byref(ow))
+    return st, oh.value, ow.value

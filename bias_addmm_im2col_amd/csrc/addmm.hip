@@ -1,0 +1,100 @@
+// addmm.hip -- out = beta*self + alpha*(mat1 @ mat2) on the gfx950 matrix
+// cores ("[ExecuTorch][WebGPU] Add optimized addmm op", Solution and
+// Implementation paragraphs: mat1 [M,K] and mat2 [K,N] row-major, the
+// epilogue picks self[r*N + c] for a full self and the broadcast self[c]
+// otherwise, and writes beta*self + alpha*acc).
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace baim {
+
+struct AddmmArgs {
+  float* out;
+  const float* self;
+  const float* A;
+  const float* B;
+  int M, N, K;
+  int self_mode;
+  float beta, alpha;
+  int tiles_m, tiles_n, group_m;
+};
+
+template <class T, int VA, int VB>
+__global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
+  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm0 = (wave / T::WN) * T::WTM, wn0 = (wave % T::WN) * T::WTN;
+
+  RowTileLoader<T, VA> al;
+  al.init(p.A, m0, p.M, p.K);
+  ColTileLoader<T, VB> bl;
+  bl.init(p.B, n0, p.N, p.K);
+  Accum<T> acc;
+  mainloop<T>(acc, al, bl, p.K, smem, wm0, wn0, lane);
+
+  // Fused epilogue: beta*self + alpha*acc, self broadcast from [N] or full.
+  const int c = lane & 31;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const int n = n0 + wn0 + 32 * j + c;
+    if (n >= p.N) continue;
+    const float srow = p.self_mode == 1 ? p.self[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
+        if (m >= p.M) continue;
+        const size_t o = (size_t)m * p.N + n;
+        const float v = acc.c[i][j][r];
+        float res;
+        if (p.self_mode == 0) {
+          res = p.alpha * v;
+        } else {
+          const float s = p.self_mode == 1 ? srow : p.self[o];
+          res = fmaf(p.alpha, v, p.beta * s);
+        }
+        p.out[o] = res;
+      }
+  }
+}
+
+typedef Tile<128, 128, 32, 2, 2> AddmmTile;
+
+template <class T, int VA, int VB>
+static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL((addmm_kernel<T, VA, VB>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
+  typedef AddmmTile T;
+  AddmmArgs a;
+  a.out = p.out;
+  a.self = p.self;
+  a.A = p.mat1;
+  a.B = p.mat2;
+  a.M = p.M;
+  a.N = p.N;
+  a.K = p.K;
+  a.self_mode = p.self_mode;
+  a.beta = p.beta;
+  a.alpha = p.alpha;
+  a.tiles_m = (p.M + T::BM - 1) / T::BM;
+  a.tiles_n = (p.N + T::BN - 1) / T::BN;
+  a.group_m = 8;
+  const int nblocks = a.tiles_m * a.tiles_n;
+  // 16-byte vector loads need K (resp. N) divisible by 4 and aligned bases.
+  const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
+  const bool vb = p.N % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
+  if (va && vb) return launch_t<T, 4, 4>(a, nblocks, stream);
+  if (va) return launch_t<T, 4, 1>(a, nblocks, stream);
+  if (vb) return launch_t<T, 1, 4>(a, nblocks, stream);
+  return launch_t<T, 1, 1>(a, nblocks, stream);
+}
+
+}  // namespace baim

@@ -1,0 +1,192 @@
+// api.cpp -- the C ABI of libbaim.so (declared in include/baim.h).
+//
+// Every check runs on the host before anything is enqueued, so an invalid
+// call launches nothing and leaves `out` untouched (the conv page computes
+// both dispatch grids before any buffer is allocated so that a throw cannot
+// leak; here nothing is allocated at all).  Validation makes no HIP call,
+// which keeps it testable on a machine without a GPU.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "baim.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive
+// Byte offsets inside one tile of the operands are 32-bit: a block's A tile
+// spans at most 256 rows of K floats, a B tile 64 rows of N floats, and the
+// conv gather addresses the whole input.
+constexpr int64_t kMaxK = (int64_t)1 << 21;
+constexpr int64_t kMaxAddmmN = (int64_t)1 << 23;
+constexpr int64_t kMaxConvInput = (int64_t)1 << 29;
+
+baim_status fail(baim_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+// Number of elements of a product of sizes, or -1 on overflow.
+int64_t elems(std::initializer_list<int64_t> dims) {
+  int64_t n = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(n, d, &n)) return -1;
+  return n;
+}
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  const uintptr_t a1 = a0 + (uintptr_t)na * 4u, b1 = b0 + (uintptr_t)nb * 4u;
+  return a0 < b1 && b0 < a1;
+}
+
+baim_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BAIM_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return BAIM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int baim_version(void) { return 100; }
+
+const char* baim_last_error(void) { return g_err.c_str(); }
+
+baim_status baim_conv2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW, int64_t sH,
+                               int64_t sW, int64_t pH, int64_t pW, int64_t dH, int64_t dW,
+                               int64_t* OH, int64_t* OW) {
+  g_err.clear();
+  if (!OH || !OW) return fail(BAIM_ERR_NULL, "baim_conv2d_out_hw: OH/OW must not be NULL");
+  *OH = *OW = 0;
+  if (H < 1 || W < 1 || KH < 1 || KW < 1)
+    return fail(BAIM_ERR_SHAPE, "conv2d: input and kernel sizes must be >= 1");
+  if (sH < 1 || sW < 1) return fail(BAIM_ERR_SHAPE, "conv2d: stride must be >= 1");
+  if (dH < 1 || dW < 1) return fail(BAIM_ERR_SHAPE, "conv2d: dilation must be >= 1");
+  if (pH < 0 || pW < 0) return fail(BAIM_ERR_SHAPE, "conv2d: padding must be >= 0");
+  if (H > kMaxElems || W > kMaxElems || KH > kMaxElems || KW > kMaxElems || pH > kMaxElems ||
+      pW > kMaxElems || dH > kMaxElems || dW > kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d: size argument too large");
+  const int64_t spanH = H + 2 * pH - dH * (KH - 1) - 1;
+  const int64_t spanW = W + 2 * pW - dW * (KW - 1) - 1;
+  if (spanH < 0 || spanW < 0)
+    return fail(BAIM_ERR_SHAPE, "conv2d: dilated kernel (%lld x %lld) larger than padded input",
+                (long long)(dH * (KH - 1) + 1), (long long)(dW * (KW - 1) + 1));
+  *OH = spanH / sH + 1;
+  *OW = spanW / sW + 1;
+  return BAIM_OK;
+}
+
+baim_status addmm_f32(float* out, const float* self, int self_2d, const float* mat1,
+                      const float* mat2, int64_t M, int64_t N, int64_t K, float beta, float alpha,
+                      void* stream) {
+  g_err.clear();
+  if (M < 0 || N < 0 || K < 0)
+    return fail(BAIM_ERR_SHAPE, "addmm: sizes must be >= 0 (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (self_2d != 0 && self_2d != 1)
+    return fail(BAIM_ERR_SHAPE, "addmm: self_2d must be 0 (self [N]) or 1 (self [M,N])");
+  const int64_t n_out = elems({M, N}), n_a = elems({M, K}), n_b = elems({K, N});
+  if (n_out < 0 || n_a < 0 || n_b < 0 || n_out >= kMaxElems || n_a >= kMaxElems ||
+      n_b >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "addmm: every tensor must have fewer than 2^31 elements");
+  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "addmm: K must be below 2^21");
+  if (N >= kMaxAddmmN) return fail(BAIM_ERR_TOO_LARGE, "addmm: N must be below 2^23");
+  if (M == 0 || N == 0) return BAIM_OK;  // empty output: nothing to do
+  const bool reads_self = beta != 0.0f;
+  if (!out) return fail(BAIM_ERR_NULL, "addmm: out is NULL");
+  if (reads_self && !self) return fail(BAIM_ERR_NULL, "addmm: self is NULL but beta != 0");
+  if (K > 0 && (!mat1 || !mat2)) return fail(BAIM_ERR_NULL, "addmm: mat1/mat2 is NULL");
+  const int64_t n_self = self_2d ? n_out : N;
+  if ((K > 0 && (overlap(out, n_out, mat1, n_a) || overlap(out, n_out, mat2, n_b))) ||
+      (reads_self && overlap(out, n_out, self, n_self)))
+    return fail(BAIM_ERR_ALIAS, "addmm: out overlaps an input");
+
+  baim::AddmmProblem p;
+  p.out = out;
+  p.self = reads_self ? self : nullptr;
+  p.mat1 = mat1;
+  p.mat2 = mat2;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.self_mode = reads_self ? (self_2d ? 2 : 1) : 0;
+  p.beta = beta;
+  p.alpha = alpha;
+  return launched(baim::launch_addmm(p, (hipStream_t)stream), "addmm_f32");
+}
+
+baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
+                            const float* bias, int64_t B, int64_t IC, int64_t H, int64_t W,
+                            int64_t OC, int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                            int64_t pH, int64_t pW, int64_t dH, int64_t dW, int64_t groups,
+                            void* stream) {
+  g_err.clear();
+  if (B < 1 || IC < 1 || OC < 1)
+    return fail(BAIM_ERR_SHAPE, "conv2d: B, IC and OC must be >= 1");
+  if (groups < 1) return fail(BAIM_ERR_SHAPE, "conv2d: groups must be >= 1");
+  int64_t OH = 0, OW = 0;
+  const baim_status hs = baim_conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, &OH, &OW);
+  if (hs != BAIM_OK) return hs;  // message already set
+  if (groups != 1)
+    return fail(BAIM_ERR_UNSUPPORTED,
+                "conv2d: groups=%lld is not routed through the im2col GEMM (groups == 1 only)",
+                (long long)groups);
+  const int64_t n_x = elems({B, IC, H, W}), n_w = elems({OC, IC, KH, KW});
+  const int64_t n_out = elems({B, OC, OH, OW}), K = elems({IC, KH, KW});
+  if (n_x < 0 || n_w < 0 || n_out < 0 || n_x >= kMaxElems || n_w >= kMaxElems ||
+      n_out >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d: every tensor must have fewer than 2^31 elements");
+  if (n_x >= kMaxConvInput) return fail(BAIM_ERR_TOO_LARGE, "conv2d: input must have fewer than 2^29 elements");
+  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d: IC*KH*KW must be below 2^21");
+  // In-kernel tap offsets (ih*W + iw over the padded plane) are 32-bit.
+  const int64_t n_pad = elems({H + 2 * pH, W + 2 * pW});
+  if (n_pad < 0 || n_pad >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d: padded input plane must have fewer than 2^31 elements");
+  if (!out || !input || !weight) return fail(BAIM_ERR_NULL, "conv2d: out/input/weight is NULL");
+  if (overlap(out, n_out, input, n_x) || overlap(out, n_out, weight, n_w) ||
+      overlap(out, n_out, bias, OC))
+    return fail(BAIM_ERR_ALIAS, "conv2d: out overlaps an input");
+
+  baim::ConvProblem q;
+  q.out = out;
+  q.x = input;
+  q.w = weight;
+  q.bias = bias;
+  q.B = (int)B;
+  q.IC = (int)IC;
+  q.H = (int)H;
+  q.W = (int)W;
+  q.OC = (int)OC;
+  q.KH = (int)KH;
+  q.KW = (int)KW;
+  q.sH = (int)sH;
+  q.sW = (int)sW;
+  q.pH = (int)pH;
+  q.pW = (int)pW;
+  q.dH = (int)dH;
+  q.dW = (int)dW;
+  q.OH = (int)OH;
+  q.OW = (int)OW;
+  return launched(baim::launch_conv2d(q, (hipStream_t)stream), "conv2d_gemm_f32");
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// gemm_core.hpp -- device side of the fp32 tiled GEMM for gfx950 (CDNA4).
+//
+// The method ("[ExecuTorch][WebGPU] Add optimized addmm op", Solution
+// paragraph) stages tiles of both operands in on-chip shared memory, syncs
+// the workgroup, and accumulates over ceil(K/BK) k-tiles so that each
+// coalesced tile load is reused by the whole output tile.  On gfx950 that
+// becomes:
+//   * a BM x BN block tile computed by WM x WN wavefronts (64 lanes each);
+//     every wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 blocks;
+//   * the contraction runs on the fp32 matrix cores,
+//     v_mfma_f32_32x32x2_f32 (A 32x2, B 2x32, C 32x32, fp32 accumulate);
+//   * both operand tiles are double-buffered in LDS; the next k-tile is
+//     fetched from HBM into registers while the current one feeds the
+//     matrix cores, then written to the other LDS buffer: one barrier per
+//     k-tile;
+//   * global reads are raw buffer loads: an offset past the buffer's range
+//     returns 0, which gives the ragged M/N/K edges and the conv's zero
+//     padding without branches.
+//
+// Lane layout of v_mfma_f32_32x32x2_f32 (lane l, c = l % 32, h = l / 32):
+//   A operand: A[row c][k h];  B operand: B[k h][col c];
+//   accumulator register j: C[row 8*(j/4) + 4*h + (j%4)][col c].
+//
+// K order: any fp32 summation order is acceptable, so inside a k-tile the
+// MFMA step s (0 <= s < BK/2) of lane-half h uses k = 8*(s/4) + 4*h + s%4.
+// Each lane then finds its A values for four consecutive steps in four
+// consecutive LDS floats (one 16-byte read), and the two lane-halves read B
+// rows four apart, which land in disjoint LDS banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "index_math.hpp"
+
+namespace baim {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource for gfx9-family: stride 0, 32-bit data format bits.
+constexpr int kBufferFlags = 0x00020000;
+// Offset used for a masked element: it is past the range of every
+// resource built here (all ranges are below 2^31 bytes), so the load
+// returns 0 without touching memory.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Resource over the `elems` floats starting at p (clamped to 2^31 - 1
+// bytes).  The range is exact, so even a wrong offset cannot read past the
+// tensor: the hardware returns 0 instead.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const float* p, int64_t elems) {
+  const int64_t bytes = elems * 4 < 0x7FFFFFFF ? elems * 4 : 0x7FFFFFFF;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, (int)bytes, kBufferFlags);
+}
+
+template <int VEC> struct Vec;
+template <> struct Vec<1> {
+  typedef float T;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+template <> struct Vec<4> {
+  typedef f32x4 T;
+  __device__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  // LDS row strides (floats).  A is [BM][BK+4]: 16-byte reads of 32
+  // consecutive rows spread over all banks.  B is [BK][BN+8]: rows four
+  // apart start 32 banks apart.
+  static constexpr int AS = BK + 4, BS = BN + 8;
+  static constexpr int A_FLOATS = BM * AS, B_FLOATS = BK * BS;
+  static constexpr int STAGE = A_FLOATS + B_FLOATS;
+  static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
+  static_assert(BN % 16 == 0, "B padding assumes BN % 16 == 0");
+};
+
+// ---------------------------------------------------------------- loaders
+
+// A tile from a row-major [rows][ld] matrix whose contiguous dim is K
+// (mat1 [M,K]; the conv weight viewed as [OC, IC*KH*KW]).
+template <class T, int VEC>
+struct RowTileLoader {
+  static constexpr int CPR = T::BK / VEC;
+  static constexpr int NCH = T::BM * CPR / T::NT;
+  static_assert((T::BM * CPR) % T::NT == 0, "A tile must split evenly over threads");
+  typedef typename Vec<VEC>::T V;
+  const float* base;  // first row of the block
+  int K, rows_left;
+  V reg[NCH];
+
+  __device__ void init(const float* A, int m0, int M, int K_) {
+    base = A + (size_t)m0 * K_;
+    K = K_;
+    rows_left = M - m0;
+  }
+  __device__ void load(int k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0, (int64_t)rows_left * K - k0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q / CPR, c = (q % CPR) * VEC;
+      const bool ok = r < rows_left && k0 + c < K;
+      reg[i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * K + c) * 4u : kOOB);
+    }
+  }
+  __device__ void store(float* As) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q / CPR, c = (q % CPR) * VEC;
+      *reinterpret_cast<V*>(&As[r * T::AS + c]) = reg[i];
+    }
+  }
+};
+
+// B tile from a row-major [K][N] matrix (mat2, read as mat2[k*N + n]).
+template <class T, int VEC>
+struct ColTileLoader {
+  static constexpr int CPR = T::BN / VEC;
+  static constexpr int NCH = T::BK * CPR / T::NT;
+  static_assert((T::BK * CPR) % T::NT == 0, "B tile must split evenly over threads");
+  typedef typename Vec<VEC>::T V;
+  const float* base;  // column n0 of row 0
+  int N, K, cols_left;
+  V reg[NCH];
+
+  __device__ void init(const float* B, int n0, int N_, int K_) {
+    base = B + n0;
+    N = N_;
+    K = K_;
+    cols_left = N_ - n0;
+  }
+  __device__ void load(int k0) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + (size_t)k0 * N, (int64_t)(K - k0) * N - (N - cols_left));
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q / CPR, c = (q % CPR) * VEC;
+      const bool ok = k0 + r < K && c < cols_left;
+      reg[i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * N + c) * 4u : kOOB);
+    }
+  }
+  __device__ void store(float* Bs) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q / CPR, c = (q % CPR) * VEC;
+      *reinterpret_cast<V*>(&Bs[r * T::BS + c]) = reg[i];
+    }
+  }
+};
+
+// ----------------------------------------------------------- contraction
+
+template <class T>
+struct Accum {
+  f32x16 c[T::FM][T::FN];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[i][j][r] = 0.0f;
+  }
+};
+
+// One k-tile: BK/2 MFMA steps for every 32x32 block of the wave's sub-tile.
+template <class T>
+__device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs, int wm0,
+                                int wn0, int lane) {
+  const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < T::BK / 8; ++g) {
+    f32x4 a[T::FM];
+    float b[T::FN][4];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+      a[i] = *reinterpret_cast<const f32x4*>(&As[(wm0 + 32 * i + c) * T::AS + 8 * g + 4 * h]);
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * T::BS + wn0 + 32 * j + c];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// The k loop: prefetch k-tile t+1 into registers, run the MFMAs on tile t
+// from LDS, write t+1 to the other LDS buffer, one barrier.
+template <class T, class AL, class BL>
+__device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int K, float* smem, int wm0,
+                                int wn0, int lane) {
+  acc.zero();
+  const int nt = (K + T::BK - 1) / T::BK;
+  if (nt == 0) return;
+  al.load(0);
+  bl.load(0);
+  al.store(smem);
+  bl.store(smem + T::A_FLOATS);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    float* cur = smem + (t & 1) * T::STAGE;
+    float* nxt = smem + ((t + 1) & 1) * T::STAGE;
+    const bool more = t + 1 < nt;
+    if (more) {
+      al.load((t + 1) * T::BK);
+      bl.load((t + 1) * T::BK);
+    }
+    mma_tile<T>(acc, cur, cur + T::A_FLOATS, wm0, wn0, lane);
+    if (more) {
+      al.store(nxt);
+      bl.store(nxt + T::A_FLOATS);
+    }
+    __syncthreads();
+  }
+}
+
+// Row of accumulator register j of a 32x32 block, relative to the block.
+__device__ inline int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+}  // namespace baim

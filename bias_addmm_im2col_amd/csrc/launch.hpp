@@ -1,0 +1,31 @@
+// launch.hpp -- host-side interface between the C ABI (api.cpp) and the
+// kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace baim {
+
+struct AddmmProblem {
+  float* out;
+  const float* self;  // read only when self_mode != 0
+  const float* mat1;
+  const float* mat2;
+  int M, N, K;
+  int self_mode;  // 0: beta == 0, self not read; 1: self [N]; 2: self [M,N]
+  float beta, alpha;
+};
+
+struct ConvProblem {
+  float* out;
+  const float* x;
+  const float* w;
+  const float* bias;  // may be NULL
+  int B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
+};
+
+hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
+hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
+
+}  // namespace baim

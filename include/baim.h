@@ -1,0 +1,129 @@
+/*
+ * baim.h -- C ABI of libbaim.so: fp32 tiled GEMM with a fused epilogue on
+ * AMD Instinct MI355X (gfx950), used as addmm and as groups==1 NCHW conv2d
+ * through an implicit im2col.
+ *
+ * Common conventions
+ *  - Every tensor pointer is a DEVICE pointer to caller-owned, contiguous,
+ *    row-major (NCHW for images) fp32 memory.  The library never allocates,
+ *    frees or retains memory; it only reads the inputs and writes `out`.
+ *  - All arguments are validated on the host before anything is enqueued.
+ *    A call that returns an error has launched nothing and left `out`
+ *    untouched; baim_last_error() then describes the problem.
+ *  - On success the work is ENQUEUED on `stream` (a hipStream_t; NULL means
+ *    the default stream) and the call returns at once.  A device fault
+ *    surfaces at the caller's next synchronisation, as with any HIP launch.
+ *  - `out` must not overlap any input (BAIM_ERR_ALIAS).
+ *  - Sizes are int64_t.  Limits (BAIM_ERR_TOO_LARGE beyond them, because
+ *    in-kernel offsets are 32-bit): every tensor holds fewer than 2^31
+ *    elements; K (IC*KH*KW for the conv) is below 2^21; addmm's N is below
+ *    2^23; the conv input holds fewer than 2^29 elements and its padded
+ *    plane (H+2pH)*(W+2pW) fewer than 2^31.
+ *  - Results: any fp32 summation order is allowed (the order inside a tile,
+ *    across tiles and inside the matrix cores is unspecified); the result
+ *    satisfies |out - exact| <= 4e-6*sqrt(K)*(|alpha|*sum_k|a*b| + |beta*self|).
+ *  - Thread safety: calls may be made from several host threads; the error
+ *    text is per thread.
+ */
+#ifndef BAIM_H
+#define BAIM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BAIM_OK = 0,
+  BAIM_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  BAIM_ERR_SHAPE = 2,       /* a size/stride/flag is out of its domain       */
+  BAIM_ERR_UNSUPPORTED = 3, /* valid conv, but not one this path computes    */
+  BAIM_ERR_TOO_LARGE = 4,   /* a tensor has 2^31 or more elements            */
+  BAIM_ERR_ALIAS = 5,       /* out overlaps an input                         */
+  BAIM_ERR_LAUNCH = 6       /* the HIP launch itself failed                  */
+} baim_status;
+
+/*
+ * addmm_f32: out[M,N] = beta*self + alpha*(mat1[M,K] @ mat2[K,N]).
+ *
+ * Defined by "[ExecuTorch][WebGPU] Add optimized addmm op" (PR #20855),
+ * Solution and Implementation paragraphs: mat1 [M,K] and mat2 [K,N] are
+ * row-major (mat2 is read as mat2[k*N + n]); self is either the bias row
+ * broadcast over rows (self_2d = 0: self[N], element self[n]) or a full
+ * matrix (self_2d = 1: self[M,N], element self[m*N + n]); alpha and beta are
+ * fp32 scalars (the page passes them as 32-bit floats, default 1.0).
+ *
+ *  out    [M,N] fp32, written in full.
+ *  self   [N] or [M,N] fp32; may be NULL only when beta == 0.  When
+ *         beta == 0 self is not read at all, so NaN/Inf in it do not
+ *         propagate (aten's rule for addmm).
+ *  mat1   [M,K], mat2 [K,N] fp32.  May be NULL only if the product is empty.
+ *  M,N,K  >= 0.  M == 0 or N == 0: nothing to do, BAIM_OK.  K == 0: the
+ *         product is empty and out = beta*self.
+ *  stream hipStream_t or NULL.
+ */
+baim_status addmm_f32(float* out, const float* self, int self_2d,
+                      const float* mat1, const float* mat2, int64_t M,
+                      int64_t N, int64_t K, float beta, float alpha,
+                      void* stream);
+
+/*
+ * conv2d_gemm_f32: out = conv2d(input, weight, bias) for groups == 1,
+ * computed as the GEMM  out[oc, n] = sum_kk weight[oc, kk] * col[kk, n]
+ * + bias[oc], with M = OC, N = B*OH*OW, K = IC*KH*KW and col the implicit
+ * im2col of the input (never materialised).
+ *
+ * Defined by "et_vk conv2d: route standard (groups==1) conv through an
+ * im2col tiled GEMM" (PR #20873), Solution and Implementation paragraphs:
+ * n decodes to (b, oh, ow) and kk to (ic, kh, kw); the input is sampled at
+ * ih = oh*sH - pH + kh*dH, iw = ow*sW - pW + kw*dW, and a tap outside the
+ * input reads 0 (zero padding); bias is added per output channel; the
+ * output is NCHW.  Grouped, depthwise and transposed convolutions are not
+ * routed through this GEMM (the page keeps them on other kernels), so
+ * groups != 1 returns BAIM_ERR_UNSUPPORTED.
+ *
+ *  out     [B,OC,OH,OW] fp32 NCHW, written in full; OH, OW as given by
+ *          baim_conv2d_out_hw().
+ *  input   [B,IC,H,W] fp32 NCHW.
+ *  weight  [OC,IC,KH,KW] fp32 (read as the row-major [OC, IC*KH*KW] matrix).
+ *  bias    [OC] fp32, or NULL for no bias.
+ *  sizes   B, IC, H, W, OC, KH, KW >= 1; strides sH, sW >= 1;
+ *          paddings pH, pW >= 0; dilations dH, dW >= 1; OH, OW >= 1.
+ *  groups  must be 1.
+ *  stream  hipStream_t or NULL.
+ */
+baim_status conv2d_gemm_f32(float* out, const float* input,
+                            const float* weight, const float* bias, int64_t B,
+                            int64_t IC, int64_t H, int64_t W, int64_t OC,
+                            int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                            int64_t pH, int64_t pW, int64_t dH, int64_t dW,
+                            int64_t groups, void* stream);
+
+/*
+ * baim_conv2d_out_hw: the output size of the conv above,
+ * OH = floor((H + 2*pH - dH*(KH-1) - 1) / sH) + 1 and likewise OW (the
+ * pages print no formula; this is the standard one, which gives the stated
+ * [1,128,192,192] output of a 7x7/stride-4/pad-3 stem on 768x768).
+ * Writes *OH and *OW and returns BAIM_OK, or BAIM_ERR_SHAPE (with *OH, *OW
+ * set to 0) if an argument is out of range or the output would be empty;
+ * BAIM_ERR_NULL if OH or OW is NULL.  Host-only; touches no GPU.
+ */
+baim_status baim_conv2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW,
+                               int64_t sH, int64_t sW, int64_t pH, int64_t pW,
+                               int64_t dH, int64_t dW, int64_t* OH,
+                               int64_t* OW);
+
+/* Text describing the last error returned on the calling thread ("" if the
+ * last call succeeded).  The pointer stays valid until the next call on the
+ * same thread. */
+const char* baim_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int baim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAIM_H */

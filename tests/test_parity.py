@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Acceptance: |out - ref| <= 4e-6*sqrt(K)*(|alpha|*sum_k|a*b| + |beta*self|)
+elementwise; integer-valued inputs (every partial sum an integer below
+2^24, so every fp32 summation order is exact) must match bit for bit.
+Definitions: "[ExecuTorch][WebGPU] Add optimized addmm op" (Solution) and
+"et_vk conv2d: route standard (groups==1) conv through an im2col tiled GEMM"
+(Solution/Implementation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bias_addmm_im2col_amd import inputs as I
+from tests._parity import addmm_sample, check_bitwise, check_close, conv_sample, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    import bias_addmm_im2col_amd  # noqa: F401  (fails loudly if not built)
+    from bias_addmm_im2col_amd import _capi
+    _capi.lib()
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def gen(shape, seed, kind="U"):
+    g = torch.Generator("cpu").manual_seed(seed)
+    if kind == "U":
+        return torch.rand(shape, generator=g) * 2 - 1
+    if kind == "I":
+        return torch.randint(-4, 5, shape, generator=g).float()
+    raise ValueError(kind)
+
+
+def run_addmm(a, b, s, beta, alpha):
+    import bias_addmm_im2col_amd as baim
+    out = baim.addmm(dev(s), dev(a), dev(b), beta=beta, alpha=alpha)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def run_conv(x, w, bias, stride, pad, dil):
+    import bias_addmm_im2col_amd as baim
+    out = baim.conv2d(dev(x), dev(w), dev(bias), stride, pad, dil)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# ------------------------------------------------------------ addmm, small
+
+ADDMM_SHAPES = [
+    # M, K, N, self_2d, beta, alpha
+    (1, 1, 1, False, 1.0, 1.0),
+    (3, 5, 7, True, 0.5, 2.0),
+    (64, 96, 80, False, 1.0, 1.0),
+    (128, 32, 128, False, 1.0, 1.0),
+    (127, 33, 129, True, 1.0, -1.0),
+    (129, 31, 257, False, 2.0, 0.5),
+    (257, 64, 130, True, -0.5, 1.5),
+    (200, 300, 300, False, 1.0, 1.0),
+    (131, 1, 67, False, 1.0, 1.0),
+    (300, 517, 100, True, 0.25, 1.0),
+    (256, 256, 512, False, 1.0, 1.0),
+    (37, 1000, 41, True, 1.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,self_2d,beta,alpha", ADDMM_SHAPES)
+def test_addmm_small_full(M, K, N, self_2d, beta, alpha):
+    say(f"addmm_f32 M={M} K={K} N={N} self_2d={self_2d} beta={beta} alpha={alpha}")
+    a, b = gen((M, K), 1), gen((K, N), 2)
+    s = gen((M, N) if self_2d else (N,), 3)
+    out = run_addmm(a, b, s, beta, alpha)
+    res = oracle.addmm(a, b, s, self_2d, beta, alpha)
+    check_close(out, res, K, alpha, f"addmm {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N,self_2d", [(64, 96, 80, False), (129, 257, 131, True),
+                                           (256, 1024, 384, False), (77, 4096, 65, True)])
+def test_addmm_integer_bitwise(M, K, N, self_2d):
+    """P-7: small-integer inputs, power-of-two alpha/beta: bit-exact."""
+    say(f"addmm_f32 integer M={M} K={K} N={N}")
+    a, b = gen((M, K), 4, "I"), gen((K, N), 5, "I")
+    s = gen((M, N) if self_2d else (N,), 6, "I")
+    out = run_addmm(a, b, s, 0.5, 2.0)
+    check_bitwise(out, oracle.addmm(a, b, s, self_2d, 0.5, 2.0), "addmm integer")
+
+
+def test_addmm_alpha_zero_is_beta_self_exactly():
+    say("addmm_f32 alpha=0")
+    a, b, s = gen((70, 50), 7), gen((50, 90), 8), gen((70, 90), 9)
+    out = run_addmm(a, b, s, 0.75, 0.0)
+    check_bitwise(out, oracle.addmm(a, b, s, True, 0.75, 0.0), "alpha=0")
+
+
+def test_addmm_identity_mat2():
+    say("addmm_f32 identity mat2")
+    a, s = gen((100, 64), 10), gen((64,), 11)
+    out = run_addmm(a, torch.eye(64), s, 0.5, 4.0)
+    check_bitwise(out, oracle.addmm(a, torch.eye(64), s, False, 0.5, 4.0), "identity")
+
+
+def test_addmm_beta_zero_ignores_nan_self():
+    import bias_addmm_im2col_amd as baim
+    say("addmm_f32 beta=0, NaN self")
+    a, b = gen((40, 24), 12), gen((24, 36), 13)
+    s = torch.full((36,), float("nan"))
+    out = baim.addmm(dev(s), dev(a), dev(b), beta=0, alpha=1.5).cpu().numpy()
+    assert np.isfinite(out).all()
+    check_close(out, oracle.addmm(a, b, s, False, 0.0, 1.5), 24, 1.5, "beta=0")
+    out2 = baim.addmm(None, dev(a), dev(b), beta=0, alpha=1.5).cpu().numpy()
+    assert np.array_equal(out, out2)
+
+
+def test_addmm_k0_and_empty():
+    import bias_addmm_im2col_amd as baim
+    say("addmm_f32 K=0 / M=0 / N=0")
+    s = gen((5, 6), 14)
+    out = baim.addmm(dev(s), torch.zeros(5, 0).cuda(), torch.zeros(0, 6).cuda(), beta=2.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), 2.0 * s.numpy())
+    e = baim.addmm(torch.zeros(6).cuda(), torch.zeros(0, 3).cuda(), torch.zeros(3, 6).cuda())
+    assert tuple(e.shape) == (0, 6)
+    e = baim.addmm(torch.zeros(0).cuda(), torch.zeros(4, 3).cuda(), torch.zeros(3, 0).cuda())
+    assert tuple(e.shape) == (4, 0)
+
+
+def test_addmm_self_row_shape_and_unaligned_operands():
+    """self given as [1,N]; mat1/mat2 starting 4 bytes into an allocation
+    (forces the scalar-load variant)."""
+    import bias_addmm_im2col_amd as baim
+    say("addmm_f32 self [1,N], unaligned operands")
+    M, K, N = 150, 68, 132
+    a, b, s = gen((M, K), 15), gen((K, N), 16), gen((1, N), 17)
+    abuf = torch.empty(M * K + 1, device="cuda")
+    abuf[1:] = dev(a).reshape(-1)
+    bbuf = torch.empty(K * N + 1, device="cuda")
+    bbuf[1:] = dev(b).reshape(-1)
+    out = baim.addmm(dev(s), abuf[1:].view(M, K), bbuf[1:].view(K, N))
+    torch.cuda.synchronize()
+    check_close(out.cpu().numpy(), oracle.addmm(a, b, s.reshape(-1), False), K, 1.0, "unaligned")
+
+
+# ----------------------------------------------------------- conv, small
+
+CONV_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, dil, bias
+    (1, 1, 5, 5, 1, 3, 3, 1, 0, 1, True),
+    (2, 3, 17, 19, 8, 3, 3, 1, 1, 1, True),
+    (1, 3, 64, 64, 16, 7, 7, 4, 3, 1, True),
+    (2, 16, 14, 14, 32, 3, 3, 1, 2, 2, False),
+    (2, 16, 15, 15, 24, 3, 3, 2, 1, 1, True),
+    (3, 5, 11, 13, 130, 2, 3, (2, 1), (0, 2), (1, 2), True),
+    (1, 64, 9, 9, 129, 1, 1, 1, 0, 1, True),
+    (2, 32, 20, 12, 64, 5, 5, (1, 2), (2, 1), (2, 1), True),
+    (1, 8, 40, 40, 200, 3, 3, 3, 1, 1, True),
+]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,has_bias", CONV_SHAPES)
+def test_conv_small_full(B, IC, H, W, OC, KH, KW, stride, pad, dil, has_bias):
+    say(f"conv2d_gemm_f32 x=[{B},{IC},{H},{W}] w=[{OC},{IC},{KH},{KW}] s={stride} p={pad} d={dil}")
+    x, w = gen((B, IC, H, W), 20), gen((OC, IC, KH, KW), 21)
+    bias = gen((OC,), 22) if has_bias else None
+    out = run_conv(x, w, bias, stride, pad, dil)
+    res = oracle.conv2d(x, w, bias, stride, pad, dil)
+    check_close(out, res, IC * KH * KW, 1.0, "conv")
+
+
+@pytest.mark.parametrize("stride,pad,dil", [(1, 1, 1), (1, 2, 2), (2, 1, 1), (4, 3, 1)])
+def test_conv_integer_bitwise(stride, pad, dil):
+    say(f"conv2d_gemm_f32 integer s={stride} p={pad} d={dil}")
+    x, w, bias = gen((2, 24, 23, 21), 23, "I"), gen((136, 24, 3, 3), 24, "I"), gen((136,), 25, "I")
+    out = run_conv(x, w, bias, stride, pad, dil)
+    check_bitwise(out, oracle.conv2d(x, w, bias, stride, pad, dil), "conv integer")
+
+
+def test_conv_1x1_equals_addmm():
+    """P-4 on the GPU: a 1x1 conv and addmm(W, x[b]) agree bit for bit on
+    integer inputs."""
+    import bias_addmm_im2col_amd as baim
+    say("conv 1x1 vs addmm")
+    B, IC, H, W, OC = 2, 40, 12, 13, 72
+    x, w = gen((B, IC, H, W), 26, "I"), gen((OC, IC, 1, 1), 27, "I")
+    bias = gen((OC,), 28, "I")
+    out = run_conv(x, w, bias, 1, 0, 1)
+    for b in range(B):
+        mm = baim.addmm(dev(bias.view(OC, 1).expand(OC, H * W).contiguous()),
+                        dev(w.view(OC, IC)), dev(x[b].reshape(IC, H * W))).cpu().numpy()
+        assert np.array_equal(mm, out[b].reshape(OC, H * W))
+
+
+def test_conv_delta_kernel_shift():
+    """P-5 on the GPU: delta weights shift the input (exact)."""
+    say("conv delta kernel")
+    C = 8
+    x = gen((2, C, 19, 17), 29)
+    w = torch.zeros(C, C, 3, 3)
+    for c in range(C):
+        w[c, c, 2, 0] = 1.0
+    out = run_conv(x, w, None, 1, (1, 1), (2, 1))
+    check_bitwise(out, oracle.conv2d(x, w, None, 1, (1, 1), (2, 1)), "delta")
+
+
+# ------------------------------------------------------- full workloads
+
+@pytest.mark.parametrize("name", [n for n, c in I.CASES.items() if c.kind == "addmm"])
+def test_workload_addmm(name):
+    import bias_addmm_im2col_amd as baim
+    c = I.CASES[name]
+    say(f"workload {name}: addmm_f32 M={c.M} K={c.K} N={c.N} self_2d={c.self_2d}")
+    a, b, s = I.addmm_inputs(c)
+    out = baim.addmm(dev(s), dev(a), dev(b), beta=c.beta, alpha=c.alpha)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    if c.M * c.N * c.K <= 64 * 96 * 80:
+        res = oracle.addmm(a, b, s, c.self_2d, c.beta, c.alpha)
+        check_close(out, res, c.K, c.alpha, name)
+        return
+    rows, cols = addmm_sample(c.M, c.N)
+    res = oracle.addmm_at(a, b, s, c.self_2d, c.beta, c.alpha, rows, cols)
+    ratio = check_close(out[rows, cols], res, c.K, c.alpha, name)
+    say(f"{name}: {rows.size} sampled outputs, max err/tol = {ratio:.3f}")
+
+
+@pytest.mark.parametrize("name", [n for n, c in I.CASES.items() if c.kind == "conv"])
+def test_workload_conv(name):
+    import bias_addmm_im2col_amd as baim
+    c = I.CASES[name]
+    say(f"workload {name}: conv2d_gemm_f32 x=[{c.B},{c.IC},{c.H},{c.W}] "
+        f"w=[{c.OC},{c.IC},{c.KH},{c.KW}] s={c.stride} p={c.padding} d={c.dilation}")
+    x, w, bias = I.conv_inputs(c)
+    out = baim.conv2d(dev(x), dev(w), dev(bias), c.stride, c.padding, c.dilation)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    OH, OW = c.out_hw()
+    assert out.shape == (c.B, c.OC, OH, OW)
+    assert np.isfinite(out).all()
+    idx = conv_sample(c.B, c.OC, OH, OW)
+    res = oracle.conv2d_at(x, w, bias, c.stride, c.padding, c.dilation, idx)
+    ratio = check_close(out.reshape(-1)[idx], res, c.IC * c.KH * c.KW, 1.0, name)
+    say(f"{name}: {idx.size} sampled outputs, max err/tol = {ratio:.3f}")
+
+
+def test_repeated_launches_are_deterministic():
+    """The same call twice gives the same bits (no cross-launch state)."""
+    import bias_addmm_im2col_amd as baim
+    say("determinism")
+    a, b, s = gen((300, 200), 30), gen((200, 260), 31), gen((260,), 32)
+    o1 = baim.addmm(dev(s), dev(a), dev(b)).cpu()
+    o2 = baim.addmm(dev(s), dev(a), dev(b)).cpu()
+    assert torch.equal(o1, o2)
