@@ -63,7 +63,7 @@ __global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
   }
 }
 
-typedef Tile<128, 128, 32, 2, 2> AddmmTile;
+typedef Tile<128, 128, 32, 2, 4> AddmmTile;
 
 template <class T, int VA, int VB>
 static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {

@@ -28,44 +28,83 @@ struct ConvArgs {
   int tiles_m, tiles_n, group_m;
 };
 
+// B operand: the implicit im2col tile B[kk, n] for kk in [k0, k0+BK),
+// n in [n0, n0+BN).
+//  * Column side (per thread, once): n -> (b, oh, ow), the input offset of
+//    the tap (kh, kw) = (0, 0) and its coordinates ih0 = oh*sH - pH,
+//    iw0 = ow*sW - pW.  Columns past N get iw0 = -(dW*(KW-1)) - 1, so
+//    every tap of theirs reads as out of range.
+//  * Row side (per k-tile, in LDS): kk -> (ic, kh, kw) gives the offset
+//    ic*H*W + kh*dH*W + kw*dW and the tap shifts dh = kh*dH, dw = kw*dW.
+//    Rows past K get dh = -(H + 2*pH) - 1, so they read as out of range.
+//    BK threads decode one row each, two k-tiles ahead of use.
+//  * Element: valid iff 0 <= ih0+dh < H and 0 <= iw0+dw < W; invalid
+//    elements load from an out-of-range offset and read 0 (the padding).
+// A wave loads 64 consecutive columns of one row per instruction, so every
+// lane of a wave reads the same table entry (an LDS broadcast).
 template <class T>
 struct ImColTileLoader {
+  static constexpr bool kHasMeta = true;
   static constexpr int RPP = T::NT / T::BN;  // tile rows covered per pass
   static constexpr int NP = T::BK / RPP;     // passes per k-tile
   static_assert(T::NT % T::BN == 0 && T::BK % RPP == 0, "im2col tile split");
   static_assert(T::BN % 64 == 0, "a wave must cover columns of a single row");
+  static_assert(T::NT >= T::BK, "one thread per table row");
+  const ConvArgs* a;
+  int4* tbl;  // [2][BK] {offset, dh, dw, unused}
   int row0, col, cbase, ih0, iw0;
-  bool cok;
   float reg[NP];
 
-  __device__ void init(const ConvArgs& a, int n0) {
+  __device__ void init(const ConvArgs& args, int n0, int4* table) {
+    a = &args;
+    tbl = table;
     col = threadIdx.x % T::BN;
-    row0 = __builtin_amdgcn_readfirstlane(threadIdx.x / T::BN);
+    row0 = threadIdx.x / T::BN;
     const int n = n0 + col;
-    cok = n < a.N;
+    const bool cok = n < args.N;
     const uint32_t nn = cok ? (uint32_t)n : 0u;
-    const uint32_t b = fdiv(nn, a.div_p);
-    const uint32_t pix = nn - b * a.div_p.d;
-    const uint32_t oh = fdiv(pix, a.div_ow);
-    const uint32_t ow = pix - oh * a.div_ow.d;
-    ih0 = (int)oh * a.sH - a.pH;
-    iw0 = (int)ow * a.sW - a.pW;
-    cbase = (int)b * a.IC * a.H * a.W + ih0 * a.W + iw0;
+    const uint32_t b = fdiv(nn, args.div_p);
+    const uint32_t pix = nn - b * args.div_p.d;
+    const uint32_t oh = fdiv(pix, args.div_ow);
+    const uint32_t ow = pix - oh * args.div_ow.d;
+    ih0 = (int)oh * args.sH - args.pH;
+    iw0 = cok ? (int)ow * args.sW - args.pW : -(args.dW * (args.KW - 1)) - 1;
+    cbase = (int)b * args.IC * args.H * args.W + ih0 * args.W + iw0;
   }
-  __device__ void load(const ConvArgs& a, int k0) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.x, a.x_elems);
+  __device__ void meta(int t) {
+    if (threadIdx.x < T::BK) {
+      const int kk = t * T::BK + (int)threadIdx.x;
+      int4 e;
+      if (kk < a->K) {
+        const uint32_t ic = fdiv((uint32_t)kk, a->div_khw);
+        const uint32_t rem = (uint32_t)kk - ic * a->div_khw.d;
+        const uint32_t kh = fdiv(rem, a->div_kw);
+        const uint32_t kw = rem - kh * a->div_kw.d;
+        e.y = (int)kh * a->dH;
+        e.z = (int)kw * a->dW;
+        e.x = (int)ic * a->H * a->W + e.y * a->W + e.z;
+      } else {
+        e.x = 0;
+        e.y = -(a->H + 2 * a->pH) - 1;
+        e.z = 0;
+      }
+      e.w = 0;
+      tbl[(t & 1) * T::BK + threadIdx.x] = e;
+    }
+  }
+  __device__ void load(int k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a->x, a->x_elems);
+    const int4* slot = tbl + ((k0 / T::BK) & 1) * T::BK;
+    // All table reads first, then branch-free address selection, so the
+    // NP global loads issue back to back.
+    int4 e[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) e[i] = slot[row0 + RPP * i];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const int kk = k0 + row0 + RPP * i;
-      const uint32_t ic = fdiv((uint32_t)kk, a.div_khw);
-      const uint32_t rem = (uint32_t)kk - ic * a.div_khw.d;
-      const uint32_t kh = fdiv(rem, a.div_kw);
-      const uint32_t kw = rem - kh * a.div_kw.d;
-      const int dh = (int)kh * a.dH, dw = (int)kw * a.dW;
-      const int off = (int)ic * a.H * a.W + dh * a.W + dw;
-      const bool ok = cok && kk < a.K && (unsigned)(ih0 + dh) < (unsigned)a.H &&
-                      (unsigned)(iw0 + dw) < (unsigned)a.W;
-      reg[i] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + off) * 4u : kOOB);
+      const unsigned ok = (unsigned)((unsigned)(ih0 + e[i].y) < (unsigned)a->H) &
+                          (unsigned)((unsigned)(iw0 + e[i].z) < (unsigned)a->W);
+      reg[i] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + e[i].x) * 4u : kOOB);
     }
   }
   __device__ void store(float* Bs) const {
@@ -74,18 +113,9 @@ struct ImColTileLoader {
   }
 };
 
-// Adapts the im2col loader to the (load(k0), store(buf)) shape of mainloop.
-template <class T>
-struct ImColBound {
-  ImColTileLoader<T> ld;
-  const ConvArgs* a;
-  __device__ void load(int k0) { ld.load(*a, k0); }
-  __device__ void store(float* Bs) const { ld.store(Bs); }
-};
-
 template <class T, int VA>
 __global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
-  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
@@ -95,9 +125,8 @@ __global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
 
   RowTileLoader<T, VA> al;
   al.init(p.w, m0, p.M, p.K);
-  ImColBound<T> bl;
-  bl.a = &p;
-  bl.ld.init(p, n0);
+  ImColTileLoader<T> bl;
+  bl.init(p, n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
   Accum<T> acc;
   mainloop<T>(acc, al, bl, p.K, smem, wm0, wn0, lane);
 
@@ -123,7 +152,7 @@ __global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
   }
 }
 
-typedef Tile<128, 128, 32, 2, 2> ConvTile;
+typedef Tile<128, 128, 32, 2, 4> ConvTile;
 
 template <class T, int VA>
 static hipError_t launch_t(const ConvArgs& a, int nblocks, hipStream_t s) {

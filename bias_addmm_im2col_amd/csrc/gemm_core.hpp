@@ -80,7 +80,10 @@ struct Tile {
   static constexpr int AS = BK + 4, BS = BN + 8;
   static constexpr int A_FLOATS = BM * AS, B_FLOATS = BK * BS;
   static constexpr int STAGE = A_FLOATS + B_FLOATS;
-  static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  // Per-k-tile loader metadata (two slots of BK int4 entries) after the
+  // two operand stages.
+  static constexpr int META_INTS = 2 * BK * 4;
+  static constexpr int SMEM_FLOATS = 2 * STAGE + META_INTS;
   static_assert(BK % 8 == 0, "BK must be a multiple of 8");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
   static_assert(BN % 16 == 0, "B padding assumes BN % 16 == 0");
@@ -92,6 +95,7 @@ struct Tile {
 // (mat1 [M,K]; the conv weight viewed as [OC, IC*KH*KW]).
 template <class T, int VEC>
 struct RowTileLoader {
+  static constexpr bool kHasMeta = false;
   static constexpr int CPR = T::BK / VEC;
   static constexpr int NCH = T::BM * CPR / T::NT;
   static_assert((T::BM * CPR) % T::NT == 0, "A tile must split evenly over threads");
@@ -128,6 +132,7 @@ struct RowTileLoader {
 // B tile from a row-major [K][N] matrix (mat2, read as mat2[k*N + n]).
 template <class T, int VEC>
 struct ColTileLoader {
+  static constexpr bool kHasMeta = false;
   static constexpr int CPR = T::BN / VEC;
   static constexpr int NCH = T::BK * CPR / T::NT;
   static_assert((T::BK * CPR) % T::NT == 0, "B tile must split evenly over threads");
@@ -161,6 +166,7 @@ struct ColTileLoader {
       *reinterpret_cast<V*>(&Bs[r * T::BS + c]) = reg[i];
     }
   }
+  __device__ void meta(int) {}
 };
 
 // ----------------------------------------------------------- contraction
@@ -205,13 +211,22 @@ __device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
 }
 
 // The k loop: prefetch k-tile t+1 into registers, run the MFMAs on tile t
-// from LDS, write t+1 to the other LDS buffer, one barrier.
+// from LDS, write t+1 to the other LDS buffer, one barrier.  A loader may
+// also keep per-k-tile metadata in LDS: meta(t) writes the metadata of
+// tile t into slot t % 2 and is called two tiles ahead, so that slot is
+// free (its last reader, load(t-2), ran before the previous barrier) and
+// visible to load(t) after the next barrier.
 template <class T, class AL, class BL>
 __device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int K, float* smem, int wm0,
                                 int wn0, int lane) {
   acc.zero();
   const int nt = (K + T::BK - 1) / T::BK;
   if (nt == 0) return;
+  if (BL::kHasMeta) {
+    bl.meta(0);
+    bl.meta(1);
+    __syncthreads();
+  }
   al.load(0);
   bl.load(0);
   al.store(smem);
@@ -225,6 +240,7 @@ __device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int K, float* sme
       al.load((t + 1) * T::BK);
       bl.load((t + 1) * T::BK);
     }
+    if (BL::kHasMeta && t + 2 < nt) bl.meta(t + 2);
     mma_tile<T>(acc, cur, cur + T::A_FLOATS, wm0, wn0, lane);
     if (more) {
       al.store(nxt);

@@ -103,8 +103,8 @@ baim_status conv2d_gemm_f32(float* out, const float* input,
 /*
  * baim_conv2d_out_hw: the output size of the conv above,
  * OH = floor((H + 2*pH - dH*(KH-1) - 1) / sH) + 1 and likewise OW (the
- * pages print no formula; this is the standard one, which gives the stated
- * [1,128,192,192] output of a 7x7/stride-4/pad-3 stem on 768x768).
+ * pages print no formula; this is the standard one, which gives a 192x192
+ * output for a 7x7, stride-4, pad-3 stem on a 768x768 input).
  * Writes *OH and *OW and returns BAIM_OK, or BAIM_ERR_SHAPE (with *OH, *OW
  * set to 0) if an argument is out of range or the output would be empty;
  * BAIM_ERR_NULL if OH or OW is NULL.  Host-only; touches no GPU.
