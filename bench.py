@@ -32,15 +32,16 @@ METRIC = "fp32 TFLOP/s (addmm, im2col conv2d) and % of MI355X fp32 MFMA peak"
 STEP_CASES = ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2",
               "up_proj_4096x1024x4096", "down_proj_4096x4096x1024",
               "ragged_577x1024x4096_full_self"]
-KERNEL_SOURCES = ["gemm_core.hpp", "index_math.hpp", "addmm.hip", "conv2d_gemm.hip"]
+KERNEL_SOURCES = ["gemm_core.hpp", "index_math.hpp", "tile_select.hpp", "tile_select.cpp",
+                  "addmm.hip", "conv2d_gemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -73,7 +74,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_op: str):
+def load_traffic(kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, only
     while the kernel sources are the ones the counters were taken on."""
     try:
@@ -83,7 +84,7 @@ def load_traffic(kernel_op: str):
         return None
     if t.get("kernel_source_sha") != kernel_source_hash():
         return None
-    entry = t.get("ops", {}).get(kernel_op)
+    entry = t.get("kernels", {}).get(kernel)
     return None if entry is None else entry.get("bytes_per_launch")
 
 
@@ -94,6 +95,13 @@ class Case:
         self.c = c
         self.op = c.kind
         self.flops = c.flops
+        M, N, K = (c.M, c.N, c.K) if c.kind == "addmm" else c.gemm_mnk
+        p = baim.gemm_plan(M, N, K)
+        self.plan = p
+        # one kernel instance per (op, block tile, waves, wave groups, K split)
+        self.kernel = (f"baim::{'addmm_kernel' if c.kind == 'addmm' else 'conv2d_gemm_kernel'}"
+                       f"<Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
+                       f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else ""))
         if c.kind == "addmm":
             a, b, s = I.addmm_inputs(c)
             self.host = (a, b, s)
@@ -206,19 +214,20 @@ def main():
     value = flops_step * args.steps / wall / 1e12
 
     case_rows = []
-    op_time = {}
-    op_flops = {}
+    k_time = {}
+    k_flops = {}
+    k_launch = {}
     for cs, ms in zip(cases, per_case_ms):
         tf = cs.flops / (ms * 1e-3) / 1e12
-        case_rows.append({"case": cs.name, "op": cs.op, "us": round(ms * 1e3, 2),
+        case_rows.append({"case": cs.name, "op": cs.op, "kernel": cs.kernel, "us": round(ms * 1e3, 2),
                           "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)})
-        op_time[cs.op] = op_time.get(cs.op, 0.0) + ms
-        op_flops[cs.op] = op_flops.get(cs.op, 0) + cs.flops
-    dom = max(op_time, key=op_time.get)
-    achieved = op_flops[dom] / (op_time[dom] * 1e-3) / 1e12
-    n_launch = sum(1 for cs in cases if cs.op == dom)
+        k_time[cs.kernel] = k_time.get(cs.kernel, 0.0) + ms
+        k_flops[cs.kernel] = k_flops.get(cs.kernel, 0) + cs.flops
+        k_launch[cs.kernel] = k_launch.get(cs.kernel, 0) + 1
+    dom = max(k_time, key=k_time.get)
+    achieved = k_flops[dom] / (k_time[dom] * 1e-3) / 1e12
+    n_launch = k_launch[dom]
     traffic = load_traffic(dom)
-    kernel_names = {"addmm": "baim::addmm_kernel", "conv": "baim::conv2d_gemm_kernel"}
 
     cpu = cpu_baseline(cases, args.cpu_seconds)
 
@@ -245,15 +254,15 @@ def main():
         "cases": case_rows,
         "roofline": {
             "bound": "mfma",
-            "kernel": kernel_names[dom],
+            "kernel": dom,
             "achieved": round(achieved, 3),
             "peak": PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
             "launches_per_step": n_launch,
-            "flops_per_launch_avg": op_flops[dom] // n_launch,
-            "avg_launch_us": round(op_time[dom] / n_launch * 1e3, 2),
+            "flops_per_launch_avg": k_flops[dom] // n_launch,
+            "avg_launch_us": round(k_time[dom] / n_launch * 1e3, 2),
         },
         "cpu_baseline": cpu,
     }

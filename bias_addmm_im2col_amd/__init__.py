@@ -20,7 +20,7 @@ from __future__ import annotations
 
 from . import _capi
 
-__all__ = ["addmm", "conv2d", "addmm_f32", "conv2d_gemm_f32", "conv2d_out_hw",
+__all__ = ["addmm", "conv2d", "addmm_f32", "conv2d_gemm_f32", "conv2d_out_hw", "gemm_plan",
            "BaimError", "library_path"]
 
 
@@ -138,6 +138,14 @@ def addmm(self, mat1, mat2, *, beta=1, alpha=1):
     _dev_f32(mat2, "mat2")
     out = torch.empty((mat1.shape[0], mat2.shape[1]), dtype=torch.float32, device=mat1.device)
     return addmm_f32(out, self, mat1, mat2, beta, alpha)
+
+
+def gemm_plan(M, N, K):
+    """The block tile the library uses for an M x N x K GEMM (dict with bm,
+    bn, bk, waves, kgroups, splits).  Host-only."""
+    st, plan = _capi.gemm_plan(M, N, K)
+    _check(st)
+    return plan
 
 
 def conv2d_out_hw(H, W, KH, KW, stride=1, padding=0, dilation=1):

@@ -25,8 +25,8 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/baim.h declares.
-EXPORTS = ("addmm_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_last_error",
-           "baim_version")
+EXPORTS = ("addmm_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_gemm_plan",
+           "baim_last_error", "baim_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -50,6 +50,8 @@ def lib():
     L.conv2d_gemm_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
     L.baim_conv2d_out_hw.restype = ctypes.c_int
+    L.baim_gemm_plan.argtypes = [_i64] * 3 + [ctypes.POINTER(ctypes.c_int)] * 6
+    L.baim_gemm_plan.restype = ctypes.c_int
     L.baim_last_error.argtypes = []
     L.baim_last_error.restype = ctypes.c_char_p
     L.baim_version.argtypes = []
@@ -70,6 +72,14 @@ def conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH
                     groups, stream) -> int:
     return lib().conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW,
                                  dH, dW, groups, stream)
+
+
+def gemm_plan(M, N, K):
+    """(status, dict) with the tile the library picks for an M x N x K GEMM."""
+    outs = [ctypes.c_int(0) for _ in range(6)]
+    st = lib().baim_gemm_plan(M, N, K, *[ctypes.byref(o) for o in outs])
+    keys = ("bm", "bn", "bk", "waves", "kgroups", "splits")
+    return st, {k: o.value for k, o in zip(keys, outs)}
 
 
 def conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW):

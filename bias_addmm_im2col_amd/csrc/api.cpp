@@ -8,11 +8,13 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <string>
 
 #include "baim.h"
 #include "launch.hpp"
+#include "tile_select.hpp"
 
 namespace {
 
@@ -70,6 +72,24 @@ extern "C" {
 int baim_version(void) { return 100; }
 
 const char* baim_last_error(void) { return g_err.c_str(); }
+
+baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn, int* bk,
+                           int* waves, int* kgroups, int* splits) {
+  g_err.clear();
+  if (!bm || !bn || !bk || !waves || !kgroups || !splits)
+    return fail(BAIM_ERR_NULL, "baim_gemm_plan: output pointers must not be NULL");
+  if (M < 0 || N < 0 || K < 0) return fail(BAIM_ERR_SHAPE, "baim_gemm_plan: sizes must be >= 0");
+  if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "baim_gemm_plan: size too large");
+  const baim::GemmPlan p = baim::plan_gemm((int)M, (int)N, (int)K, getenv("BAIM_TILE"));
+  *bm = baim::kTileBM[p.cfg];
+  *bn = baim::kTileBN[p.cfg];
+  *bk = baim::kTileBK[p.cfg];
+  *waves = baim::kTileWaves[p.cfg];
+  *kgroups = baim::kTileKGroups[p.cfg];
+  *splits = p.splits;
+  return BAIM_OK;
+}
 
 baim_status baim_conv2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW, int64_t sH,
                                int64_t sW, int64_t pH, int64_t pW, int64_t dH, int64_t dW,

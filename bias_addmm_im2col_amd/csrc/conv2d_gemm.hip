@@ -11,8 +11,11 @@
 // per thread; the row decode kk -> (ic, kh, kw) is uniform across a wave
 // (a wave loads 64 consecutive columns of one row) and runs on the scalar
 // unit with multiply-high division.
+#include <stdlib.h>
+
 #include "gemm_core.hpp"
 #include "launch.hpp"
+#include "tile_select.hpp"
 
 namespace baim {
 
@@ -25,7 +28,7 @@ struct ConvArgs {
   int M, N, K;
   int x_elems;  // B*IC*H*W
   FastDiv div_khw, div_kw, div_p, div_ow;
-  int tiles_m, tiles_n, group_m;
+  int tiles_m, tiles_n, group_m, splits, kt_per_split;
 };
 
 // B operand: the implicit im2col tile B[kk, n] for kk in [k0, k0+BK),
@@ -113,30 +116,31 @@ struct ImColTileLoader {
   }
 };
 
-template <class T, int VA>
+template <class T, int VA, bool SPLIT>
 __global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const BlockWork w = block_work(p.tiles_m, p.tiles_n, p.group_m, SPLIT ? p.splits : 1,
+                                 p.kt_per_split, p.K, T::BM, T::BN, T::BK);
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm0 = (wave / T::WN) * T::WTM, wn0 = (wave % T::WN) * T::WTN;
+  const WaveSlot ws = wave_slot<T>();
+  const int wm0 = ws.wm0, wn0 = ws.wn0;
 
   RowTileLoader<T, VA> al;
-  al.init(p.w, m0, p.M, p.K);
+  al.init(p.w, w.m0, p.M, p.K);
   ImColTileLoader<T> bl;
-  bl.init(p, n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
+  bl.init(p, w.n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, p.K, smem, wm0, wn0, lane);
+  mainloop<T>(acc, al, bl, w.t_begin, w.t_end, smem, ws, lane);
+  if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // Epilogue: + bias[oc], NCHW store: column n = (b, pix) goes to
-  // out[b, oc, pix] = out[(b*OC + oc)*P + pix], P = OH*OW.
+  // out[b, oc, pix] = out[(b*OC + oc)*P + pix], P = OH*OW.  A K slice adds
+  // its partial sum instead (the bias is already in out).
   const int c = lane & 31;
   const uint32_t P = p.div_p.d;
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
-    const int n = n0 + wn0 + 32 * j + c;
+    const int n = w.n0 + wn0 + 32 * j + c;
     if (n >= p.N) continue;
     const uint32_t b = fdiv((uint32_t)n, p.div_p);
     const size_t obase = (size_t)b * p.OC * P + ((uint32_t)n - b * P);
@@ -144,24 +148,85 @@ __global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int oc = m0 + wm0 + 32 * i + acc_row(r, lane);
+        const int oc = w.m0 + wm0 + 32 * i + acc_row(r, lane);
         if (oc >= p.M) continue;
-        const float bv = p.bias ? p.bias[oc] : 0.0f;
-        p.out[obase + (size_t)oc * P] = acc.c[i][j][r] + bv;
+        float* o = &p.out[obase + (size_t)oc * P];
+        if (SPLIT) {
+          unsafeAtomicAdd(o, acc.c[i][j][r]);
+        } else {
+          *o = acc.c[i][j][r] + (p.bias ? p.bias[oc] : 0.0f);
+        }
       }
   }
 }
 
-typedef Tile<128, 128, 32, 2, 4> ConvTile;
+// out[b, oc, pix] = bias[oc] (or 0), before the K slices add their partial
+// products.
+__global__ __launch_bounds__(256) void conv_init_kernel(float* out, const float* bias,
+                                                        uint32_t total, FastDiv div_p,
+                                                        uint32_t OC) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+    float v = 0.0f;
+    if (bias) v = bias[fdiv(i, div_p) % OC];
+    out[i] = v;
+  }
+}
 
-template <class T, int VA>
+typedef Tile<128, 128, 32, 2, 4> T128x128;
+typedef Tile<128, 64, 32, 4, 2> T128x64;
+typedef Tile<64, 128, 32, 2, 4> T64x128;
+typedef Tile<64, 64, 32, 2, 2> T64x64;
+typedef Tile<128, 128, 64, 2, 4, 2> T128x128K2;
+typedef Tile<128, 64, 64, 4, 2, 2> T128x64K2;
+typedef Tile<64, 64, 64, 2, 2, 2> T64x64K2;
+typedef Tile<64, 64, 128, 2, 2, 4> T64x64K4;
+
+// The host planner's table must describe exactly these tiles.
+template <class T>
+constexpr bool same_tile(int cfg) {
+  return T::BM == kTileBM[cfg] && T::BN == kTileBN[cfg] && T::BK == kTileBK[cfg] &&
+         T::NT == 64 * kTileWaves[cfg] && T::WK == kTileKGroups[cfg];
+}
+static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x64) &&
+                  same_tile<T64x128>(TILE_64x128) && same_tile<T64x64>(TILE_64x64) &&
+                  same_tile<T128x128K2>(TILE_128x128_K2) && same_tile<T128x64K2>(TILE_128x64_K2) &&
+                  same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
+              "tile table out of sync with the compiled tiles");
+
+template <class T, int VA, bool SPLIT>
 static hipError_t launch_t(const ConvArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA, SPLIT>), dim3(nblocks), dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
+template <class T, bool SPLIT>
+static hipError_t launch_vec(const ConvArgs& a, int nblocks, bool va, hipStream_t s) {
+  return va ? launch_t<T, 4, SPLIT>(a, nblocks, s) : launch_t<T, 1, SPLIT>(a, nblocks, s);
+}
+
+template <bool SPLIT>
+static hipError_t launch_cfg(int cfg, const ConvArgs& a, int nblocks, bool va, hipStream_t s) {
+  switch (cfg) {
+    case TILE_128x64:
+      return launch_vec<T128x64, SPLIT>(a, nblocks, va, s);
+    case TILE_64x128:
+      return launch_vec<T64x128, SPLIT>(a, nblocks, va, s);
+    case TILE_64x64:
+      return launch_vec<T64x64, SPLIT>(a, nblocks, va, s);
+    case TILE_128x128_K2:
+      return launch_vec<T128x128K2, SPLIT>(a, nblocks, va, s);
+    case TILE_128x64_K2:
+      return launch_vec<T128x64K2, SPLIT>(a, nblocks, va, s);
+    case TILE_64x64_K2:
+      return launch_vec<T64x64K2, SPLIT>(a, nblocks, va, s);
+    case TILE_64x64_K4:
+      return launch_vec<T64x64K4, SPLIT>(a, nblocks, va, s);
+    default:
+      return launch_vec<T128x128, SPLIT>(a, nblocks, va, s);
+  }
+}
+
 hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
-  typedef ConvTile T;
   ConvArgs a;
   a.out = q.out;
   a.x = q.x;
@@ -189,13 +254,24 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.div_kw = make_fastdiv((uint32_t)q.KW);
   a.div_p = make_fastdiv((uint32_t)(q.OH * q.OW));
   a.div_ow = make_fastdiv((uint32_t)q.OW);
-  a.tiles_m = (a.M + T::BM - 1) / T::BM;
-  a.tiles_n = (a.N + T::BN - 1) / T::BN;
+  const GemmPlan plan = plan_gemm(a.M, a.N, a.K, getenv("BAIM_TILE"));
+  a.tiles_m = plan.tiles_m;
+  a.tiles_n = plan.tiles_n;
   a.group_m = 8;
-  const int nblocks = a.tiles_m * a.tiles_n;
+  a.splits = plan.splits;
+  a.kt_per_split = plan.kt_per_split;
+  const int nblocks = (int)plan_blocks(plan);
   const bool va = a.K % 4 == 0 && ((uintptr_t)q.w & 15) == 0;
-  if (va) return launch_t<T, 4>(a, nblocks, stream);
-  return launch_t<T, 1>(a, nblocks, stream);
+  if (plan.splits > 1) {
+    const uint32_t total = (uint32_t)a.M * (uint32_t)a.N;
+    const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
+    hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias, total,
+                       a.div_p, (uint32_t)q.OC);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_cfg<true>(plan.cfg, a, nblocks, va, stream);
+  }
+  return launch_cfg<false>(plan.cfg, a, nblocks, va, stream);
 }
 
 }  // namespace baim

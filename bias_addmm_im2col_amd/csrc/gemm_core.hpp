@@ -68,12 +68,17 @@ template <> struct Vec<4> {
   }
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+// Block tile BM x BN x BK computed by WM x WN x WK waves: WM x WN waves
+// split the output tile, and WK groups of them split each k-tile (group g
+// takes k in [g*BK/WK, (g+1)*BK/WK)); the groups' partial tiles are summed
+// through LDS at the end, in group order.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_ = 1>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr int NT = 64 * WM * WN;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, WK = WK_;
+  static constexpr int NT = 64 * WM * WN * WK;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int BKW = BK / WK;  // k per wave group and k-tile
   // LDS row strides (floats).  A is [BM][BK+4]: 16-byte reads of 32
   // consecutive rows spread over all banks.  B is [BK][BN+8]: rows four
   // apart start 32 banks apart.
@@ -84,10 +89,24 @@ struct Tile {
   // two operand stages.
   static constexpr int META_INTS = 2 * BK * 4;
   static constexpr int SMEM_FLOATS = 2 * STAGE + META_INTS;
-  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert(BKW % 8 == 0, "each wave group needs a multiple of 8 k per tile");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
   static_assert(BN % 16 == 0, "B padding assumes BN % 16 == 0");
+  static_assert(NT <= 1024, "at most 1024 threads per block");
+  static_assert((WK - 1) * BM * BN <= 2 * STAGE, "k-group reduction must fit in the stages");
 };
+
+// Where a wave works: its output sub-tile origin and its k offset.
+struct WaveSlot {
+  int wm0, wn0, kofs, kgroup;
+};
+
+template <class T>
+__device__ inline WaveSlot wave_slot() {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave / (T::WM * T::WN), wmn = wave % (T::WM * T::WN);
+  return WaveSlot{(wmn / T::WN) * T::WTM, (wmn % T::WN) * T::WTN, kg * T::BKW, kg};
+}
 
 // ---------------------------------------------------------------- loaders
 
@@ -184,22 +203,24 @@ struct Accum {
   }
 };
 
-// One k-tile: BK/2 MFMA steps for every 32x32 block of the wave's sub-tile.
+// One k-tile: for the wave's k range [kofs, kofs + BKW), BKW/2 MFMA steps
+// for every 32x32 block of the wave's sub-tile.
 template <class T>
-__device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs, int wm0,
-                                int wn0, int lane) {
+__device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
+                                const WaveSlot& ws, int lane) {
   const int c = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int g = 0; g < T::BK / 8; ++g) {
+  for (int g = 0; g < T::BKW / 8; ++g) {
+    const int k = ws.kofs + 8 * g + 4 * h;
     f32x4 a[T::FM];
     float b[T::FN][4];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
-      a[i] = *reinterpret_cast<const f32x4*>(&As[(wm0 + 32 * i + c) * T::AS + 8 * g + 4 * h]);
+      a[i] = *reinterpret_cast<const f32x4*>(&As[(ws.wm0 + 32 * i + c) * T::AS + k]);
 #pragma unroll
     for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * T::BS + wn0 + 32 * j + c];
+      for (int s = 0; s < 4; ++s) b[j][s] = Bs[(k + s) * T::BS + ws.wn0 + 32 * j + c];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -210,44 +231,102 @@ __device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
   }
 }
 
-// The k loop: prefetch k-tile t+1 into registers, run the MFMAs on tile t
-// from LDS, write t+1 to the other LDS buffer, one barrier.  A loader may
-// also keep per-k-tile metadata in LDS: meta(t) writes the metadata of
-// tile t into slot t % 2 and is called two tiles ahead, so that slot is
-// free (its last reader, load(t-2), ran before the previous barrier) and
-// visible to load(t) after the next barrier.
+// Sum the k groups' partial tiles into group 0 (group order, so the result
+// does not depend on timing).  Returns true for the waves that hold the
+// final tile and run the epilogue.  Called by every thread after mainloop.
+template <class T>
+__device__ inline bool reduce_k_groups(Accum<T>& acc, float* smem, const WaveSlot& ws,
+                                       int lane) {
+  if (T::WK == 1) return true;
+  constexpr int REGS = T::FM * T::FN * 16;
+  constexpr int WAVE_FLOATS = REGS * 64;  // one wave's accumulators
+  constexpr int GROUP_FLOATS = T::WM * T::WN * WAVE_FLOATS;
+  const int wmn = (threadIdx.x >> 6) % (T::WM * T::WN);
+  if (ws.kgroup > 0) {
+    float* dst = smem + (ws.kgroup - 1) * GROUP_FLOATS + wmn * WAVE_FLOATS + lane;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[((i * T::FN + j) * 16 + r) * 64] = acc.c[i][j][r];
+  }
+  __syncthreads();
+  if (ws.kgroup > 0) return false;
+#pragma unroll 1
+  for (int g = 1; g < T::WK; ++g) {
+    const float* src = smem + (g - 1) * GROUP_FLOATS + wmn * WAVE_FLOATS + lane;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc.c[i][j][r] += src[((i * T::FN + j) * 16 + r) * 64];
+  }
+  return true;
+}
+
+// The k loop over k-tiles [t_begin, t_end): prefetch k-tile t+1 into
+// registers, run the MFMAs on tile t from LDS, write t+1 to the other LDS
+// buffer, one barrier.  A loader may also keep per-k-tile metadata in LDS:
+// meta(t) writes the metadata of tile t into slot t % 2 and is called two
+// tiles ahead, so that slot is free (its last reader, load(t-2), ran before
+// the previous barrier) and visible to load(t) after the next barrier.
 template <class T, class AL, class BL>
-__device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int K, float* smem, int wm0,
-                                int wn0, int lane) {
+__device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
+                                float* smem, const WaveSlot& ws, int lane) {
   acc.zero();
-  const int nt = (K + T::BK - 1) / T::BK;
-  if (nt == 0) return;
+  if (t_begin >= t_end) return;
   if (BL::kHasMeta) {
-    bl.meta(0);
-    bl.meta(1);
+    bl.meta(t_begin);
+    bl.meta(t_begin + 1);
     __syncthreads();
   }
-  al.load(0);
-  bl.load(0);
+  al.load(t_begin * T::BK);
+  bl.load(t_begin * T::BK);
   al.store(smem);
   bl.store(smem + T::A_FLOATS);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    float* cur = smem + (t & 1) * T::STAGE;
-    float* nxt = smem + ((t + 1) & 1) * T::STAGE;
-    const bool more = t + 1 < nt;
+  for (int t = t_begin; t < t_end; ++t) {
+    const int i = t - t_begin;
+    float* cur = smem + (i & 1) * T::STAGE;
+    float* nxt = smem + ((i + 1) & 1) * T::STAGE;
+    const bool more = t + 1 < t_end;
     if (more) {
       al.load((t + 1) * T::BK);
       bl.load((t + 1) * T::BK);
     }
-    if (BL::kHasMeta && t + 2 < nt) bl.meta(t + 2);
-    mma_tile<T>(acc, cur, cur + T::A_FLOATS, wm0, wn0, lane);
+    if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
+    mma_tile<T>(acc, cur, cur + T::A_FLOATS, ws, lane);
     if (more) {
       al.store(nxt);
       bl.store(nxt + T::A_FLOATS);
     }
     __syncthreads();
   }
+}
+
+// Which output tile and which K slice a block computes.  Blocks are laid
+// out slice-major (all tiles of slice 0, then slice 1, ...) over the
+// XCD-remapped ids, so neighbouring tiles of the same slice share an XCD.
+struct BlockWork {
+  int m0, n0, t_begin, t_end;
+};
+
+__device__ inline BlockWork block_work(int tiles_m, int tiles_n, int group_m, int splits,
+                                       int kt_per_split, int K, int BM, int BN, int BK) {
+  const int lid = xcd_linear(blockIdx.x, gridDim.x);
+  const int ntiles = tiles_m * tiles_n;
+  const int z = lid / ntiles;
+  int tm, tn;
+  grouped_tile(lid - z * ntiles, tiles_m, tiles_n, group_m, tm, tn);
+  const int nkt = (K + BK - 1) / BK;
+  BlockWork w;
+  w.m0 = tm * BM;
+  w.n0 = tn * BN;
+  w.t_begin = splits > 1 ? z * kt_per_split : 0;
+  w.t_end = splits > 1 ? min(nkt, w.t_begin + kt_per_split) : nkt;
+  return w;
 }
 
 // Row of accumulator register j of a 32x32 block, relative to the block.

@@ -35,15 +35,19 @@ inline FastDiv make_fastdiv(uint32_t d) {
   return FastDiv{d, (uint32_t)m, l};
 }
 
-// Block -> output tile.  The hardware hands workgroup i to XCD i % 8; the
-// remap gives each XCD a contiguous run of logical ids, and the grouped
-// raster walks group_m tile-rows at a time, so neighbouring tiles (which
-// share A rows and B columns) run on the same XCD and share its L2.
-BAIM_HD inline void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int group_m,
-                                int& tm, int& tn) {
+// Block -> output tile, in two steps.  The hardware hands workgroup i to
+// XCD i % 8; xcd_linear gives each XCD a contiguous run of logical ids.
+// grouped_tile then walks group_m tile-rows at a time, so neighbouring
+// tiles (which share A rows and B columns) run on the same XCD and share
+// its L2.
+BAIM_HD inline int xcd_linear(int bid, int nblocks) {
   const int q = nblocks >> 3, r = nblocks & 7;
   const int x = bid & 7, i = bid >> 3;
-  const int lid = x * q + (x < r ? x : r) + i;
+  return x * q + (x < r ? x : r) + i;
+}
+
+BAIM_HD inline void grouped_tile(int lid, int tiles_m, int tiles_n, int group_m, int& tm,
+                                 int& tn) {
   const int per_group = group_m * tiles_n;
   const int g = lid / per_group;
   const int first_m = g * group_m;
@@ -52,6 +56,11 @@ BAIM_HD inline void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, 
   const int in_g = lid - g * per_group;
   tm = first_m + in_g % gsz;
   tn = in_g / gsz;
+}
+
+BAIM_HD inline void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int group_m,
+                                int& tm, int& tn) {
+  grouped_tile(xcd_linear(bid, nblocks), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace baim

@@ -1,0 +1,90 @@
+// tile_select.cpp -- see tile_select.hpp.
+//
+// The choice follows how the chip fills (256 CUs) and how deep K is; the
+// thresholds come from timing every configuration on the workload shapes
+// (large / down / up projections, FFN, ragged 577-row, 3x3 and 7x7 convs):
+//  * >= 512 tiles of 128x128: the 128x128 tile (most reuse per byte).
+//  * >= 192 such tiles and deep K: 128x128 with each k-tile split over two
+//    wave groups (16 waves per block: one block per CU still keeps four
+//    waves per SIMD).
+//  * >= 256 such tiles and moderate K: half-size tiles (more blocks).
+//  * many 64x64 tiles, or very shallow K: 64x64.
+//  * few tiles and deep K: 64x64 with 2 or 4 wave groups per tile.
+//  * so few tiles that one per CU is out of reach, with deep K: K is split
+//    across blocks, which add partial tiles into a pre-initialised output
+//    with atomics.  Only this last case is not bit-reproducible run to run.
+#include "tile_select.hpp"
+
+#include <stdlib.h>
+
+namespace baim {
+
+namespace {
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+GemmPlan make(int cfg, int M, int N, int K, int splits) {
+  GemmPlan p;
+  p.cfg = cfg;
+  p.tiles_m = cdiv(M, kTileBM[cfg]);
+  p.tiles_n = cdiv(N, kTileBN[cfg]);
+  const int nkt = cdiv(K, kTileBK[cfg]);
+  if (splits < 1) splits = 1;
+  if (splits > nkt) splits = nkt > 0 ? nkt : 1;
+  p.kt_per_split = nkt > 0 ? cdiv(nkt, splits) : 0;
+  // drop slices that would be empty after rounding up the slice length
+  p.splits = p.kt_per_split > 0 ? cdiv(nkt, p.kt_per_split) : 1;
+  return p;
+}
+
+int64_t tiles_of(int cfg, int M, int N) {
+  return (int64_t)cdiv(M, kTileBM[cfg]) * cdiv(N, kTileBN[cfg]);
+}
+
+bool parse_override(const char* s, int* cfg, int* splits) {
+  if (!s || !*s) return false;
+  char* end = nullptr;
+  const long c = strtol(s, &end, 10);
+  if (end == s || c < 0 || c >= TILE_NCFG) return false;
+  long k = 1;
+  if (*end == ',') {
+    const char* t = end + 1;
+    k = strtol(t, &end, 10);
+    if (end == t || k < 1 || k > 64) return false;
+  }
+  if (*end != '\0') return false;
+  *cfg = (int)c;
+  *splits = (int)k;
+  return true;
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
+  int cfg = 0, splits = 1;
+  if (parse_override(override_spec, &cfg, &splits)) return make(cfg, M, N, K, splits);
+
+  const int nkt = cdiv(K, 32);  // k-tiles of depth 32
+  const int64_t t128 = tiles_of(TILE_128x128, M, N);
+  if (t128 >= 2 * kNumCUs) return make(TILE_128x128, M, N, K, 1);
+  if (t128 >= (3 * kNumCUs) / 4 && nkt >= 48) return make(TILE_128x128_K2, M, N, K, 1);
+  if (t128 >= kNumCUs && nkt > 8) {
+    // Half-size tiles: the orientation that wastes less of a ragged edge;
+    // on a tie the 64-row tile.
+    const int64_t t_wide = tiles_of(TILE_128x64, M, N), t_tall = tiles_of(TILE_64x128, M, N);
+    return make(t_wide < t_tall ? TILE_128x64 : TILE_64x128, M, N, K, 1);
+  }
+  const int64_t t64 = tiles_of(TILE_64x64, M, N);
+  if (t64 >= 2 * kNumCUs || nkt <= 8) return make(TILE_64x64, M, N, K, 1);
+  if (t64 >= kNumCUs / 4 || nkt < 64)
+    return make(nkt >= 64 ? TILE_64x64_K4 : (nkt >= 32 ? TILE_64x64_K2 : TILE_64x64), M, N, K, 1);
+  // Fewer than a quarter of the CUs would get a tile: split K (depth-128
+  // k-tiles of the 4-group 64x64 tile) so tiles * splits covers the CUs,
+  // keeping at least 8 k-tiles per slice.
+  const int nkt128 = cdiv(K, 128);
+  int s = (int)((kNumCUs + t64 - 1) / t64);
+  if (s > nkt128 / 8) s = nkt128 / 8;
+  return make(TILE_64x64_K4, M, N, K, s < 1 ? 1 : s);
+}
+
+}  // namespace baim

@@ -126,6 +126,24 @@ def test_conv_out_hw(lib):
     assert lib.baim_conv2d_out_hw(1, 1, 1, 1, 1, 1, 0, 0, 1, 1, None, None) == _capi.BAIM_ERR_NULL
 
 
+def test_gemm_plan(lib, monkeypatch):
+    import bias_addmm_im2col_amd as baim
+    monkeypatch.delenv("BAIM_TILE", raising=False)
+    p = baim.gemm_plan(4096, 4096, 1024)
+    assert (p["bm"], p["bn"], p["bk"], p["waves"], p["kgroups"], p["splits"]) == (128, 128, 32, 8, 1, 1)
+    # every workload shape is planned without a cross-block K split
+    from bias_addmm_im2col_amd import inputs as I
+    for c in I.CASES.values():
+        M, N, K = (c.M, c.N, c.K) if c.kind == "addmm" else c.gemm_mnk
+        assert baim.gemm_plan(M, N, K)["splits"] == 1, c.name
+    monkeypatch.setenv("BAIM_TILE", "7,3")
+    p = baim.gemm_plan(300, 300, 30000)
+    assert (p["bm"], p["bn"], p["bk"], p["waves"], p["kgroups"], p["splits"]) == (64, 64, 128, 16, 4, 3)
+    st, _ = _capi.gemm_plan(-1, 2, 3)
+    assert st == _capi.BAIM_ERR_SHAPE
+    assert lib.baim_gemm_plan(1, 1, 1, None, None, None, None, None, None) == _capi.BAIM_ERR_NULL
+
+
 def test_python_layer_checks_before_the_library():
     """Dtype/device/shape errors of the torch wrapper, raised on the CPU."""
     import torch

@@ -259,3 +259,50 @@ def test_repeated_launches_are_deterministic():
     o1 = baim.addmm(dev(s), dev(a), dev(b)).cpu()
     o2 = baim.addmm(dev(s), dev(a), dev(b)).cpu()
     assert torch.equal(o1, o2)
+
+
+# ------------------------------------------- every tile config and K split
+# BAIM_TILE="cfg[,splits]" forces the host's choice: 0 = 128x128, 1 = 128x64,
+# 2 = 64x128, 3 = 64x64 (BK 32); 4 = 128x128, 5 = 128x64, 6 = 64x64 with
+# each k-tile split over 2 wave groups (BK 64); 7 = 64x64 over 4 groups
+# (BK 128); splits > 1 adds K slices into a pre-initialised out.
+TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "0,3", "1,2", "2,4", "3,5", "0,64",
+              "4,2", "6,3", "7,2"]
+
+
+@pytest.mark.parametrize("spec", TILE_SPECS)
+def test_addmm_forced_tile_configs(spec, monkeypatch):
+    monkeypatch.setenv("BAIM_TILE", spec)
+    for M, K, N, self_2d, beta, alpha in [(130, 300, 257, True, 0.5, 2.0),
+                                          (77, 1000, 65, False, 1.0, 1.0),
+                                          (256, 64, 128, False, 0.0, -1.0),
+                                          (33, 45, 70, True, 1.0, 1.0)]:
+        say(f"BAIM_TILE={spec} addmm_f32 M={M} K={K} N={N} self_2d={self_2d}")
+        a, b = gen((M, K), 40), gen((K, N), 41)
+        s = gen((M, N) if self_2d else (N,), 42)
+        out = run_addmm(a, b, s, beta, alpha)
+        check_close(out, oracle.addmm(a, b, s, self_2d, beta, alpha), K, alpha, f"addmm {spec}")
+    say(f"BAIM_TILE={spec} addmm_f32 integer")
+    a, b, s = gen((129, 520), 43, "I"), gen((520, 200), 44, "I"), gen((200,), 45, "I")
+    out = run_addmm(a, b, s, 2.0, 0.5)
+    check_bitwise(out, oracle.addmm(a, b, s, False, 2.0, 0.5), f"addmm integer {spec}")
+
+
+@pytest.mark.parametrize("spec", TILE_SPECS)
+def test_conv_forced_tile_configs(spec, monkeypatch):
+    monkeypatch.setenv("BAIM_TILE", spec)
+    for B, IC, H, W, OC, KH, KW, stride, pad, dil, has_bias in [
+            (2, 24, 23, 21, 136, 3, 3, 1, 1, 1, True),
+            (1, 3, 40, 44, 70, 7, 7, 4, 3, 1, False),
+            (2, 16, 15, 15, 24, 3, 3, 2, 1, 2, True)]:
+        say(f"BAIM_TILE={spec} conv2d_gemm_f32 x=[{B},{IC},{H},{W}] w=[{OC},{IC},{KH},{KW}] "
+            f"s={stride} p={pad} d={dil}")
+        x, w = gen((B, IC, H, W), 46), gen((OC, IC, KH, KW), 47)
+        bias = gen((OC,), 48) if has_bias else None
+        out = run_conv(x, w, bias, stride, pad, dil)
+        check_close(out, oracle.conv2d(x, w, bias, stride, pad, dil), IC * KH * KW, 1.0,
+                    f"conv {spec}")
+    say(f"BAIM_TILE={spec} conv2d_gemm_f32 integer")
+    x, w, bias = gen((2, 40, 19, 17), 49, "I"), gen((72, 40, 3, 3), 50, "I"), gen((72,), 51, "I")
+    out = run_conv(x, w, bias, 1, 1, 1)
+    check_bitwise(out, oracle.conv2d(x, w, bias, 1, 1, 1), f"conv integer {spec}")

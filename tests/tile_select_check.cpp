@@ -1,0 +1,50 @@
+// Host check of plan_gemm (built with g++ by tests/test_index_math.py):
+// every plan covers the problem, has no empty K slice, and honours a valid
+// override while ignoring a malformed one.
+#include <stdio.h>
+
+#include <initializer_list>
+
+#include "tile_select.hpp"
+
+using namespace baim;
+
+static int check(int M, int N, int K, const char* spec) {
+  const GemmPlan p = plan_gemm(M, N, K, spec);
+  const int nkt = (K + kTileBK[p.cfg] - 1) / kTileBK[p.cfg];
+  if (p.cfg < 0 || p.cfg >= TILE_NCFG) return printf("bad cfg %d\n", p.cfg), 1;
+  if ((int64_t)p.tiles_m * kTileBM[p.cfg] < M || (int64_t)(p.tiles_m - 1) * kTileBM[p.cfg] >= M)
+    return printf("tiles_m %d wrong for M=%d\n", p.tiles_m, M), 1;
+  if ((int64_t)p.tiles_n * kTileBN[p.cfg] < N || (int64_t)(p.tiles_n - 1) * kTileBN[p.cfg] >= N)
+    return printf("tiles_n %d wrong for N=%d\n", p.tiles_n, N), 1;
+  if (p.splits < 1) return printf("splits %d\n", p.splits), 1;
+  if (p.splits > 1) {
+    if ((int64_t)p.splits * p.kt_per_split < nkt || (int64_t)(p.splits - 1) * p.kt_per_split >= nkt)
+      return printf("slices %d x %d do not tile %d k-tiles\n", p.splits, p.kt_per_split, nkt), 1;
+  }
+  if (plan_blocks(p) >= (1ll << 31)) return printf("too many blocks\n"), 1;
+  return 0;
+}
+
+int main() {
+  int bad = 0;
+  const int sizes[] = {1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 577, 1000, 1024,
+                       2048, 3072, 3364, 4096, 12544, 36864};
+  const char* specs[] = {nullptr, "", "0", "1", "2", "3", "0,4", "3,2", "1,64", "9", "x", "0,",
+                         "0,0", "2,7x", "-1"};
+  for (int M : sizes)
+    for (int N : sizes)
+      for (int K : {0, 1, 31, 32, 147, 768, 1024, 2304, 4096, 100000})
+        for (const char* s : specs) bad += check(M, N, K, s);
+  // a valid override is honoured
+  const GemmPlan f = plan_gemm(4096, 4096, 4096, "3,4");
+  if (f.cfg != TILE_64x64 || f.splits != 4) bad += printf("override not honoured\n") > 0;
+  // a malformed override is ignored (same as no override)
+  const GemmPlan g = plan_gemm(300, 500, 700, "2,7x"), h = plan_gemm(300, 500, 700, nullptr);
+  if (g.cfg != h.cfg || g.splits != h.splits) bad += printf("bad override not ignored\n") > 0;
+  // K == 0 never splits
+  if (plan_gemm(8, 8, 0, "0,4").splits != 1) bad += printf("K=0 split\n") > 0;
+  if (bad) return 1;
+  printf("OK\n");
+  return 0;
+}
