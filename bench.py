@@ -101,7 +101,8 @@ class Case:
         # one kernel instance per (op, block tile, waves, wave groups, K split)
         self.kernel = (f"baim::{'addmm_kernel' if c.kind == 'addmm' else 'conv2d_gemm_kernel'}"
                        f"<Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
-                       f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else ""))
+                       f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else "")
+                       + (f" stream {p['stream_blocks']}" if p['stream_blocks'] > 0 else ""))
         if c.kind == "addmm":
             a, b, s = I.addmm_inputs(c)
             self.host = (a, b, s)

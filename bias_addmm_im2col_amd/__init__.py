@@ -141,8 +141,8 @@ def addmm(self, mat1, mat2, *, beta=1, alpha=1):
 
 
 def gemm_plan(M, N, K):
-    """The block tile the library uses for an M x N x K GEMM (dict with bm,
-    bn, bk, waves, kgroups, splits).  Host-only."""
+    """How the library computes an M x N x K GEMM (dict with bm, bn, bk,
+    waves, kgroups, splits, stream_blocks).  Host-only."""
     st, plan = _capi.gemm_plan(M, N, K)
     _check(st)
     return plan

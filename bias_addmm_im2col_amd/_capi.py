@@ -50,7 +50,7 @@ def lib():
     L.conv2d_gemm_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
     L.baim_conv2d_out_hw.restype = ctypes.c_int
-    L.baim_gemm_plan.argtypes = [_i64] * 3 + [ctypes.POINTER(ctypes.c_int)] * 6
+    L.baim_gemm_plan.argtypes = [_i64] * 3 + [ctypes.POINTER(ctypes.c_int)] * 7
     L.baim_gemm_plan.restype = ctypes.c_int
     L.baim_last_error.argtypes = []
     L.baim_last_error.restype = ctypes.c_char_p
@@ -76,9 +76,9 @@ def conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH
 
 def gemm_plan(M, N, K):
     """(status, dict) with the tile the library picks for an M x N x K GEMM."""
-    outs = [ctypes.c_int(0) for _ in range(6)]
+    outs = [ctypes.c_int(0) for _ in range(7)]
     st = lib().baim_gemm_plan(M, N, K, *[ctypes.byref(o) for o in outs])
-    keys = ("bm", "bn", "bk", "waves", "kgroups", "splits")
+    keys = ("bm", "bn", "bk", "waves", "kgroups", "splits", "stream_blocks")
     return st, {k: o.value for k, o in zip(keys, outs)}
 
 

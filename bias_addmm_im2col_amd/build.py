@@ -30,8 +30,23 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+def _scratch_kernels(remarks: str):
+    """Kernels whose resource-usage remark reports private (scratch) memory:
+    a spill or an address-taken argument, both costly in these kernels."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0].strip())
+            if n > 0:
+                bad.append((name, n))
+    return bad
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libbaim.so (always rebuilds)."""
+    """Compile every source into libbaim.so (always rebuilds).  Fails if a
+    kernel uses scratch memory."""
     objs = []
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
     procs = []
@@ -40,22 +55,31 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c"]
         if src.endswith(".cpp"):
             cmd += ["-x", "hip"]
+        else:
+            cmd += ["-Rpass-analysis=kernel-resource-usage"]
         cmd += [os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True), src))
         objs.append(obj)
     failed = []
+    scratch = []
     for p, src in procs:
         _, err = p.communicate()
-        # hipcc's host pass does not know the packed-fp32 feature: harmless
-        err = "\n".join(l for l in err.splitlines() if "packed-fp32-ops" not in l)
+        scratch += _scratch_kernels(err)
+        # hipcc's host pass does not know the packed-fp32 feature: harmless;
+        # resource-usage remarks are parsed above
+        err = "\n".join(l for l in err.splitlines()
+                        if "packed-fp32-ops" not in l and "remark:" not in l)
         if p.returncode != 0:
             failed.append((src, err))
         elif verbose and err.strip():
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n".join(f"--- {s}\n{e}" for s, e in failed))
+    if scratch:
+        raise RuntimeError("kernels use scratch memory:\n" +
+                           "\n".join(f"  {n}: {b} bytes/lane" for n, b in scratch))
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)

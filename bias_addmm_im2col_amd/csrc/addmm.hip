@@ -4,9 +4,14 @@
 // epilogue picks self[r*N + c] for a full self and the broadcast self[c]
 // otherwise, and writes beta*self + alpha*acc).
 //
-// With a K split (chosen for grids too small to fill the chip), a first
-// kernel writes beta*self (or 0) into out and every K slice then adds its
-// alpha*partial with a hardware fp32 atomic add.
+// Work split (see gemm_core.hpp): one tile per block; or K slices; or
+// stream pieces.  A tile cut into exactly two pieces is combined without a
+// workspace: out starts as a sentinel, each piece swaps its partial in, and
+// the piece that gets the other's partial back adds the two (an order-free
+// sum) and writes the fused epilogue, so the result is the same bits on
+// every run.  With more than two K slices (grids too small for anything
+// else) out starts as beta*self and the slices add alpha*partial with
+// hardware fp32 atomics.
 #include <stdlib.h>
 
 #include "gemm_core.hpp"
@@ -23,59 +28,117 @@ struct AddmmArgs {
   int M, N, K;
   int self_mode;  // 0: beta == 0 (self not read); 1: self [N]; 2: self [M,N]
   float beta, alpha;
-  int tiles_m, tiles_n, group_m, splits, kt_per_split;
+  Sched sched;
 };
 
-template <class T, int VA, int VB, bool SPLIT>
-__global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
-  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
-  const BlockWork w = block_work(p.tiles_m, p.tiles_n, p.group_m, SPLIT ? p.splits : 1,
-                                 p.kt_per_split, p.K, T::BM, T::BN, T::BK);
+template <class T, int VA, int VB>
+__device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int m0, int n0, int tb,
+                                   int te, int epi) {
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
-  const int wm0 = ws.wm0, wn0 = ws.wn0;
-
   RowTileLoader<T, VA> al;
-  al.init(p.A, w.m0, p.M, p.K);
+  al.init(p.A, m0, p.M, p.K);
   ColTileLoader<T, VB> bl;
-  bl.init(p.B, w.n0, p.N, p.K);
+  bl.init(p.B, n0, p.N, p.K);
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, w.t_begin, w.t_end, smem, ws, lane);
+  mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // Fused epilogue: beta*self + alpha*acc, self broadcast from [N] or full.
   const int c = lane & 31;
+  if (epi == EPI_EXCHANGE) {
+    // Two-piece tile: swap every partial in first (all swaps in flight at
+    // once), then finish the elements whose other piece had already landed.
+    uint32_t other[T::FM][T::FN][16];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = n0 + ws.wn0 + 32 * j + c, m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          other[i][j][r] = kPieceSentinel;
+          if (n < p.N && m < p.M)
+            other[i][j][r] = atomicExch(reinterpret_cast<unsigned int*>(&p.out[(size_t)m * p.N + n]),
+                                        __float_as_uint(acc.c[i][j][r]));
+        }
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int n = n0 + ws.wn0 + 32 * j + c;
+      if (n >= p.N) continue;
+      const float srow = p.self_mode == 1 ? p.self[n] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          if (m >= p.M || other[i][j][r] == kPieceSentinel) continue;
+          const size_t o = (size_t)m * p.N + n;
+          const float v = __uint_as_float(other[i][j][r]) + acc.c[i][j][r];
+          if (p.self_mode == 0) {
+            p.out[o] = p.alpha * v;
+          } else {
+            const float sv = p.self_mode == 1 ? srow : p.self[o];
+            p.out[o] = fmaf(p.alpha, v, p.beta * sv);
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
-    const int n = w.n0 + wn0 + 32 * j + c;
+    const int n = n0 + ws.wn0 + 32 * j + c;
     if (n >= p.N) continue;
-    const float srow = !SPLIT && p.self_mode == 1 ? p.self[n] : 0.0f;
+    const float srow = p.self_mode == 1 && epi == EPI_STORE ? p.self[n] : 0.0f;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = w.m0 + wm0 + 32 * i + acc_row(r, lane);
+        const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
         if (m >= p.M) continue;
         const size_t o = (size_t)m * p.N + n;
         const float v = acc.c[i][j][r];
-        if (SPLIT) {
+        if (epi == EPI_ATOMIC) {
           unsafeAtomicAdd(&p.out[o], p.alpha * v);
         } else if (p.self_mode == 0) {
           p.out[o] = p.alpha * v;
         } else {
-          const float s = p.self_mode == 1 ? srow : p.self[o];
-          p.out[o] = fmaf(p.alpha, v, p.beta * s);
+          const float sv = p.self_mode == 1 ? srow : p.self[o];
+          p.out[o] = fmaf(p.alpha, v, p.beta * sv);
         }
       }
   }
 }
 
-// out = beta*self (self_mode 1 or 2) or 0 (self_mode 0), before the K slices
-// add their partial products.
+template <class T, int VA, int VB, int MODE>
+__global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
+  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+  for_each_piece<MODE>(p.sched, T::BM, T::BN, [&](int m0, int n0, int tb, int te, int epi) __attribute__((always_inline)) {
+    addmm_piece<T, VA, VB>(p, smem, m0, n0, tb, te, epi);
+  });
+}
+
+// Output initialisation before a split tile's pieces land: the sentinel
+// (two-piece combine, 16-byte stores) or beta*self / 0 (atomic K slices).
 __global__ __launch_bounds__(256) void addmm_init_kernel(float* out, const float* self,
                                                          int self_mode, float beta,
-                                                         uint32_t total, FastDiv div_n) {
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
+                                                         int sentinel, uint32_t total,
+                                                         FastDiv div_n) {
+  const uint32_t stride = gridDim.x * 256u;
+  if (sentinel) {
+    const float s = __uint_as_float(kPieceSentinel);
+    const f32x4 s4 = {s, s, s, s};
+    const uint32_t head = (uint32_t)((16u - ((uintptr_t)out & 15u)) & 15u) / 4u;
+    const uint32_t h = head < total ? head : total;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < h; i += stride) out[i] = s;
+    const uint32_t nvec = (total - h) / 4u;
+    f32x4* o4 = reinterpret_cast<f32x4*>(out + h);
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < nvec; i += stride) o4[i] = s4;
+    for (uint32_t i = h + nvec * 4u + blockIdx.x * 256u + threadIdx.x; i < total; i += stride)
+      out[i] = s;
+    return;
+  }
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += stride) {
     float v = 0.0f;
     if (self_mode == 1) {
       const uint32_t m = fdiv(i, div_n);
@@ -108,45 +171,58 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
                   same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
               "tile table out of sync with the compiled tiles");
 
-template <class T, int VA, int VB, bool SPLIT>
+template <class T, int VA, int VB, int MODE>
 static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, SPLIT>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE>), dim3(nblocks), dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <class T, bool SPLIT>
+// Stream pieces are compiled for aligned operands only (the launcher falls
+// back to one tile per block otherwise).
+template <class T, int CFG, int MODE>
 static hipError_t launch_vec(const AddmmArgs& a, int nblocks, bool va, bool vb, hipStream_t s) {
-  if (va && vb) return launch_t<T, 4, 4, SPLIT>(a, nblocks, s);
-  if (va) return launch_t<T, 4, 1, SPLIT>(a, nblocks, s);
-  if (vb) return launch_t<T, 1, 4, SPLIT>(a, nblocks, s);
-  return launch_t<T, 1, 1, SPLIT>(a, nblocks, s);
+  if constexpr (MODE == MODE_STREAM) {
+    if constexpr (kTileStream[CFG]) return launch_t<T, 4, 4, MODE_STREAM>(a, nblocks, s);
+    return hipErrorInvalidValue;  // never planned
+  } else if constexpr (MODE == MODE_SLICES && !kTileSlices[CFG]) {
+    return hipErrorInvalidValue;  // never planned
+  } else {
+    if (va && vb) return launch_t<T, 4, 4, MODE>(a, nblocks, s);
+    if (va) return launch_t<T, 4, 1, MODE>(a, nblocks, s);
+    if (vb) return launch_t<T, 1, 4, MODE>(a, nblocks, s);
+    return launch_t<T, 1, 1, MODE>(a, nblocks, s);
+  }
 }
 
-template <bool SPLIT>
+template <int MODE>
 static hipError_t launch_cfg(int cfg, const AddmmArgs& a, int nblocks, bool va, bool vb,
                              hipStream_t s) {
   switch (cfg) {
     case TILE_128x64:
-      return launch_vec<T128x64, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64, TILE_128x64, MODE>(a, nblocks, va, vb, s);
     case TILE_64x128:
-      return launch_vec<T64x128, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T64x128, TILE_64x128, MODE>(a, nblocks, va, vb, s);
     case TILE_64x64:
-      return launch_vec<T64x64, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64, TILE_64x64, MODE>(a, nblocks, va, vb, s);
     case TILE_128x128_K2:
-      return launch_vec<T128x128K2, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128K2, TILE_128x128_K2, MODE>(a, nblocks, va, vb, s);
     case TILE_128x64_K2:
-      return launch_vec<T128x64K2, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64K2, TILE_128x64_K2, MODE>(a, nblocks, va, vb, s);
     case TILE_64x64_K2:
-      return launch_vec<T64x64K2, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K2, TILE_64x64_K2, MODE>(a, nblocks, va, vb, s);
     case TILE_64x64_K4:
-      return launch_vec<T64x64K4, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K4, TILE_64x64_K4, MODE>(a, nblocks, va, vb, s);
     default:
-      return launch_vec<T128x128, SPLIT>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128, TILE_128x128, MODE>(a, nblocks, va, vb, s);
   }
 }
 
 hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
-  const GemmPlan plan = plan_gemm(p.M, p.N, p.K, getenv("BAIM_TILE"));
+  // 16-byte vector loads need K (resp. N) divisible by 4 and aligned bases.
+  const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
+  const bool vb = p.N % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
+  GemmPlan plan = plan_gemm(p.M, p.N, p.K, getenv("BAIM_TILE"));
+  if (plan.mode == MODE_STREAM && !(va && vb)) plan = plan_tiles_only(plan, p.M, p.N, p.K);
   AddmmArgs a;
   a.out = p.out;
   a.self = p.self;
@@ -158,25 +234,25 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
   a.self_mode = p.self_mode;
   a.beta = p.beta;
   a.alpha = p.alpha;
-  a.tiles_m = plan.tiles_m;
-  a.tiles_n = plan.tiles_n;
-  a.group_m = 8;
-  a.splits = plan.splits;
-  a.kt_per_split = plan.kt_per_split;
+  a.sched = Sched{plan.tiles_m, plan.tiles_n, 8, plan.nkt, plan.splits, plan.kt_per_split};
   const int nblocks = (int)plan_blocks(plan);
-  // 16-byte vector loads need K (resp. N) divisible by 4 and aligned bases.
-  const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
-  const bool vb = p.N % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
-  if (plan.splits > 1) {
+  if (plan_needs_init(plan)) {
     const uint32_t total = (uint32_t)p.M * (uint32_t)p.N;
     const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
     hipLaunchKernelGGL(addmm_init_kernel, dim3(gb), dim3(256), 0, stream, p.out, p.self,
-                       p.self_mode, p.beta, total, make_fastdiv((uint32_t)p.N));
+                       p.self_mode, p.beta, plan_uses_exchange(plan) ? 1 : 0, total,
+                       make_fastdiv((uint32_t)p.N));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_cfg<true>(plan.cfg, a, nblocks, va, vb, stream);
   }
-  return launch_cfg<false>(plan.cfg, a, nblocks, va, vb, stream);
+  switch (plan.mode) {
+    case MODE_SLICES:
+      return launch_cfg<MODE_SLICES>(plan.cfg, a, nblocks, va, vb, stream);
+    case MODE_STREAM:
+      return launch_cfg<MODE_STREAM>(plan.cfg, a, nblocks, va, vb, stream);
+    default:
+      return launch_cfg<MODE_TILE>(plan.cfg, a, nblocks, va, vb, stream);
+  }
 }
 
 }  // namespace baim

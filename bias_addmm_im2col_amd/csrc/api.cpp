@@ -74,9 +74,9 @@ int baim_version(void) { return 100; }
 const char* baim_last_error(void) { return g_err.c_str(); }
 
 baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn, int* bk,
-                           int* waves, int* kgroups, int* splits) {
+                           int* waves, int* kgroups, int* splits, int* stream_blocks) {
   g_err.clear();
-  if (!bm || !bn || !bk || !waves || !kgroups || !splits)
+  if (!bm || !bn || !bk || !waves || !kgroups || !splits || !stream_blocks)
     return fail(BAIM_ERR_NULL, "baim_gemm_plan: output pointers must not be NULL");
   if (M < 0 || N < 0 || K < 0) return fail(BAIM_ERR_SHAPE, "baim_gemm_plan: sizes must be >= 0");
   if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems)
@@ -87,7 +87,8 @@ baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn, in
   *bk = baim::kTileBK[p.cfg];
   *waves = baim::kTileWaves[p.cfg];
   *kgroups = baim::kTileKGroups[p.cfg];
-  *splits = p.splits;
+  *splits = p.mode == baim::MODE_SLICES ? p.splits : 1;
+  *stream_blocks = p.mode == baim::MODE_STREAM ? p.workers : 0;
   return BAIM_OK;
 }
 

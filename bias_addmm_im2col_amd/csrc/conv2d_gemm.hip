@@ -28,7 +28,7 @@ struct ConvArgs {
   int M, N, K;
   int x_elems;  // B*IC*H*W
   FastDiv div_khw, div_kw, div_p, div_ow;
-  int tiles_m, tiles_n, group_m, splits, kt_per_split;
+  Sched sched;
 };
 
 // B operand: the implicit im2col tile B[kk, n] for kk in [k0, k0+BK),
@@ -116,60 +116,110 @@ struct ImColTileLoader {
   }
 };
 
-template <class T, int VA, bool SPLIT>
-__global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
-  __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
-  const BlockWork w = block_work(p.tiles_m, p.tiles_n, p.group_m, SPLIT ? p.splits : 1,
-                                 p.kt_per_split, p.K, T::BM, T::BN, T::BK);
+template <class T, int VA>
+__device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m0, int n0, int tb, int te,
+                                  int epi) {
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
-  const int wm0 = ws.wm0, wn0 = ws.wn0;
-
   RowTileLoader<T, VA> al;
-  al.init(p.w, w.m0, p.M, p.K);
+  al.init(p.w, m0, p.M, p.K);
   ImColTileLoader<T> bl;
-  bl.init(p, w.n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
+  bl.init(p, n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, w.t_begin, w.t_end, smem, ws, lane);
+  mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // Epilogue: + bias[oc], NCHW store: column n = (b, pix) goes to
-  // out[b, oc, pix] = out[(b*OC + oc)*P + pix], P = OH*OW.  A K slice adds
-  // its partial sum instead (the bias is already in out).
+  // out[b, oc, pix] = out[(b*OC + oc)*P + pix], P = OH*OW.  A split tile's
+  // pieces are combined first (see the two-piece exchange and the atomic
+  // K slices in gemm_core.hpp).
   const int c = lane & 31;
   const uint32_t P = p.div_p.d;
+  size_t obase[T::FN];
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
-    const int n = w.n0 + wn0 + 32 * j + c;
+    const int n = n0 + ws.wn0 + 32 * j + c;
+    const uint32_t b = fdiv((uint32_t)(n < p.N ? n : 0), p.div_p);
+    obase[j] = (size_t)b * p.OC * P + ((uint32_t)n - b * P);
+  }
+  if (epi == EPI_EXCHANGE) {
+    // Two-piece tile: swap every partial in first (all swaps in flight at
+    // once), then finish the elements whose other piece had already landed.
+    uint32_t other[T::FM][T::FN][16];
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = n0 + ws.wn0 + 32 * j + c, oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          other[i][j][r] = kPieceSentinel;
+          if (n < p.N && oc < p.M)
+            other[i][j][r] = atomicExch(
+                reinterpret_cast<unsigned int*>(&p.out[obase[j] + (size_t)oc * P]),
+                __float_as_uint(acc.c[i][j][r]));
+        }
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int n = n0 + ws.wn0 + 32 * j + c, oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          if (n >= p.N || oc >= p.M || other[i][j][r] == kPieceSentinel) continue;
+          const float v = __uint_as_float(other[i][j][r]) + acc.c[i][j][r];
+          p.out[obase[j] + (size_t)oc * P] = v + (p.bias ? p.bias[oc] : 0.0f);
+        }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const int n = n0 + ws.wn0 + 32 * j + c;
     if (n >= p.N) continue;
-    const uint32_t b = fdiv((uint32_t)n, p.div_p);
-    const size_t obase = (size_t)b * p.OC * P + ((uint32_t)n - b * P);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int oc = w.m0 + wm0 + 32 * i + acc_row(r, lane);
+        const int oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
         if (oc >= p.M) continue;
-        float* o = &p.out[obase + (size_t)oc * P];
-        if (SPLIT) {
+        float* o = &p.out[obase[j] + (size_t)oc * P];
+        if (epi == EPI_ATOMIC)
           unsafeAtomicAdd(o, acc.c[i][j][r]);
-        } else {
+        else
           *o = acc.c[i][j][r] + (p.bias ? p.bias[oc] : 0.0f);
-        }
       }
   }
 }
 
-// out[b, oc, pix] = bias[oc] (or 0), before the K slices add their partial
-// products.
+template <class T, int VA, int MODE>
+__global__ __launch_bounds__(T::NT) void conv2d_gemm_kernel(ConvArgs p) {
+  __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
+  for_each_piece<MODE>(p.sched, T::BM, T::BN, [&](int m0, int n0, int tb, int te, int epi) __attribute__((always_inline)) {
+    conv_piece<T, VA>(p, smem, m0, n0, tb, te, epi);
+  });
+}
+
+// Output initialisation before a split tile's pieces land: the sentinel
+// (two-piece combine, 16-byte stores) or bias[oc] / 0 (atomic K slices).
 __global__ __launch_bounds__(256) void conv_init_kernel(float* out, const float* bias,
-                                                        uint32_t total, FastDiv div_p,
-                                                        uint32_t OC) {
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += gridDim.x * 256u) {
-    float v = 0.0f;
-    if (bias) v = bias[fdiv(i, div_p) % OC];
-    out[i] = v;
+                                                        int sentinel, uint32_t total,
+                                                        FastDiv div_p, uint32_t OC) {
+  const uint32_t stride = gridDim.x * 256u;
+  if (sentinel) {
+    const float s = __uint_as_float(kPieceSentinel);
+    const f32x4 s4 = {s, s, s, s};
+    const uint32_t head = (uint32_t)((16u - ((uintptr_t)out & 15u)) & 15u) / 4u;
+    const uint32_t h = head < total ? head : total;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < h; i += stride) out[i] = s;
+    const uint32_t nvec = (total - h) / 4u;
+    f32x4* o4 = reinterpret_cast<f32x4*>(out + h);
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < nvec; i += stride) o4[i] = s4;
+    for (uint32_t i = h + nvec * 4u + blockIdx.x * 256u + threadIdx.x; i < total; i += stride)
+      out[i] = s;
+    return;
   }
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += stride)
+    out[i] = bias ? bias[fdiv(i, div_p) % OC] : 0.0f;
 }
 
 typedef Tile<128, 128, 32, 2, 4> T128x128;
@@ -193,36 +243,45 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
                   same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
               "tile table out of sync with the compiled tiles");
 
-template <class T, int VA, bool SPLIT>
+template <class T, int VA, int MODE>
 static hipError_t launch_t(const ConvArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA, SPLIT>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA, MODE>), dim3(nblocks), dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
-template <class T, bool SPLIT>
+// Stream pieces are compiled for 16-byte weight loads only (the launcher
+// falls back to one tile per block otherwise).
+template <class T, int CFG, int MODE>
 static hipError_t launch_vec(const ConvArgs& a, int nblocks, bool va, hipStream_t s) {
-  return va ? launch_t<T, 4, SPLIT>(a, nblocks, s) : launch_t<T, 1, SPLIT>(a, nblocks, s);
+  if constexpr (MODE == MODE_STREAM) {
+    if constexpr (kTileStream[CFG]) return launch_t<T, 4, MODE_STREAM>(a, nblocks, s);
+    return hipErrorInvalidValue;  // never planned
+  } else if constexpr (MODE == MODE_SLICES && !kTileSlices[CFG]) {
+    return hipErrorInvalidValue;  // never planned
+  } else {
+    return va ? launch_t<T, 4, MODE>(a, nblocks, s) : launch_t<T, 1, MODE>(a, nblocks, s);
+  }
 }
 
-template <bool SPLIT>
+template <int MODE>
 static hipError_t launch_cfg(int cfg, const ConvArgs& a, int nblocks, bool va, hipStream_t s) {
   switch (cfg) {
     case TILE_128x64:
-      return launch_vec<T128x64, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T128x64, TILE_128x64, MODE>(a, nblocks, va, s);
     case TILE_64x128:
-      return launch_vec<T64x128, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T64x128, TILE_64x128, MODE>(a, nblocks, va, s);
     case TILE_64x64:
-      return launch_vec<T64x64, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T64x64, TILE_64x64, MODE>(a, nblocks, va, s);
     case TILE_128x128_K2:
-      return launch_vec<T128x128K2, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T128x128K2, TILE_128x128_K2, MODE>(a, nblocks, va, s);
     case TILE_128x64_K2:
-      return launch_vec<T128x64K2, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T128x64K2, TILE_128x64_K2, MODE>(a, nblocks, va, s);
     case TILE_64x64_K2:
-      return launch_vec<T64x64K2, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T64x64K2, TILE_64x64_K2, MODE>(a, nblocks, va, s);
     case TILE_64x64_K4:
-      return launch_vec<T64x64K4, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T64x64K4, TILE_64x64_K4, MODE>(a, nblocks, va, s);
     default:
-      return launch_vec<T128x128, SPLIT>(a, nblocks, va, s);
+      return launch_vec<T128x128, TILE_128x128, MODE>(a, nblocks, va, s);
   }
 }
 
@@ -254,24 +313,27 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.div_kw = make_fastdiv((uint32_t)q.KW);
   a.div_p = make_fastdiv((uint32_t)(q.OH * q.OW));
   a.div_ow = make_fastdiv((uint32_t)q.OW);
-  const GemmPlan plan = plan_gemm(a.M, a.N, a.K, getenv("BAIM_TILE"));
-  a.tiles_m = plan.tiles_m;
-  a.tiles_n = plan.tiles_n;
-  a.group_m = 8;
-  a.splits = plan.splits;
-  a.kt_per_split = plan.kt_per_split;
-  const int nblocks = (int)plan_blocks(plan);
   const bool va = a.K % 4 == 0 && ((uintptr_t)q.w & 15) == 0;
-  if (plan.splits > 1) {
+  GemmPlan plan = plan_gemm(a.M, a.N, a.K, getenv("BAIM_TILE"));
+  if (plan.mode == MODE_STREAM && !va) plan = plan_tiles_only(plan, a.M, a.N, a.K);
+  a.sched = Sched{plan.tiles_m, plan.tiles_n, 8, plan.nkt, plan.splits, plan.kt_per_split};
+  const int nblocks = (int)plan_blocks(plan);
+  if (plan_needs_init(plan)) {
     const uint32_t total = (uint32_t)a.M * (uint32_t)a.N;
     const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
-    hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias, total,
-                       a.div_p, (uint32_t)q.OC);
+    hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias,
+                       plan_uses_exchange(plan) ? 1 : 0, total, a.div_p, (uint32_t)q.OC);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_cfg<true>(plan.cfg, a, nblocks, va, stream);
   }
-  return launch_cfg<false>(plan.cfg, a, nblocks, va, stream);
+  switch (plan.mode) {
+    case MODE_SLICES:
+      return launch_cfg<MODE_SLICES>(plan.cfg, a, nblocks, va, stream);
+    case MODE_STREAM:
+      return launch_cfg<MODE_STREAM>(plan.cfg, a, nblocks, va, stream);
+    default:
+      return launch_cfg<MODE_TILE>(plan.cfg, a, nblocks, va, stream);
+  }
 }
 
 }  // namespace baim

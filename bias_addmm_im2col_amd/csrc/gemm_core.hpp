@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include "index_math.hpp"
+#include "tile_select.hpp"
 
 namespace baim {
 
@@ -206,7 +207,7 @@ struct Accum {
 // One k-tile: for the wave's k range [kofs, kofs + BKW), BKW/2 MFMA steps
 // for every 32x32 block of the wave's sub-tile.
 template <class T>
-__device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
+__device__ __forceinline__ void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
                                 const WaveSlot& ws, int lane) {
   const int c = lane & 31, h = lane >> 5;
 #pragma unroll
@@ -235,7 +236,7 @@ __device__ inline void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
 // does not depend on timing).  Returns true for the waves that hold the
 // final tile and run the epilogue.  Called by every thread after mainloop.
 template <class T>
-__device__ inline bool reduce_k_groups(Accum<T>& acc, float* smem, const WaveSlot& ws,
+__device__ __forceinline__ bool reduce_k_groups(Accum<T>& acc, float* smem, const WaveSlot& ws,
                                        int lane) {
   if (T::WK == 1) return true;
   constexpr int REGS = T::FM * T::FN * 16;
@@ -273,7 +274,7 @@ __device__ inline bool reduce_k_groups(Accum<T>& acc, float* smem, const WaveSlo
 // tiles ahead, so that slot is free (its last reader, load(t-2), ran before
 // the previous barrier) and visible to load(t) after the next barrier.
 template <class T, class AL, class BL>
-__device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
+__device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
                                 float* smem, const WaveSlot& ws, int lane) {
   acc.zero();
   if (t_begin >= t_end) return;
@@ -306,27 +307,65 @@ __device__ inline void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int 
   }
 }
 
-// Which output tile and which K slice a block computes.  Blocks are laid
-// out slice-major (all tiles of slice 0, then slice 1, ...) over the
-// XCD-remapped ids, so neighbouring tiles of the same slice share an XCD.
-struct BlockWork {
-  int m0, n0, t_begin, t_end;
+// ------------------------------------------------------------ scheduling
+//
+// How blocks map to work:
+//  MODE_TILE    one output tile per block, all of K.
+//  MODE_SLICES  tiles x splits blocks; block (tile, z) computes K slice z.
+//  MODE_STREAM  P blocks share the (tile, k-tile) units evenly: block w
+//               takes units [w*U/P, (w+1)*U/P) in tile-major order, so a
+//               tile is either whole in one block or cut into pieces.
+// Block ids are XCD-remapped and tiles follow the grouped raster, so
+// neighbouring tiles share an XCD's L2.
+// How a (piece of a) tile writes its result.
+enum {
+  EPI_STORE = 0,     // whole tile: fused epilogue, plain stores
+  EPI_ATOMIC = 1,    // one of several K slices: atomic add into an initialised out
+  EPI_EXCHANGE = 2,  // one of exactly two pieces: swap in, the second combines
 };
 
-__device__ inline BlockWork block_work(int tiles_m, int tiles_n, int group_m, int splits,
-                                       int kt_per_split, int K, int BM, int BN, int BK) {
+// Bit pattern written into out before two-piece tiles are combined: a
+// signalling NaN, which no arithmetic produces (results are quiet NaNs), so
+// it cannot be mistaken for a partial sum.
+constexpr uint32_t kPieceSentinel = 0x7FA5A5A5u;
+
+struct Sched {
+  int tiles_m, tiles_n, group_m;
+  int nkt;                     // k-tiles per tile
+  int splits, kt_per_split;    // MODE_SLICES
+};
+
+template <int MODE, class F>
+__device__ __forceinline__ void for_each_piece(const Sched& s, int BM, int BN, F&& f) {
   const int lid = xcd_linear(blockIdx.x, gridDim.x);
-  const int ntiles = tiles_m * tiles_n;
-  const int z = lid / ntiles;
+  const int ntiles = s.tiles_m * s.tiles_n;
   int tm, tn;
-  grouped_tile(lid - z * ntiles, tiles_m, tiles_n, group_m, tm, tn);
-  const int nkt = (K + BK - 1) / BK;
-  BlockWork w;
-  w.m0 = tm * BM;
-  w.n0 = tn * BN;
-  w.t_begin = splits > 1 ? z * kt_per_split : 0;
-  w.t_end = splits > 1 ? min(nkt, w.t_begin + kt_per_split) : nkt;
-  return w;
+  if (MODE == MODE_STREAM) {
+    const int64_t total = (int64_t)ntiles * s.nkt;
+    const int64_t P = gridDim.x;
+    const int64_t base = total / P, rem = total % P;
+    int64_t u = lid * base + (lid < rem ? lid : rem);
+    const int64_t ue = u + base + (lid < rem ? 1 : 0);
+    while (u < ue) {
+      const int tile = (int)(u / s.nkt);
+      const int kb = (int)(u - (int64_t)tile * s.nkt);
+      const int ke = (int)(s.nkt < kb + (ue - u) ? s.nkt : kb + (ue - u));
+      grouped_tile(tile, s.tiles_m, s.tiles_n, s.group_m, tm, tn);
+      f(tm * BM, tn * BN, kb, ke, (kb == 0 && ke == s.nkt) ? EPI_STORE : EPI_EXCHANGE);
+      u += ke - kb;
+      __syncthreads();  // LDS is reused by the next piece
+    }
+  } else {
+    const int z = lid / ntiles;
+    grouped_tile(lid - z * ntiles, s.tiles_m, s.tiles_n, s.group_m, tm, tn);
+    if (MODE == MODE_SLICES) {
+      const int tb = z * s.kt_per_split;
+      const int te = s.nkt < tb + s.kt_per_split ? s.nkt : tb + s.kt_per_split;
+      f(tm * BM, tn * BN, tb, te, s.splits == 2 ? EPI_EXCHANGE : EPI_ATOMIC);
+    } else {
+      f(tm * BM, tn * BN, 0, s.nkt, EPI_STORE);
+    }
+  }
 }
 
 // Row of accumulator register j of a 32x32 block, relative to the block.

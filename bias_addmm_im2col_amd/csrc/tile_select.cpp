@@ -6,7 +6,8 @@
 //  * >= 512 tiles of 128x128: the 128x128 tile (most reuse per byte).
 //  * >= 192 such tiles and deep K: 128x128 with each k-tile split over two
 //    wave groups (16 waves per block: one block per CU still keeps four
-//    waves per SIMD).
+//    waves per SIMD); below 256 tiles, 128x64 pieces streamed over exactly
+//    one block per CU instead, so no CU idles.
 //  * >= 256 such tiles and moderate K: half-size tiles (more blocks).
 //  * many 64x64 tiles, or very shallow K: 64x64.
 //  * few tiles and deep K: 64x64 with 2 or 4 wave groups per tile.
@@ -28,12 +29,33 @@ GemmPlan make(int cfg, int M, int N, int K, int splits) {
   p.cfg = cfg;
   p.tiles_m = cdiv(M, kTileBM[cfg]);
   p.tiles_n = cdiv(N, kTileBN[cfg]);
-  const int nkt = cdiv(K, kTileBK[cfg]);
-  if (splits < 1) splits = 1;
-  if (splits > nkt) splits = nkt > 0 ? nkt : 1;
-  p.kt_per_split = nkt > 0 ? cdiv(nkt, splits) : 0;
-  // drop slices that would be empty after rounding up the slice length
-  p.splits = p.kt_per_split > 0 ? cdiv(nkt, p.kt_per_split) : 1;
+  p.nkt = cdiv(K, kTileBK[cfg]);
+  p.mode = MODE_TILE;
+  p.splits = 1;
+  p.kt_per_split = p.nkt;
+  p.workers = 0;
+  if (splits > p.nkt) splits = p.nkt;
+  if (splits >= 2 && kTileSlices[cfg]) {
+    p.kt_per_split = cdiv(p.nkt, splits);
+    // drop slices that would be empty after rounding up the slice length
+    p.splits = cdiv(p.nkt, p.kt_per_split);
+    if (p.splits >= 2) {
+      p.mode = MODE_SLICES;
+    } else {
+      p.splits = 1;
+      p.kt_per_split = p.nkt;
+    }
+  }
+  return p;
+}
+
+GemmPlan make_stream(int cfg, int M, int N, int K, int64_t workers) {
+  GemmPlan p = make(cfg, M, N, K, 1);
+  // fewer workers than tiles keeps every tile in at most two pieces
+  if (kTileStream[cfg] && p.nkt >= 2 && workers >= 1 && workers < plan_tiles(p)) {
+    p.mode = MODE_STREAM;
+    p.workers = (int)workers;
+  }
   return p;
 }
 
@@ -41,33 +63,49 @@ int64_t tiles_of(int cfg, int M, int N) {
   return (int64_t)cdiv(M, kTileBM[cfg]) * cdiv(N, kTileBN[cfg]);
 }
 
-bool parse_override(const char* s, int* cfg, int* splits) {
+// "cfg", "cfg,S" or "cfg,sP"
+bool parse_override(const char* s, int* cfg, int* splits, int* workers) {
   if (!s || !*s) return false;
   char* end = nullptr;
   const long c = strtol(s, &end, 10);
   if (end == s || c < 0 || c >= TILE_NCFG) return false;
-  long k = 1;
+  long k = 1, w = 0;
   if (*end == ',') {
     const char* t = end + 1;
-    k = strtol(t, &end, 10);
-    if (end == t || k < 1 || k > 64) return false;
+    if (*t == 's') {
+      ++t;
+      w = strtol(t, &end, 10);
+      if (end == t || w < 1 || w > (1 << 20)) return false;
+    } else {
+      k = strtol(t, &end, 10);
+      if (end == t || k < 1 || k > 64) return false;
+    }
   }
   if (*end != '\0') return false;
   *cfg = (int)c;
   *splits = (int)k;
+  *workers = (int)w;
   return true;
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
-  int cfg = 0, splits = 1;
-  if (parse_override(override_spec, &cfg, &splits)) return make(cfg, M, N, K, splits);
+  int cfg = 0, splits = 1, workers = 0;
+  if (parse_override(override_spec, &cfg, &splits, &workers))
+    return workers > 0 ? make_stream(cfg, M, N, K, workers) : make(cfg, M, N, K, splits);
 
   const int nkt = cdiv(K, 32);  // k-tiles of depth 32
   const int64_t t128 = tiles_of(TILE_128x128, M, N);
   if (t128 >= 2 * kNumCUs) return make(TILE_128x128, M, N, K, 1);
-  if (t128 >= (3 * kNumCUs) / 4 && nkt >= 48) return make(TILE_128x128_K2, M, N, K, 1);
+  if (t128 >= (3 * kNumCUs) / 4 && nkt >= 48) {
+    // 192..255 tiles leave CUs idle; stream 128x64 pieces over exactly one
+    // block per CU instead (at most two pieces per tile, combined
+    // deterministically).  On the 3x3 conv: 174 -> 167 us.
+    if (t128 < kNumCUs && tiles_of(TILE_128x64_K2, M, N) >= kNumCUs)
+      return make_stream(TILE_128x64_K2, M, N, K, kNumCUs);
+    return make(TILE_128x128_K2, M, N, K, 1);
+  }
   if (t128 >= kNumCUs && nkt > 8) {
     // Half-size tiles: the orientation that wastes less of a ragged edge;
     // on a tie the 64-row tile.
@@ -85,6 +123,10 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
   int s = (int)((kNumCUs + t64 - 1) / t64);
   if (s > nkt128 / 8) s = nkt128 / 8;
   return make(TILE_64x64_K4, M, N, K, s < 1 ? 1 : s);
+}
+
+GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K) {
+  return make(p.cfg, M, N, K, 1);
 }
 
 }  // namespace baim

@@ -26,23 +26,51 @@ constexpr int kTileBN[TILE_NCFG] = {128, 64, 128, 64, 128, 64, 64, 64};
 constexpr int kTileBK[TILE_NCFG] = {32, 32, 32, 32, 64, 64, 64, 128};
 constexpr int kTileWaves[TILE_NCFG] = {8, 8, 8, 4, 16, 16, 8, 16};
 constexpr int kTileKGroups[TILE_NCFG] = {1, 1, 1, 1, 2, 2, 2, 4};
+// Configurations compiled with the K-slice and stream schedules (the
+// others would exceed their register budget with the extra state).
+constexpr bool kTileSlices[TILE_NCFG] = {true, true, true, true, false, true, true, true};
+constexpr bool kTileStream[TILE_NCFG] = {true, true, true, true, false, true, true, false};
 constexpr int kNumCUs = 256;  // MI355X
 
+// How blocks map to work (the kernels' scheduling modes).
+enum PlanMode {
+  MODE_TILE = 0,    // one output tile per block
+  MODE_SLICES = 1,  // tiles x splits blocks, one K slice each
+  MODE_STREAM = 2,  // `workers` blocks share the (tile, k-tile) units evenly
+};
+
 struct GemmPlan {
-  int cfg;           // TileCfg
+  int cfg;  // TileCfg
   int tiles_m, tiles_n;
-  int splits;        // K slices (1: no split); every slice is non-empty
-  int kt_per_split;  // k-tiles per slice
+  int nkt;           // k-tiles of the tile's BK per tile
+  int mode;          // PlanMode
+  int splits;        // MODE_SLICES: K slices (>= 2, none empty); else 1
+  int kt_per_split;  // MODE_SLICES: k-tiles per slice
+  int workers;       // MODE_STREAM: blocks (< tiles, so a tile has at most 2 pieces)
 };
 
 // Plan for problem (M, N, K) with every dimension >= 0.  `override_spec`
-// (may be NULL) is "cfg" or "cfg,splits" and forces the choice; an
-// unparsable or out-of-range spec is ignored.
+// (may be NULL) forces the choice: "cfg" (one tile per block), "cfg,S" (S
+// K slices) or "cfg,sP" (stream over P blocks); an unparsable or
+// out-of-range spec is ignored.
 GemmPlan plan_gemm(int M, int N, int K, const char* override_spec);
+
+// The same tile configuration with one tile per block.
+GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K);
+
+inline int64_t plan_tiles(const GemmPlan& p) { return (int64_t)p.tiles_m * p.tiles_n; }
 
 // The block count of a plan.
 inline int64_t plan_blocks(const GemmPlan& p) {
-  return (int64_t)p.tiles_m * p.tiles_n * p.splits;
+  if (p.mode == MODE_STREAM) return p.workers;
+  return plan_tiles(p) * (p.mode == MODE_SLICES ? p.splits : 1);
+}
+
+// Whether out must be initialised before the GEMM kernel, and whether the
+// split tiles are combined by the two-piece exchange (else atomic adds).
+inline bool plan_needs_init(const GemmPlan& p) { return p.mode != MODE_TILE; }
+inline bool plan_uses_exchange(const GemmPlan& p) {
+  return p.mode == MODE_STREAM || (p.mode == MODE_SLICES && p.splits == 2);
 }
 
 }  // namespace baim

@@ -115,19 +115,24 @@ baim_status baim_conv2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW,
                                int64_t* OW);
 
 /*
- * baim_gemm_plan: the block tile the library uses for a GEMM of size
- * M x N x K (the same choice serves both ops; for the conv M = OC,
- * N = B*OH*OW, K = IC*KH*KW).  Writes the block tile BM x BN x BK, the
- * waves per block, the number of wave groups that split each k-tile
- * (partial tiles summed in a fixed order) and the number of K slices
- * spread over separate blocks (> 1 only for grids too small to fill the
- * chip: the slices are then added into the output with atomics, so the
- * last bits may differ from run to run).  The environment variable
- * BAIM_TILE="cfg[,splits]" (cfg 0..7) overrides the choice for tuning,
+ * baim_gemm_plan: how the library computes a GEMM of size M x N x K (the
+ * same choice serves both ops; for the conv M = OC, N = B*OH*OW,
+ * K = IC*KH*KW).  Writes the block tile BM x BN x BK, the waves per block,
+ * the number of wave groups that split each k-tile (their partial tiles
+ * are summed in a fixed order), and how tiles map to blocks:
+ *   splits > 1         K is cut into `splits` slices on separate blocks;
+ *   stream_blocks > 0  `stream_blocks` blocks share the work evenly, so a
+ *                      tile may be cut into two pieces.
+ * A tile cut into exactly two pieces is combined with a fixed, order-free
+ * sum (bit-reproducible).  Only with splits > 2 (grids too small to fill
+ * the chip otherwise) are the slices added with atomics, and the last bits
+ * may then differ from run to run.  The environment variable BAIM_TILE
+ * ("cfg", "cfg,S" or "cfg,sP", cfg 0..7) overrides the choice for tuning,
  * here and in the two ops.  Host-only; touches no GPU.
  */
 baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn,
-                           int* bk, int* waves, int* kgroups, int* splits);
+                           int* bk, int* waves, int* kgroups, int* splits,
+                           int* stream_blocks);
 
 /* Text describing the last error returned on the calling thread ("" if the
  * last call succeeded).  The pointer stays valid until the next call on the

@@ -262,12 +262,13 @@ def test_repeated_launches_are_deterministic():
 
 
 # ------------------------------------------- every tile config and K split
-# BAIM_TILE="cfg[,splits]" forces the host's choice: 0 = 128x128, 1 = 128x64,
-# 2 = 64x128, 3 = 64x64 (BK 32); 4 = 128x128, 5 = 128x64, 6 = 64x64 with
-# each k-tile split over 2 wave groups (BK 64); 7 = 64x64 over 4 groups
-# (BK 128); splits > 1 adds K slices into a pre-initialised out.
+# BAIM_TILE forces the host's choice: cfg 0 = 128x128, 1 = 128x64, 2 = 64x128,
+# 3 = 64x64 (BK 32); 4 = 128x128, 5 = 128x64, 6 = 64x64 with each k-tile
+# split over 2 wave groups (BK 64); 7 = 64x64 over 4 groups (BK 128).
+# "cfg,S": S K slices on separate blocks (S == 2: two-piece exchange,
+# S > 2: atomic adds); "cfg,sP": stream over P blocks (two-piece exchange).
 TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "0,3", "1,2", "2,4", "3,5", "0,64",
-              "4,2", "6,3", "7,2"]
+              "4,2", "6,3", "7,2", "3,s7", "0,s2", "4,s3", "6,s5", "2,s9", "1,s4", "7,s1"]
 
 
 @pytest.mark.parametrize("spec", TILE_SPECS)
@@ -306,3 +307,45 @@ def test_conv_forced_tile_configs(spec, monkeypatch):
     x, w, bias = gen((2, 40, 19, 17), 49, "I"), gen((72, 40, 3, 3), 50, "I"), gen((72,), 51, "I")
     out = run_conv(x, w, bias, 1, 1, 1)
     check_bitwise(out, oracle.conv2d(x, w, bias, 1, 1, 1), f"conv integer {spec}")
+
+
+@pytest.mark.parametrize("spec", ["3,s7", "0,2", "6,s5", "1,s4"])
+def test_two_piece_paths_are_bit_reproducible(spec, monkeypatch):
+    """Stream pieces and 2-slice splits combine with an order-free sum: the
+    same call gives the same bits every time."""
+    import bias_addmm_im2col_amd as baim
+    monkeypatch.setenv("BAIM_TILE", spec)
+    say(f"BAIM_TILE={spec} reproducibility")
+    a, b, s = gen((300, 700), 52), gen((700, 260), 53), gen((300, 260), 54)
+    outs = [baim.addmm(dev(s), dev(a), dev(b), beta=0.5, alpha=2.0).cpu() for _ in range(4)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    x, w, bias = gen((2, 40, 19, 17), 55), gen((72, 40, 3, 3), 56), gen((72,), 57)
+    outs = [baim.conv2d(dev(x), dev(w), dev(bias), 1, 1, 1).cpu() for _ in range(4)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+
+
+@pytest.mark.parametrize("spec", ["3,s7", "1,2", "7,3"])
+def test_split_paths_with_unaligned_out(spec, monkeypatch):
+    """The output-initialisation kernels handle an out that starts 4 bytes
+    past a 16-byte boundary and whose size is not a multiple of 4."""
+    import bias_addmm_im2col_amd as baim
+    monkeypatch.setenv("BAIM_TILE", spec)
+    say(f"BAIM_TILE={spec} unaligned out")
+    M, K, N = 131, 600, 197
+    a, b, s = gen((M, K), 58), gen((K, N), 59), gen((N,), 60)
+    buf = torch.full((M * N + 1,), 7.0, device="cuda")
+    out = buf[1:].view(M, N)
+    baim.addmm_f32(out, dev(s), dev(a), dev(b), 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert float(buf[0]) == 7.0
+    check_close(out.cpu().numpy(), oracle.addmm(a, b, s, False, 1.0, 1.0), K, 1.0, f"addmm {spec}")
+    x, w, bias = gen((2, 24, 21, 19), 61), gen((70, 24, 3, 3), 62), gen((70,), 63)
+    OH, OW = baim.conv2d_out_hw(21, 19, 3, 3, 1, 1, 1)
+    cbuf = torch.full((2 * 70 * OH * OW + 1,), 7.0, device="cuda")
+    cout = cbuf[1:].view(2, 70, OH, OW)
+    baim.conv2d_gemm_f32(cout, dev(x), dev(w), dev(bias), 1, 1, 1)
+    torch.cuda.synchronize()
+    assert float(cbuf[0]) == 7.0
+    check_close(cout.cpu().numpy(), oracle.conv2d(x, w, bias, 1, 1, 1), 24 * 9, 1.0, f"conv {spec}")

@@ -18,6 +18,10 @@ static int check(int M, int N, int K, const char* spec) {
   if ((int64_t)p.tiles_n * kTileBN[p.cfg] < N || (int64_t)(p.tiles_n - 1) * kTileBN[p.cfg] >= N)
     return printf("tiles_n %d wrong for N=%d\n", p.tiles_n, N), 1;
   if (p.splits < 1) return printf("splits %d\n", p.splits), 1;
+  if ((p.mode == MODE_SLICES) != (p.splits > 1)) return printf("mode/splits mismatch\n"), 1;
+  if (p.mode == MODE_STREAM && (p.workers < 1 || p.workers >= plan_tiles(p) || p.nkt < 2))
+    return printf("stream workers %d for %lld tiles\n", p.workers, (long long)plan_tiles(p)), 1;
+  if (p.nkt != nkt) return printf("nkt %d != %d\n", p.nkt, nkt), 1;
   if (p.splits > 1) {
     if ((int64_t)p.splits * p.kt_per_split < nkt || (int64_t)(p.splits - 1) * p.kt_per_split >= nkt)
       return printf("slices %d x %d do not tile %d k-tiles\n", p.splits, p.kt_per_split, nkt), 1;
@@ -31,7 +35,7 @@ int main() {
   const int sizes[] = {1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 577, 1000, 1024,
                        2048, 3072, 3364, 4096, 12544, 36864};
   const char* specs[] = {nullptr, "", "0", "1", "2", "3", "0,4", "3,2", "1,64", "9", "x", "0,",
-                         "0,0", "2,7x", "-1"};
+                         "0,0", "2,7x", "-1", "1,s256", "4,s1", "3,s100000", "0,s", "2,s0"};
   for (int M : sizes)
     for (int N : sizes)
       for (int K : {0, 1, 31, 32, 147, 768, 1024, 2304, 4096, 100000})
@@ -42,6 +46,10 @@ int main() {
   // a malformed override is ignored (same as no override)
   const GemmPlan g = plan_gemm(300, 500, 700, "2,7x"), h = plan_gemm(300, 500, 700, nullptr);
   if (g.cfg != h.cfg || g.splits != h.splits) bad += printf("bad override not ignored\n") > 0;
+  // a stream override keeps fewer workers than tiles, else falls back to tiles
+  const GemmPlan st = plan_gemm(256, 12544, 2304, "1,s256");
+  if (st.mode != MODE_STREAM || st.workers != 256) bad += printf("stream override\n") > 0;
+  if (plan_gemm(64, 64, 2304, "1,s256").mode != MODE_TILE) bad += printf("stream fallback\n") > 0;
   // K == 0 never splits
   if (plan_gemm(8, 8, 0, "0,4").splits != 1) bad += printf("K=0 split\n") > 0;
   if (bad) return 1;
