@@ -150,14 +150,15 @@ __global__ __launch_bounds__(256) void addmm_init_kernel(float* out, const float
   }
 }
 
-typedef Tile<128, 128, 32, 2, 4> T128x128;
-typedef Tile<128, 64, 32, 4, 2> T128x64;
-typedef Tile<64, 128, 32, 2, 4> T64x128;
-typedef Tile<64, 64, 32, 2, 2> T64x64;
-typedef Tile<128, 128, 64, 2, 4, 2> T128x128K2;
-typedef Tile<128, 64, 64, 4, 2, 2> T128x64K2;
-typedef Tile<64, 64, 64, 2, 2, 2> T64x64K2;
-typedef Tile<64, 64, 128, 2, 2, 4> T64x64K4;
+// Every tile prefetches two k-tiles ahead (see mainloop).
+typedef Tile<128, 128, 32, 2, 4, 1, 2> T128x128;
+typedef Tile<128, 64, 32, 4, 2, 1, 2> T128x64;
+typedef Tile<64, 128, 32, 2, 4, 1, 2> T64x128;
+typedef Tile<64, 64, 32, 2, 2, 1, 2> T64x64;
+typedef Tile<128, 128, 64, 2, 4, 2, 2> T128x128K2;
+typedef Tile<128, 64, 64, 4, 2, 2, 2> T128x64K2;
+typedef Tile<64, 64, 64, 2, 2, 2, 2> T64x64K2;
+typedef Tile<64, 64, 128, 2, 2, 4, 2> T64x64K4;
 
 // The host planner's table must describe exactly these tiles.
 template <class T>

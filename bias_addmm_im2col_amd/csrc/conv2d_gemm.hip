@@ -40,7 +40,7 @@ struct ConvArgs {
 //  * Row side (per k-tile, in LDS): kk -> (ic, kh, kw) gives the offset
 //    ic*H*W + kh*dH*W + kw*dW and the tap shifts dh = kh*dH, dw = kw*dW.
 //    Rows past K get dh = -(H + 2*pH) - 1, so they read as out of range.
-//    BK threads decode one row each, two k-tiles ahead of use.
+//    BK threads decode one row each, ahead of use (see mainloop).
 //  * Element: valid iff 0 <= ih0+dh < H and 0 <= iw0+dw < W; invalid
 //    elements load from an out-of-range offset and read 0 (the padding).
 // A wave loads 64 consecutive columns of one row per instruction, so every
@@ -54,9 +54,9 @@ struct ImColTileLoader {
   static_assert(T::BN % 64 == 0, "a wave must cover columns of a single row");
   static_assert(T::NT >= T::BK, "one thread per table row");
   const ConvArgs* a;
-  int4* tbl;  // [2][BK] {offset, dh, dw, unused}
+  int4* tbl;  // [META_SLOTS][BK] {offset, dh, dw, unused}
   int row0, col, cbase, ih0, iw0;
-  float reg[NP];
+  float reg[2][NP];  // two register slots (prefetch depth up to 2)
 
   __device__ void init(const ConvArgs& args, int n0, int4* table) {
     a = &args;
@@ -92,12 +92,13 @@ struct ImColTileLoader {
         e.z = 0;
       }
       e.w = 0;
-      tbl[(t & 1) * T::BK + threadIdx.x] = e;
+      tbl[(t % T::META_SLOTS) * T::BK + threadIdx.x] = e;
     }
   }
+  template <int S>
   __device__ void load(int k0) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a->x, a->x_elems);
-    const int4* slot = tbl + ((k0 / T::BK) & 1) * T::BK;
+    const int4* slot = tbl + ((k0 / T::BK) % T::META_SLOTS) * T::BK;
     // All table reads first, then branch-free address selection, so the
     // NP global loads issue back to back.
     int4 e[NP];
@@ -107,12 +108,13 @@ struct ImColTileLoader {
     for (int i = 0; i < NP; ++i) {
       const unsigned ok = (unsigned)((unsigned)(ih0 + e[i].y) < (unsigned)a->H) &
                           (unsigned)((unsigned)(iw0 + e[i].z) < (unsigned)a->W);
-      reg[i] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + e[i].x) * 4u : kOOB);
+      reg[S][i] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + e[i].x) * 4u : kOOB);
     }
   }
+  template <int S>
   __device__ void store(float* Bs) const {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) Bs[(row0 + RPP * i) * T::BS + col] = reg[i];
+    for (int i = 0; i < NP; ++i) Bs[(row0 + RPP * i) * T::BS + col] = reg[S][i];
   }
 };
 
@@ -222,14 +224,16 @@ __global__ __launch_bounds__(256) void conv_init_kernel(float* out, const float*
     out[i] = bias ? bias[fdiv(i, div_p) % OC] : 0.0f;
 }
 
-typedef Tile<128, 128, 32, 2, 4> T128x128;
-typedef Tile<128, 64, 32, 4, 2> T128x64;
-typedef Tile<64, 128, 32, 2, 4> T64x128;
-typedef Tile<64, 64, 32, 2, 2> T64x64;
-typedef Tile<128, 128, 64, 2, 4, 2> T128x128K2;
-typedef Tile<128, 64, 64, 4, 2, 2> T128x64K2;
-typedef Tile<64, 64, 64, 2, 2, 2> T64x64K2;
-typedef Tile<64, 64, 128, 2, 2, 4> T64x64K4;
+typedef Tile<128, 128, 32, 2, 4, 1, 2> T128x128;
+typedef Tile<128, 64, 32, 4, 2, 1, 2> T128x64;
+typedef Tile<64, 128, 32, 2, 4, 1, 2> T64x128;
+typedef Tile<64, 64, 32, 2, 2, 1, 2> T64x64;
+// The 16-wave 128x128 tile keeps a one-tile prefetch here: the im2col
+// loader's extra registers would not fit a second slot in its budget.
+typedef Tile<128, 128, 64, 2, 4, 2, 1> T128x128K2;
+typedef Tile<128, 64, 64, 4, 2, 2, 2> T128x64K2;
+typedef Tile<64, 64, 64, 2, 2, 2, 2> T64x64K2;
+typedef Tile<64, 64, 128, 2, 2, 4, 2> T64x64K4;
 
 // The host planner's table must describe exactly these tiles.
 template <class T>

@@ -73,9 +73,10 @@ template <> struct Vec<4> {
 // split the output tile, and WK groups of them split each k-tile (group g
 // takes k in [g*BK/WK, (g+1)*BK/WK)); the groups' partial tiles are summed
 // through LDS at the end, in group order.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_ = 1>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int WK_ = 1, int PF_ = 1>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, WK = WK_;
+  static constexpr int PF = PF_;  // global->register prefetch depth in k-tiles (1 or 2)
   static constexpr int NT = 64 * WM * WN * WK;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -86,14 +87,16 @@ struct Tile {
   static constexpr int AS = BK + 4, BS = BN + 8;
   static constexpr int A_FLOATS = BM * AS, B_FLOATS = BK * BS;
   static constexpr int STAGE = A_FLOATS + B_FLOATS;
-  // Per-k-tile loader metadata (two slots of BK int4 entries) after the
+  // Per-k-tile loader metadata (four slots of BK int4 entries) after the
   // two operand stages.
-  static constexpr int META_INTS = 2 * BK * 4;
+  static constexpr int META_SLOTS = 4;
+  static constexpr int META_INTS = META_SLOTS * BK * 4;
   static constexpr int SMEM_FLOATS = 2 * STAGE + META_INTS;
   static_assert(BKW % 8 == 0, "each wave group needs a multiple of 8 k per tile");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32x32 blocks");
   static_assert(BN % 16 == 0, "B padding assumes BN % 16 == 0");
   static_assert(NT <= 1024, "at most 1024 threads per block");
+  static_assert(PF == 1 || PF == 2, "prefetch depth 1 or 2");
   static_assert((WK - 1) * BM * BN <= 2 * STAGE, "k-group reduction must fit in the stages");
 };
 
@@ -122,13 +125,14 @@ struct RowTileLoader {
   typedef typename Vec<VEC>::T V;
   const float* base;  // first row of the block
   int K, rows_left;
-  V reg[NCH];
+  V reg[2][NCH];  // two register slots (prefetch depth up to 2)
 
   __device__ void init(const float* A, int m0, int M, int K_) {
     base = A + (size_t)m0 * K_;
     K = K_;
     rows_left = M - m0;
   }
+  template <int S>
   __device__ void load(int k0) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0, (int64_t)rows_left * K - k0);
 #pragma unroll
@@ -136,15 +140,16 @@ struct RowTileLoader {
       const int q = threadIdx.x + T::NT * i;
       const int r = q / CPR, c = (q % CPR) * VEC;
       const bool ok = r < rows_left && k0 + c < K;
-      reg[i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * K + c) * 4u : kOOB);
+      reg[S][i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * K + c) * 4u : kOOB);
     }
   }
+  template <int S>
   __device__ void store(float* As) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = threadIdx.x + T::NT * i;
       const int r = q / CPR, c = (q % CPR) * VEC;
-      *reinterpret_cast<V*>(&As[r * T::AS + c]) = reg[i];
+      *reinterpret_cast<V*>(&As[r * T::AS + c]) = reg[S][i];
     }
   }
 };
@@ -159,7 +164,7 @@ struct ColTileLoader {
   typedef typename Vec<VEC>::T V;
   const float* base;  // column n0 of row 0
   int N, K, cols_left;
-  V reg[NCH];
+  V reg[2][NCH];
 
   __device__ void init(const float* B, int n0, int N_, int K_) {
     base = B + n0;
@@ -167,6 +172,7 @@ struct ColTileLoader {
     K = K_;
     cols_left = N_ - n0;
   }
+  template <int S>
   __device__ void load(int k0) {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(base + (size_t)k0 * N, (int64_t)(K - k0) * N - (N - cols_left));
@@ -175,15 +181,16 @@ struct ColTileLoader {
       const int q = threadIdx.x + T::NT * i;
       const int r = q / CPR, c = (q % CPR) * VEC;
       const bool ok = k0 + r < K && c < cols_left;
-      reg[i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * N + c) * 4u : kOOB);
+      reg[S][i] = Vec<VEC>::load(rs, ok ? (uint32_t)(r * N + c) * 4u : kOOB);
     }
   }
+  template <int S>
   __device__ void store(float* Bs) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = threadIdx.x + T::NT * i;
       const int r = q / CPR, c = (q % CPR) * VEC;
-      *reinterpret_cast<V*>(&Bs[r * T::BS + c]) = reg[i];
+      *reinterpret_cast<V*>(&Bs[r * T::BS + c]) = reg[S][i];
     }
   }
   __device__ void meta(int) {}
@@ -267,43 +274,83 @@ __device__ __forceinline__ bool reduce_k_groups(Accum<T>& acc, float* smem, cons
   return true;
 }
 
-// The k loop over k-tiles [t_begin, t_end): prefetch k-tile t+1 into
-// registers, run the MFMAs on tile t from LDS, write t+1 to the other LDS
-// buffer, one barrier.  A loader may also keep per-k-tile metadata in LDS:
-// meta(t) writes the metadata of tile t into slot t % 2 and is called two
-// tiles ahead, so that slot is free (its last reader, load(t-2), ran before
-// the previous barrier) and visible to load(t) after the next barrier.
+// The k loop over k-tiles [t_begin, t_end).  Tile t is fetched from global
+// memory into register slot (t - t_begin) % 2 PF iterations before it is
+// needed; each iteration runs the MFMAs on tile t from one LDS buffer,
+// writes tile t+1 from its register slot into the other buffer, and ends
+// with one barrier.  With PF = 2 the loads of tile t+2 are in flight during
+// the whole of iteration t and the wait before writing tile t+1 covers only
+// loads issued an iteration earlier.  The loop is unrolled by two so that
+// register slots are compile-time indices.
+//
+// A loader may also keep per-k-tile metadata in LDS: meta(t) writes the
+// metadata of tile t into slot t % 4 and is called PF + 1 tiles ahead of
+// load(t).  The slot it overwrites was last read by load(t - 4), several
+// barriers earlier, and load(t) runs after the next barrier.
 template <class T, class AL, class BL>
-__device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
-                                float* smem, const WaveSlot& ws, int lane) {
-  acc.zero();
-  if (t_begin >= t_end) return;
-  if (BL::kHasMeta) {
-    bl.meta(t_begin);
-    bl.meta(t_begin + 1);
-    __syncthreads();
+struct MainLoop {
+  AL& al;
+  BL& bl;
+  Accum<T>& acc;
+  float* smem;
+  const WaveSlot& ws;
+  int lane, t_end;
+
+  template <int S>
+  __device__ __forceinline__ void fetch(int t) {
+    al.template load<S>(t * T::BK);
+    bl.template load<S>(t * T::BK);
   }
-  al.load(t_begin * T::BK);
-  bl.load(t_begin * T::BK);
-  al.store(smem);
-  bl.store(smem + T::A_FLOATS);
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int i = t - t_begin;
+  template <int S>
+  __device__ __forceinline__ void put(int t, float* buf) {
+    (void)t;
+    al.template store<S>(buf);
+    bl.template store<S>(buf + T::A_FLOATS);
+  }
+  // One iteration for tile t held in register slot S (S = (t - t_begin) % 2).
+  template <int S>
+  __device__ __forceinline__ void step(int t, int i) {
     float* cur = smem + (i & 1) * T::STAGE;
     float* nxt = smem + ((i + 1) & 1) * T::STAGE;
-    const bool more = t + 1 < t_end;
-    if (more) {
-      al.load((t + 1) * T::BK);
-      bl.load((t + 1) * T::BK);
+    // PF = 1 needs a single register slot: tile t+1 is fetched and written
+    // within the same iteration.
+    constexpr int NEXT = T::PF == 2 ? 1 - S : 0;
+    if (T::PF == 2) {
+      if (t + 2 < t_end) fetch<S>(t + 2);
+      if (BL::kHasMeta && t + 3 < t_end) bl.meta(t + 3);
+    } else {
+      if (t + 1 < t_end) fetch<0>(t + 1);
+      if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
     }
-    if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
     mma_tile<T>(acc, cur, cur + T::A_FLOATS, ws, lane);
-    if (more) {
-      al.store(nxt);
-      bl.store(nxt + T::A_FLOATS);
-    }
+    if (t + 1 < t_end) put<NEXT>(t + 1, nxt);
     __syncthreads();
+  }
+};
+
+template <class T, class AL, class BL>
+__device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
+                                         float* smem, const WaveSlot& ws, int lane) {
+  acc.zero();
+  if (t_begin >= t_end) return;
+  MainLoop<T, AL, BL> ml{al, bl, acc, smem, ws, lane, t_end};
+  if (BL::kHasMeta) {
+#pragma unroll
+    for (int d = 0; d <= T::PF; ++d)
+      if (t_begin + d < t_end) bl.meta(t_begin + d);
+    __syncthreads();
+  }
+  ml.template fetch<0>(t_begin);
+  if (T::PF == 2 && t_begin + 1 < t_end) ml.template fetch<1>(t_begin + 1);
+  ml.template put<0>(t_begin, smem);
+  __syncthreads();
+  if (T::PF == 2) {
+    for (int t = t_begin; t < t_end; t += 2) {
+      ml.template step<0>(t, t - t_begin);
+      if (t + 1 < t_end) ml.template step<1>(t + 1, t + 1 - t_begin);
+    }
+  } else {
+    for (int t = t_begin; t < t_end; ++t) ml.template step<0>(t, t - t_begin);
   }
 }
 
