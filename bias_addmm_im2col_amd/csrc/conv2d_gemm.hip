@@ -44,25 +44,28 @@ struct ConvArgs {
 //  * Element: valid iff 0 <= ih0+dh < H and 0 <= iw0+dw < W; invalid
 //    elements load from an out-of-range offset and read 0 (the padding).
 // A wave loads 64 consecutive columns of one row per instruction, so every
-// lane of a wave reads the same table entry (an LDS broadcast).
+// lane of a wave reads the same table entry (an LDS broadcast).  Each lane
+// gathers four consecutive rows of its column and stores them with one
+// 16-byte write into the transposed tile [BN][BK+4].
 template <class T>
 struct ImColTileLoader {
   static constexpr bool kHasMeta = true;
-  static constexpr int RPP = T::NT / T::BN;  // tile rows covered per pass
-  static constexpr int NP = T::BK / RPP;     // passes per k-tile
-  static_assert(T::NT % T::BN == 0 && T::BK % RPP == 0, "im2col tile split");
-  static_assert(T::BN % 64 == 0, "a wave must cover columns of a single row");
+  static constexpr bool kBTransposed = true;
+  static constexpr int RPP = T::NT / T::BN;  // row quads covered per pass
+  static constexpr int NP = T::BK * T::BN / T::NT;  // elements per thread
+  static constexpr int NQ = NP / 4;                 // quads per thread
+  static_assert(T::NT % T::BN == 0 && NP % 4 == 0 && T::BK == 4 * RPP * NQ, "im2col tile split");
   static_assert(T::NT >= T::BK, "one thread per table row");
   const ConvArgs* a;
   int4* tbl;  // [META_SLOTS][BK] {offset, dh, dw, unused}
-  int row0, col, cbase, ih0, iw0;
-  float reg[2][NP];  // two register slots (prefetch depth up to 2)
+  int q0, col, cbase, ih0, iw0;
+  f32x4 reg[2][NQ];  // two register slots (prefetch depth up to 2)
 
   __device__ void init(const ConvArgs& args, int n0, int4* table) {
     a = &args;
     tbl = table;
     col = threadIdx.x % T::BN;
-    row0 = threadIdx.x / T::BN;
+    q0 = threadIdx.x / T::BN;
     const int n = n0 + col;
     const bool cok = n < args.N;
     const uint32_t nn = cok ? (uint32_t)n : 0u;
@@ -103,18 +106,24 @@ struct ImColTileLoader {
     // NP global loads issue back to back.
     int4 e[NP];
 #pragma unroll
-    for (int i = 0; i < NP; ++i) e[i] = slot[row0 + RPP * i];
+    for (int i = 0; i < NQ; ++i)
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const unsigned ok = (unsigned)((unsigned)(ih0 + e[i].y) < (unsigned)a->H) &
-                          (unsigned)((unsigned)(iw0 + e[i].z) < (unsigned)a->W);
-      reg[S][i] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + e[i].x) * 4u : kOOB);
-    }
+      for (int s = 0; s < 4; ++s) e[4 * i + s] = slot[4 * (q0 + RPP * i) + s];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int4 v = e[4 * i + s];
+        const unsigned ok = (unsigned)((unsigned)(ih0 + v.y) < (unsigned)a->H) &
+                            (unsigned)((unsigned)(iw0 + v.z) < (unsigned)a->W);
+        reg[S][i][s] = Vec<1>::load(rs, ok ? (uint32_t)(cbase + v.x) * 4u : kOOB);
+      }
   }
   template <int S>
-  __device__ void store(float* Bs) const {
+  __device__ void store(float* Bt) const {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) Bs[(row0 + RPP * i) * T::BS + col] = reg[S][i];
+    for (int i = 0; i < NQ; ++i)
+      *reinterpret_cast<f32x4*>(&Bt[col * T::BTS + 4 * (q0 + RPP * i)]) = reg[S][i];
   }
 };
 

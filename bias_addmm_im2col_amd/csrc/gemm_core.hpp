@@ -85,7 +85,11 @@ struct Tile {
   // consecutive rows spread over all banks.  B is [BK][BN+8]: rows four
   // apart start 32 banks apart.
   static constexpr int AS = BK + 4, BS = BN + 8;
-  static constexpr int A_FLOATS = BM * AS, B_FLOATS = BK * BS;
+  // A loader may instead keep B transposed, [BN][BK+4] like A, so that the
+  // MFMA B fragments are 16-byte reads too.
+  static constexpr int BTS = BK + 4;
+  static constexpr int A_FLOATS = BM * AS;
+  static constexpr int B_FLOATS = BK * BS > BN * BTS ? BK * BS : BN * BTS;
   static constexpr int STAGE = A_FLOATS + B_FLOATS;
   // Per-k-tile loader metadata (four slots of BK int4 entries) after the
   // two operand stages.
@@ -119,6 +123,7 @@ __device__ inline WaveSlot wave_slot() {
 template <class T, int VEC>
 struct RowTileLoader {
   static constexpr bool kHasMeta = false;
+  static constexpr bool kBTransposed = false;
   static constexpr int CPR = T::BK / VEC;
   static constexpr int NCH = T::BM * CPR / T::NT;
   static_assert((T::BM * CPR) % T::NT == 0, "A tile must split evenly over threads");
@@ -158,6 +163,7 @@ struct RowTileLoader {
 template <class T, int VEC>
 struct ColTileLoader {
   static constexpr bool kHasMeta = false;
+  static constexpr bool kBTransposed = false;
   static constexpr int CPR = T::BN / VEC;
   static constexpr int NCH = T::BK * CPR / T::NT;
   static_assert((T::BK * CPR) % T::NT == 0, "B tile must split evenly over threads");
@@ -212,23 +218,30 @@ struct Accum {
 };
 
 // One k-tile: for the wave's k range [kofs, kofs + BKW), BKW/2 MFMA steps
-// for every 32x32 block of the wave's sub-tile.
-template <class T>
+// for every 32x32 block of the wave's sub-tile.  B is read from [BK][BN+8]
+// (four 4-byte reads per lane and 4 steps) or, with BT, from the transposed
+// [BN][BK+4] (one 16-byte read).
+template <class T, bool BT>
 __device__ __forceinline__ void mma_tile(Accum<T>& acc, const float* As, const float* Bs,
-                                const WaveSlot& ws, int lane) {
+                                         const WaveSlot& ws, int lane) {
   const int c = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int g = 0; g < T::BKW / 8; ++g) {
     const int k = ws.kofs + 8 * g + 4 * h;
     f32x4 a[T::FM];
-    float b[T::FN][4];
+    f32x4 b[T::FN];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
       a[i] = *reinterpret_cast<const f32x4*>(&As[(ws.wm0 + 32 * i + c) * T::AS + k]);
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j)
+    for (int j = 0; j < T::FN; ++j) {
+      if (BT) {
+        b[j] = *reinterpret_cast<const f32x4*>(&Bs[(ws.wn0 + 32 * j + c) * T::BTS + k]);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[j][s] = Bs[(k + s) * T::BS + ws.wn0 + 32 * j + c];
+        for (int s = 0; s < 4; ++s) b[j][s] = Bs[(k + s) * T::BS + ws.wn0 + 32 * j + c];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -322,7 +335,7 @@ struct MainLoop {
       if (t + 1 < t_end) fetch<0>(t + 1);
       if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
     }
-    mma_tile<T>(acc, cur, cur + T::A_FLOATS, ws, lane);
+    mma_tile<T, BL::kBTransposed>(acc, cur, cur + T::A_FLOATS, ws, lane);
     if (t + 1 < t_end) put<NEXT>(t + 1, nxt);
     __syncthreads();
   }
