@@ -91,15 +91,15 @@ def load_traffic(kernel: str):
 class Case:
     def __init__(self, name, torch, baim, I):
         self.name = name
-        c = I.CASES[name]
+        c = I.CASES[name] if name in I.CASES else I.LINEAR_CASES[name]
         self.c = c
         self.op = c.kind
         self.flops = c.flops
-        M, N, K = (c.M, c.N, c.K) if c.kind == "addmm" else c.gemm_mnk
+        M, N, K = (c.M, c.N, c.K) if c.kind != "conv" else c.gemm_mnk
         p = baim.gemm_plan(M, N, K)
         self.plan = p
         # one kernel instance per (op, block tile, waves, wave groups, K split)
-        self.kernel = (f"baim::{'addmm_kernel' if c.kind == 'addmm' else 'conv2d_gemm_kernel'}"
+        self.kernel = (f"baim::{'conv2d_gemm_kernel' if c.kind == 'conv' else 'addmm_kernel'}"
                        f"<Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
                        f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else "")
                        + (f" stream {p['stream_blocks']}" if p['stream_blocks'] > 0 else ""))
@@ -110,6 +110,14 @@ class Case:
             self.out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
             self.K = c.K
             self.run = lambda: baim.addmm_f32(self.out, self.s, self.a, self.b, c.beta, c.alpha)
+        elif c.kind == "linear":
+            x, w, b = I.linear_inputs(c)
+            self.host = (x, w, b)
+            self.x, self.w = x.cuda(), w.cuda()
+            self.bias = None if b is None else b.cuda()
+            self.out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+            self.K = c.K
+            self.run = lambda: baim.linear_f32(self.out, self.x, self.w, self.bias)
         else:
             x, w, bias = I.conv_inputs(c)
             self.host = (x, w, bias)
@@ -119,6 +127,32 @@ class Case:
             self.K = c.IC * c.KH * c.KW
             self.run = lambda: baim.conv2d_gemm_f32(self.out, self.x, self.w, self.bias,
                                                     c.stride, c.padding, c.dilation, 1)
+
+
+def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
+    """Ops beyond the step's workload (linear, weight [N,K]), timed the same
+    way but reported separately: they are not part of `value`.  Each case
+    first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
+    switch to new buffers)."""
+    rows = []
+    for name in I.LINEAR_CASES:
+        cs = Case(name, torch, baim, I)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warmup_s:
+            for _ in range(10):
+                cs.run()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            cs.run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        tf = cs.flops / us / 1e6
+        rows.append({"case": name, "op": "linear", "kernel": cs.kernel, "us": round(us, 2),
+                     "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)})
+    return rows
 
 
 def cpu_baseline(cases, budget_s):
@@ -230,6 +264,8 @@ def main():
     n_launch = k_launch[dom]
     traffic = load_traffic(dom)
 
+    widened = time_widened(torch, baim, I)
+
     cpu = cpu_baseline(cases, args.cpu_seconds)
 
     line = {
@@ -266,6 +302,7 @@ def main():
             "avg_launch_us": round(k_time[dom] / n_launch * 1e3, 2),
         },
         "cpu_baseline": cpu,
+        "widened": widened,
     }
     print(json.dumps(line), flush=True)
 

@@ -7,6 +7,8 @@ arguments and allocates outputs with torch:
 * ``addmm(self, mat1, mat2, *, beta=1, alpha=1)`` --
   ``beta*self + alpha*(mat1 @ mat2)`` with self ``[N]`` (or ``[1,N]``) or
   ``[M,N]`` ("[ExecuTorch][WebGPU] Add optimized addmm op", Solution).
+* ``linear(x, weight, bias=None)`` -- ``x @ weight^T + bias`` with weight
+  ``[N,K]``, the linear_fp32 form the addmm page shares its GEMM with.
 * ``conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1,
   groups=1)`` -- groups==1 NCHW convolution as an implicit-im2col GEMM
   ("et_vk conv2d: route standard (groups==1) conv through an im2col tiled
@@ -20,7 +22,8 @@ from __future__ import annotations
 
 from . import _capi
 
-__all__ = ["addmm", "conv2d", "addmm_f32", "conv2d_gemm_f32", "conv2d_out_hw", "gemm_plan",
+__all__ = ["addmm", "linear", "conv2d", "addmm_f32", "linear_f32", "conv2d_gemm_f32",
+           "conv2d_out_hw", "gemm_plan",
            "BaimError", "library_path"]
 
 
@@ -138,6 +141,49 @@ def addmm(self, mat1, mat2, *, beta=1, alpha=1):
     _dev_f32(mat2, "mat2")
     out = torch.empty((mat1.shape[0], mat2.shape[1]), dtype=torch.float32, device=mat1.device)
     return addmm_f32(out, self, mat1, mat2, beta, alpha)
+
+
+def linear_f32(out, x, weight, bias=None):
+    """out[M,N] = x[M,K] @ weight[N,K]^T + bias[N], written into ``out``."""
+    import torch
+    out, x, weight = _dev_f32(out, "out"), _dev_f32(x, "x"), _dev_f32(weight, "weight")
+    if x.dim() != 2 or weight.dim() != 2 or out.dim() != 2:
+        raise ValueError("x, weight and out must be 2-D")
+    M, K = x.shape
+    N, K2 = weight.shape
+    if K2 != K:
+        raise ValueError(f"weight must be [N, K={K}], got {list(weight.shape)}")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}], got {list(out.shape)}")
+    devs = {out.device, x.device, weight.device}
+    bias_ptr = None
+    if bias is not None:
+        bias = _dev_f32(bias, "bias")
+        if tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be [{N}]")
+        bias_ptr = bias.data_ptr()
+        devs.add(bias.device)
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.linear_f32(out.data_ptr(), x.data_ptr(), weight.data_ptr(), bias_ptr, M, N, K,
+                              _stream(dev))
+    _check(st)
+    return out
+
+
+def linear(x, weight, bias=None):
+    """x[..., K] @ weight[N, K]^T + bias[N] as a new [..., N] fp32 tensor."""
+    import torch
+    x, weight = _dev_f32(x, "x"), _dev_f32(weight, "weight")
+    if weight.dim() != 2 or x.dim() < 1:
+        raise ValueError("weight must be 2-D and x at least 1-D")
+    lead = tuple(x.shape[:-1])
+    x2 = x.reshape(-1, x.shape[-1])
+    out = torch.empty((x2.shape[0], weight.shape[0]), dtype=torch.float32, device=x.device)
+    linear_f32(out, x2, weight, bias)
+    return out.reshape(lead + (weight.shape[0],))
 
 
 def gemm_plan(M, N, K):

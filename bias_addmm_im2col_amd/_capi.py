@@ -25,7 +25,7 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/baim.h declares.
-EXPORTS = ("addmm_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_gemm_plan",
+EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_gemm_plan",
            "baim_last_error", "baim_version")
 
 _lib = None
@@ -46,6 +46,8 @@ def lib():
     L.addmm_f32.argtypes = [_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _i64, _i64,
                             ctypes.c_float, ctypes.c_float, _vp]
     L.addmm_f32.restype = ctypes.c_int
+    L.linear_f32.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+    L.linear_f32.restype = ctypes.c_int
     L.conv2d_gemm_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 14 + [_vp]
     L.conv2d_gemm_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
@@ -66,6 +68,10 @@ def last_error() -> str:
 
 def addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream) -> int:
     return lib().addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream)
+
+
+def linear_f32(out, x, w, bias, M, N, K, stream) -> int:
+    return lib().linear_f32(out, x, w, bias, M, N, K, stream)
 
 
 def conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,

@@ -2,7 +2,10 @@
 // cores ("[ExecuTorch][WebGPU] Add optimized addmm op", Solution and
 // Implementation paragraphs: mat1 [M,K] and mat2 [K,N] row-major, the
 // epilogue picks self[r*N + c] for a full self and the broadcast self[c]
-// otherwise, and writes beta*self + alpha*acc).
+// otherwise, and writes beta*self + alpha*acc).  The same kernel computes
+// linear, out = x @ weight^T + bias with weight [N,K] (the page's
+// linear_fp32 reads that transposed weight), when instantiated with WNK:
+// the weight's K-contiguous rows load straight into the transposed B tile.
 //
 // Work split (see gemm_core.hpp): one tile per block; or K slices; or
 // stream pieces.  A tile cut into exactly two pieces is combined without a
@@ -13,6 +16,8 @@
 // else) out starts as beta*self and the slices add alpha*partial with
 // hardware fp32 atomics.
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "gemm_core.hpp"
 #include "launch.hpp"
@@ -31,14 +36,14 @@ struct AddmmArgs {
   Sched sched;
 };
 
-template <class T, int VA, int VB>
+template <class T, int VA, int VB, bool WNK>
 __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int m0, int n0, int tb,
                                    int te, int epi) {
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
   RowTileLoader<T, VA> al;
   al.init(p.A, m0, p.M, p.K);
-  ColTileLoader<T, VB> bl;
+  typename std::conditional<WNK, KRowLoader<T, VB, T::BN, true>, ColTileLoader<T, VB>>::type bl;
   bl.init(p.B, n0, p.N, p.K);
   Accum<T> acc;
   mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
@@ -110,11 +115,11 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
   }
 }
 
-template <class T, int VA, int VB, int MODE>
+template <class T, int VA, int VB, int MODE, bool WNK>
 __global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
   for_each_piece<MODE>(p.sched, T::BM, T::BN, [&](int m0, int n0, int tb, int te, int epi) __attribute__((always_inline)) {
-    addmm_piece<T, VA, VB>(p, smem, m0, n0, tb, te, epi);
+    addmm_piece<T, VA, VB, WNK>(p, smem, m0, n0, tb, te, epi);
   });
 }
 
@@ -172,21 +177,26 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
                   same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
               "tile table out of sync with the compiled tiles");
 
-template <class T, int VA, int VB, int MODE>
+template <class T, int VA, int VB, int MODE, bool WNK = false>
 static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE, WNK>), dim3(nblocks), dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
 // Stream pieces are compiled for aligned operands only (the launcher falls
 // back to one tile per block otherwise).
-template <class T, int CFG, int MODE>
+// Linear (WNK) is compiled with 16-byte loads of both operands or with
+// 4-byte loads of both (its x and weight rows share K).
+template <class T, int CFG, int MODE, bool WNK>
 static hipError_t launch_vec(const AddmmArgs& a, int nblocks, bool va, bool vb, hipStream_t s) {
   if constexpr (MODE == MODE_STREAM) {
-    if constexpr (kTileStream[CFG]) return launch_t<T, 4, 4, MODE_STREAM>(a, nblocks, s);
+    if constexpr (kTileStream[CFG]) return launch_t<T, 4, 4, MODE_STREAM, WNK>(a, nblocks, s);
     return hipErrorInvalidValue;  // never planned
   } else if constexpr (MODE == MODE_SLICES && !kTileSlices[CFG]) {
     return hipErrorInvalidValue;  // never planned
+  } else if constexpr (WNK) {
+    if (va && vb) return launch_t<T, 4, 4, MODE, true>(a, nblocks, s);
+    return launch_t<T, 1, 1, MODE, true>(a, nblocks, s);
   } else {
     if (va && vb) return launch_t<T, 4, 4, MODE>(a, nblocks, s);
     if (va) return launch_t<T, 4, 1, MODE>(a, nblocks, s);
@@ -195,33 +205,34 @@ static hipError_t launch_vec(const AddmmArgs& a, int nblocks, bool va, bool vb, 
   }
 }
 
-template <int MODE>
+template <int MODE, bool WNK>
 static hipError_t launch_cfg(int cfg, const AddmmArgs& a, int nblocks, bool va, bool vb,
                              hipStream_t s) {
   switch (cfg) {
     case TILE_128x64:
-      return launch_vec<T128x64, TILE_128x64, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64, TILE_128x64, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_64x128:
-      return launch_vec<T64x128, TILE_64x128, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T64x128, TILE_64x128, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_64x64:
-      return launch_vec<T64x64, TILE_64x64, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64, TILE_64x64, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_128x128_K2:
-      return launch_vec<T128x128K2, TILE_128x128_K2, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128K2, TILE_128x128_K2, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_128x64_K2:
-      return launch_vec<T128x64K2, TILE_128x64_K2, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64K2, TILE_128x64_K2, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_64x64_K2:
-      return launch_vec<T64x64K2, TILE_64x64_K2, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K2, TILE_64x64_K2, MODE, WNK>(a, nblocks, va, vb, s);
     case TILE_64x64_K4:
-      return launch_vec<T64x64K4, TILE_64x64_K4, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K4, TILE_64x64_K4, MODE, WNK>(a, nblocks, va, vb, s);
     default:
-      return launch_vec<T128x128, TILE_128x128, MODE>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128, TILE_128x128, MODE, WNK>(a, nblocks, va, vb, s);
   }
 }
 
 hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
-  // 16-byte vector loads need K (resp. N) divisible by 4 and aligned bases.
+  // 16-byte vector loads need the contiguous dim (K for mat1 and for a
+  // [N,K] weight, N for mat2 [K,N]) divisible by 4 and aligned bases.
   const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
-  const bool vb = p.N % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
+  const bool vb = (p.weight_nk ? p.K : p.N) % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
   GemmPlan plan = plan_gemm(p.M, p.N, p.K, getenv("BAIM_TILE"));
   if (plan.mode == MODE_STREAM && !(va && vb)) plan = plan_tiles_only(plan, p.M, p.N, p.K);
   AddmmArgs a;
@@ -246,13 +257,23 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (p.weight_nk) {
+    switch (plan.mode) {
+      case MODE_SLICES:
+        return launch_cfg<MODE_SLICES, true>(plan.cfg, a, nblocks, va, vb, stream);
+      case MODE_STREAM:
+        return launch_cfg<MODE_STREAM, true>(plan.cfg, a, nblocks, va, vb, stream);
+      default:
+        return launch_cfg<MODE_TILE, true>(plan.cfg, a, nblocks, va, vb, stream);
+    }
+  }
   switch (plan.mode) {
     case MODE_SLICES:
-      return launch_cfg<MODE_SLICES>(plan.cfg, a, nblocks, va, vb, stream);
+      return launch_cfg<MODE_SLICES, false>(plan.cfg, a, nblocks, va, vb, stream);
     case MODE_STREAM:
-      return launch_cfg<MODE_STREAM>(plan.cfg, a, nblocks, va, vb, stream);
+      return launch_cfg<MODE_STREAM, false>(plan.cfg, a, nblocks, va, vb, stream);
     default:
-      return launch_cfg<MODE_TILE>(plan.cfg, a, nblocks, va, vb, stream);
+      return launch_cfg<MODE_TILE, false>(plan.cfg, a, nblocks, va, vb, stream);
   }
 }
 

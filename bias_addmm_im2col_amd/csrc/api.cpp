@@ -146,6 +146,7 @@ baim_status addmm_f32(float* out, const float* self, int self_2d, const float* m
   p.self = reads_self ? self : nullptr;
   p.mat1 = mat1;
   p.mat2 = mat2;
+  p.weight_nk = false;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -153,6 +154,40 @@ baim_status addmm_f32(float* out, const float* self, int self_2d, const float* m
   p.beta = beta;
   p.alpha = alpha;
   return launched(baim::launch_addmm(p, (hipStream_t)stream), "addmm_f32");
+}
+
+baim_status linear_f32(float* out, const float* x, const float* weight, const float* bias,
+                       int64_t M, int64_t N, int64_t K, void* stream) {
+  g_err.clear();
+  if (M < 0 || N < 0 || K < 0)
+    return fail(BAIM_ERR_SHAPE, "linear: sizes must be >= 0 (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  const int64_t n_out = elems({M, N}), n_x = elems({M, K}), n_w = elems({N, K});
+  if (n_out < 0 || n_x < 0 || n_w < 0 || n_out >= kMaxElems || n_x >= kMaxElems ||
+      n_w >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "linear: every tensor must have fewer than 2^31 elements");
+  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "linear: K must be below 2^21");
+  if (N >= kMaxAddmmN) return fail(BAIM_ERR_TOO_LARGE, "linear: N must be below 2^23");
+  if (M == 0 || N == 0) return BAIM_OK;
+  if (!out) return fail(BAIM_ERR_NULL, "linear: out is NULL");
+  if (K > 0 && (!x || !weight)) return fail(BAIM_ERR_NULL, "linear: x/weight is NULL");
+  if ((K > 0 && (overlap(out, n_out, x, n_x) || overlap(out, n_out, weight, n_w))) ||
+      overlap(out, n_out, bias, N))
+    return fail(BAIM_ERR_ALIAS, "linear: out overlaps an input");
+
+  baim::AddmmProblem p;
+  p.out = out;
+  p.self = bias;
+  p.mat1 = x;
+  p.mat2 = weight;
+  p.weight_nk = true;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.self_mode = bias ? 1 : 0;
+  p.beta = 1.0f;
+  p.alpha = 1.0f;
+  return launched(baim::launch_addmm(p, (hipStream_t)stream), "linear_f32");
 }
 
 baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,

@@ -118,24 +118,27 @@ __device__ inline WaveSlot wave_slot() {
 
 // ---------------------------------------------------------------- loaders
 
-// A tile from a row-major [rows][ld] matrix whose contiguous dim is K
-// (mat1 [M,K]; the conv weight viewed as [OC, IC*KH*KW]).
-template <class T, int VEC>
-struct RowTileLoader {
+// ROWS x BK tile of a row-major matrix whose contiguous dim is K, stored in
+// LDS as [ROWS][BK+4].  As the A operand: rows m of mat1 [M,K] or of the
+// conv weight viewed as [OC, IC*KH*KW].  As the B operand (AS_B): rows n
+// of a [N,K] weight, which is B already transposed.
+template <class T, int VEC, int ROWS, bool AS_B>
+struct KRowLoader {
   static constexpr bool kHasMeta = false;
-  static constexpr bool kBTransposed = false;
+  static constexpr bool kBTransposed = AS_B;
   static constexpr int CPR = T::BK / VEC;
-  static constexpr int NCH = T::BM * CPR / T::NT;
-  static_assert((T::BM * CPR) % T::NT == 0, "A tile must split evenly over threads");
+  static constexpr int NCH = ROWS * CPR / T::NT;
+  static_assert((ROWS * CPR) % T::NT == 0, "tile must split evenly over threads");
+  static_assert(T::AS == T::BTS, "A and transposed-B rows share one stride");
   typedef typename Vec<VEC>::T V;
   const float* base;  // first row of the block
   int K, rows_left;
   V reg[2][NCH];  // two register slots (prefetch depth up to 2)
 
-  __device__ void init(const float* A, int m0, int M, int K_) {
-    base = A + (size_t)m0 * K_;
+  __device__ void init(const float* A, int r0, int R, int K_) {
+    base = A + (size_t)r0 * K_;
     K = K_;
-    rows_left = M - m0;
+    rows_left = R - r0;
   }
   template <int S>
   __device__ void load(int k0) {
@@ -149,15 +152,19 @@ struct RowTileLoader {
     }
   }
   template <int S>
-  __device__ void store(float* As) const {
+  __device__ void store(float* dst) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int q = threadIdx.x + T::NT * i;
       const int r = q / CPR, c = (q % CPR) * VEC;
-      *reinterpret_cast<V*>(&As[r * T::AS + c]) = reg[S][i];
+      *reinterpret_cast<V*>(&dst[r * T::AS + c]) = reg[S][i];
     }
   }
+  __device__ void meta(int) {}
 };
+
+template <class T, int VEC>
+using RowTileLoader = KRowLoader<T, VEC, T::BM, false>;
 
 // B tile from a row-major [K][N] matrix (mat2, read as mat2[k*N + n]).
 template <class T, int VEC>

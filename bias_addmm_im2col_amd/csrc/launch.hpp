@@ -11,7 +11,8 @@ struct AddmmProblem {
   float* out;
   const float* self;  // read only when self_mode != 0
   const float* mat1;
-  const float* mat2;
+  const float* mat2;  // [K,N]; or, with weight_nk, a [N,K] weight (linear)
+  bool weight_nk;
   int M, N, K;
   int self_mode;  // 0: beta == 0, self not read; 1: self [N]; 2: self [M,N]
   float beta, alpha;

@@ -75,6 +75,23 @@ class ConvCase:
         return 2 * M * N * K
 
 
+@dataclass(frozen=True)
+class LinearCase:
+    name: str
+    M: int
+    K: int
+    N: int
+    x: tuple
+    w: tuple
+    bias: tuple | None
+    seed: int = 0
+    kind: str = field(default="linear", init=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
 U11 = ("U", -1.0, 1.0)
 U01 = ("U", 0.0, 1.0)
 
@@ -102,6 +119,13 @@ CASES = {c.name: c for c in [
     AddmmCase("up_proj_4096x1024x4096", 4096, 1024, 4096, N(1), N(0.02), N(0.02), False),
     AddmmCase("down_proj_4096x4096x1024", 4096, 4096, 1024, N(1), N(0.02), N(0.02), False),
     AddmmCase("ragged_577x1024x4096_full_self", 577, 1024, 4096, N(1), N(0.02), N(1), True),
+]}
+
+# linear (x @ weight^T + bias, weight [N,K]): the FFN projection shape with
+# the weight stored as [out_features, in_features].
+LINEAR_CASES = {c.name: c for c in [
+    LinearCase("linear_ffn_2048x768x3072", 2048, 768, 3072, N(1), N(0.02), N(0.02)),
+    LinearCase("linear_ragged_577x1024x4096_nobias", 577, 1024, 4096, N(1), N(0.02), None),
 ]}
 
 # Groups of cases as the workload list states them (small / FFN / stem /
@@ -148,5 +172,18 @@ def conv_inputs(case: ConvCase):
     return x, w, b
 
 
+def linear_inputs(case: LinearCase):
+    """(x [M,K], weight [N,K], bias [N] or None)."""
+    g = torch.Generator("cpu").manual_seed(case.seed)
+    x = draw((case.M, case.K), case.x, g)
+    w = draw((case.N, case.K), case.w, g)
+    b = None if case.bias is None else draw((case.N,), case.bias, g)
+    return x, w, b
+
+
 def inputs(case):
-    return addmm_inputs(case) if case.kind == "addmm" else conv_inputs(case)
+    if case.kind == "addmm":
+        return addmm_inputs(case)
+    if case.kind == "linear":
+        return linear_inputs(case)
+    return conv_inputs(case)

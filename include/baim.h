@@ -69,6 +69,27 @@ baim_status addmm_f32(float* out, const float* self, int self_2d,
                       void* stream);
 
 /*
+ * linear_f32: out[M,N] = x[M,K] @ weight[N,K]^T + bias[N].
+ *
+ * From "[ExecuTorch][WebGPU] Add optimized addmm op", Implementation
+ * paragraph: the addmm kernel shares its tiled-GEMM skeleton with
+ * linear_fp32, whose weight is read transposed, as [N,K] (addmm instead
+ * reads mat2 as [K,N]).  This is that linear: the same kernels and tile
+ * choice as addmm_f32, with the weight's K-contiguous rows loaded directly
+ * as the transposed B tile.
+ *
+ *  out     [M,N] fp32, written in full.
+ *  x       [M,K] fp32.   weight  [N,K] fp32.   May be NULL only if K == 0.
+ *  bias    [N] fp32, or NULL for no bias.
+ *  M,N,K   >= 0.  M == 0 or N == 0: nothing to do, BAIM_OK.  K == 0: out is
+ *          the broadcast bias (or 0).
+ *  stream  hipStream_t or NULL.
+ */
+baim_status linear_f32(float* out, const float* x, const float* weight,
+                       const float* bias, int64_t M, int64_t N, int64_t K,
+                       void* stream);
+
+/*
  * conv2d_gemm_f32: out = conv2d(input, weight, bias) for groups == 1,
  * computed as the GEMM  out[oc, n] = sum_kk weight[oc, kk] * col[kk, n]
  * + bias[oc], with M = OC, N = B*OH*OW, K = IC*KH*KW and col the implicit

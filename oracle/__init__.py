@@ -11,6 +11,9 @@ marshals numpy arrays.  Definitions followed:
 * addmm -- "[ExecuTorch][WebGPU] Add optimized addmm op" (PR #20855),
   Solution/Implementation: ``out = beta*self + alpha*(mat1 @ mat2)``,
   self broadcast from [N] or full [M,N].
+* linear -- the same page, Implementation: the GEMM skeleton shared with
+  linear_fp32, which reads a transposed [N,K] weight:
+  ``out = x @ weight^T + bias``.
 * conv2d -- "et_vk conv2d: route standard (groups==1) conv through an im2col
   tiled GEMM" (PR #20873), Solution/Implementation: direct sum over
   (ic, kh, kw) taps at ih = oh*sH - pH + kh*dH (and the W analogue),
@@ -69,6 +72,10 @@ def _load():
                                     ctypes.c_float, ctypes.c_float, _i64, _lp, _lp,
                                     _dp, _dp]
     lib.oracle_addmm_at.restype = None
+    lib.oracle_linear.argtypes = [_i64, _i64, _i64, _fp, _fp, _fp, _dp, _dp]
+    lib.oracle_linear.restype = None
+    lib.oracle_linear_at.argtypes = [_i64, _i64, _i64, _fp, _fp, _fp, _i64, _lp, _lp, _dp, _dp]
+    lib.oracle_linear_at.restype = None
     lib.oracle_conv_out_size.argtypes = [_i64] * 5
     lib.oracle_conv_out_size.restype = _i64
     lib.oracle_conv2d.argtypes = [_i64] * 13 + [_fp, _fp, _fp, _dp, _dp]
@@ -146,6 +153,42 @@ def addmm_at(mat1, mat2, self, self_2d: bool, beta, alpha, rows, cols) -> Result
                             int(bool(self_2d)), beta, alpha, n, _ptr(rows, _lp),
                             _ptr(cols, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
     return Result(ref, sabs, _selfabs_addmm(self, self_2d, beta, M, N, rows, cols))
+
+
+def _selfabs_bias(bias, M, N, rows=None, cols=None):
+    if bias is None:
+        return np.zeros((M, N) if rows is None else (len(rows),))
+    b = np.abs(bias.astype(np.float64))
+    return np.broadcast_to(b, (M, N)) if rows is None else b[cols]
+
+
+def linear(x, weight, bias=None) -> Result:
+    """Full [M,N] reference of x[M,K] @ weight[N,K]^T + bias[N] in fp64."""
+    x, weight, bias = _f32(x), _f32(weight), _f32(bias)
+    M, K = x.shape
+    N, K2 = weight.shape
+    assert K == K2
+    ref = np.empty((M, N), np.float64)
+    sabs = np.empty((M, N), np.float64)
+    _load().oracle_linear(M, N, K, _ptr(x, _fp), _ptr(weight, _fp), _ptr(bias, _fp),
+                          _ptr(ref, _dp), _ptr(sabs, _dp))
+    return Result(ref, sabs, _selfabs_bias(bias, M, N))
+
+
+def linear_at(x, weight, bias, rows, cols) -> Result:
+    """Linear reference at sampled outputs (rows[s], cols[s])."""
+    x, weight, bias = _f32(x), _f32(weight), _f32(bias)
+    M, K = x.shape
+    N = weight.shape[0]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    assert (rows >= 0).all() and (rows < M).all() and (cols >= 0).all() and (cols < N).all()
+    n = rows.size
+    ref = np.empty(n, np.float64)
+    sabs = np.empty(n, np.float64)
+    _load().oracle_linear_at(M, N, K, _ptr(x, _fp), _ptr(weight, _fp), _ptr(bias, _fp), n,
+                             _ptr(rows, _lp), _ptr(cols, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
+    return Result(ref, sabs, _selfabs_bias(bias, M, N, rows, cols))
 
 
 def conv_out_size(size, k, stride, pad, dil) -> int:

@@ -13,6 +13,9 @@
  *    out = beta*self + alpha*(mat1 @ mat2) with mat1 [M,K], mat2 [K,N]
  *    row-major (mat2 read as mat2[k*N + n]), and self either broadcast from
  *    [N] (self[c]) or a full [M,N] (self[r*N + c]).
+ *  - the same page, Implementation paragraph: the addmm kernel shares its
+ *    tiled-GEMM skeleton with linear_fp32, which reads a transposed [N,K]
+ *    weight: linear computes out[m,n] = sum_k x[m,k] * weight[n,k] + bias[n].
  *  - "et_vk conv2d: route standard (groups==1) conv through an im2col tiled
  *    GEMM" (pytorch/executorch PR #20873), Solution and Implementation
  *    paragraphs: groups==1 conv is a GEMM with M=OC, N=B*OH*OW, K=IC*KH*KW;
@@ -93,6 +96,43 @@ void oracle_addmm_at(int64_t M, int64_t N, int64_t K, const float* mat1,
   for (int64_t s = 0; s < n; ++s)
     addmm_one(rows[s], cols[s], N, K, mat1, mat2, self, self_2d, beta, alpha,
               &ref[s], &sabs[s]);
+}
+
+/* One linear output element: the dot product of row m of x and row n of
+ * weight (both K-contiguous), plus bias[n] (NULL bias means 0). */
+static void linear_one(int64_t m, int64_t n, int64_t K, const float* x,
+                       const float* w, const float* bias, double* ref,
+                       double* sabs) {
+  double acc = 0.0, aabs = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double p = (double)x[m * K + k] * (double)w[n * K + k];
+    acc += p;
+    aabs += fabs(p);
+  }
+  *ref = (bias ? (double)bias[n] : 0.0) + acc;
+  *sabs = aabs;
+}
+
+/* Full linear: ref and sabs are [M,N] row-major doubles. */
+void oracle_linear(int64_t M, int64_t N, int64_t K, const float* x,
+                   const float* w, const float* bias, double* ref,
+                   double* sabs) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n)
+      linear_one(m, n, K, x, w, bias, &ref[m * N + n], &sabs[m * N + n]);
+}
+
+/* linear at n sampled outputs (rows[s], cols[s]). */
+void oracle_linear_at(int64_t M, int64_t N, int64_t K, const float* x,
+                      const float* w, const float* bias, int64_t n,
+                      const int64_t* rows, const int64_t* cols, double* ref,
+                      double* sabs) {
+  (void)M;
+  (void)N;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < n; ++s)
+    linear_one(rows[s], cols[s], K, x, w, bias, &ref[s], &sabs[s]);
 }
 
 /* Output spatial size of a conv along one axis; <= 0 means no valid output. */

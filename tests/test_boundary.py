@@ -82,6 +82,34 @@ def test_addmm_empty_output_is_ok_without_launch(lib):
     assert _capi.last_error() == ""
 
 
+def linear(out=O, x=A, w=Bp, bias=S, M=8, N=8, K=8):
+    return _capi.linear_f32(out, x, w, bias, M, N, K, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), _capi.BAIM_ERR_SHAPE),
+    (dict(K=-2), _capi.BAIM_ERR_SHAPE),
+    (dict(out=None), _capi.BAIM_ERR_NULL),
+    (dict(x=None), _capi.BAIM_ERR_NULL),
+    (dict(w=None), _capi.BAIM_ERR_NULL),
+    (dict(M=1 << 16, K=1 << 15), _capi.BAIM_ERR_TOO_LARGE),
+    (dict(N=1 << 16, K=1 << 15), _capi.BAIM_ERR_TOO_LARGE),
+    (dict(M=1, N=1, K=1 << 21), _capi.BAIM_ERR_TOO_LARGE),
+    (dict(out=A + 4), _capi.BAIM_ERR_ALIAS),
+    (dict(out=Bp - 8), _capi.BAIM_ERR_ALIAS),
+    (dict(out=S - 4), _capi.BAIM_ERR_ALIAS),
+])
+def test_linear_rejects(lib, kw, status):
+    st = linear(**kw)
+    assert st == status, (st, _capi.last_error())
+    assert _capi.last_error()
+
+
+def test_linear_null_bias_and_empty_are_fine_to_validate(lib):
+    assert linear(M=0) == _capi.BAIM_OK
+    assert linear(N=0, out=None, x=None, w=None) == _capi.BAIM_OK
+
+
 def conv(out=O, x=A, w=Bp, bias=S, B=1, IC=3, H=8, W=8, OC=4, KH=3, KW=3, sH=1, sW=1, pH=1,
          pW=1, dH=1, dW=1, groups=1):
     return _capi.conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH,
@@ -134,7 +162,7 @@ def test_gemm_plan(lib, monkeypatch):
     # every workload shape is planned without a cross-block K split
     from bias_addmm_im2col_amd import inputs as I
     for c in I.CASES.values():
-        M, N, K = (c.M, c.N, c.K) if c.kind == "addmm" else c.gemm_mnk
+        M, N, K = (c.M, c.N, c.K) if c.kind != "conv" else c.gemm_mnk
         assert baim.gemm_plan(M, N, K)["splits"] <= 2, c.name
     monkeypatch.setenv("BAIM_TILE", "7,3")
     p = baim.gemm_plan(300, 300, 30000)

@@ -412,3 +412,48 @@ def test_regression_fixture_unchanged():
     x, w, bias = (rand32(sh, sd) for sh, sd in zip([(1, 2, 5, 5), (3, 2, 3, 3), (3,)], gc["seeds"]))
     r = oracle.conv2d(x, w, bias, gc["stride"], gc["padding"], gc["dilation"])
     assert r.ref.tolist() == gc["ref"] and r.sabs.tolist() == gc["sabs"]
+
+
+# ------------------------------------------------------------------ linear
+
+def test_linear_matches_exact_rationals():
+    """Tiny linear against exact rational arithmetic."""
+    M, K, N = 3, 6, 4
+    x, w, b = rand32((M, K), 64), rand32((N, K), 65), rand32((N,), 66)
+    r = oracle.linear(x, w, b)
+    for i in range(M):
+        for j in range(N):
+            exact = Fraction(float(b[j])) + sum(Fraction(float(x[i, k])) * Fraction(float(w[j, k]))
+                                                for k in range(K))
+            mag = float(r.sabs[i, j]) + abs(float(b[j]))
+            assert abs(Fraction(r.ref[i, j]) - exact) <= (K + 2) * U64 * mag
+
+
+def test_linear_is_addmm_with_transposed_weight():
+    """linear(x, W, b) == addmm(b, x, W^T) bit for bit (same terms, same order)."""
+    x, w, b = rand32((17, 29), 67), rand32((13, 29), 68), rand32((13,), 69)
+    r = oracle.linear(x, w, b)
+    ra = oracle.addmm(x, np.ascontiguousarray(w.T), b, False, 1.0, 1.0)
+    assert np.array_equal(r.ref, ra.ref) and np.array_equal(r.sabs, ra.sabs)
+    rn = oracle.linear(x, w, None)
+    assert np.array_equal(rn.ref, oracle.addmm(x, np.ascontiguousarray(w.T), b, False, 0.0, 1.0).ref)
+
+
+def test_linear_identity_weight_and_library():
+    x = rand32((9, 12), 70)
+    r = oracle.linear(x, np.eye(12, dtype=np.float32), None)
+    assert np.array_equal(r.ref, x.astype(np.float64))
+    w, b = rand32((7, 12), 71), rand32((7,), 72)
+    t = F.linear(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                 torch.from_numpy(b).double()).numpy()
+    np.testing.assert_allclose(oracle.linear(x, w, b).ref, t, rtol=1e-12, atol=1e-12)
+
+
+def test_sampled_linear_equals_full():
+    x, w, b = rand32((21, 17), 73), rand32((19, 17), 74), rand32((19,), 75)
+    full = oracle.linear(x, w, b)
+    g = np.random.default_rng(2)
+    rows, cols = g.integers(0, 21, 100), g.integers(0, 19, 100)
+    at = oracle.linear_at(x, w, b, rows, cols)
+    assert np.array_equal(at.ref, full.ref[rows, cols])
+    assert np.array_equal(at.selfabs, full.selfabs[rows, cols])

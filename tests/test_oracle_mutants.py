@@ -31,6 +31,8 @@ MUTANTS = {
     "weight_kh_kw_swapped": ("* c->KH + kh) * c->KW + kw]", "* c->KH + kw) * c->KW + kh]"),
     "bias_dropped": ("(bias ? (double)bias[oc] : 0.0)", "0.0"),
     "out_size_off_by_one": ("return span / s + 1;", "return (span + 1) / s + 1;"),
+    "linear_weight_k_misindexed": ("(double)w[n * K + k]", "(double)w[n * K + (K - 1 - k)]"),
+    "linear_bias_dropped": ("*ref = (bias ? (double)bias[n] : 0.0) + acc;", "*ref = acc;"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
 }

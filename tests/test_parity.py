@@ -349,3 +349,74 @@ def test_split_paths_with_unaligned_out(spec, monkeypatch):
     torch.cuda.synchronize()
     assert float(cbuf[0]) == 7.0
     check_close(cout.cpu().numpy(), oracle.conv2d(x, w, bias, 1, 1, 1), 24 * 9, 1.0, f"conv {spec}")
+
+
+# ------------------------------------------------------------------ linear
+# out = x @ weight^T + bias, weight [N,K] (the linear_fp32 form the addmm
+# page shares its GEMM skeleton with).
+
+def run_linear(x, w, b):
+    import bias_addmm_im2col_amd as baim
+    out = baim.linear(dev(x), dev(w), dev(b))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,K,N,has_bias", [
+    (1, 1, 1, True), (3, 5, 7, False), (64, 96, 80, True), (127, 33, 129, True),
+    (129, 31, 257, False), (257, 64, 130, True), (300, 517, 100, True), (37, 1000, 41, False)])
+def test_linear_small_full(M, K, N, has_bias):
+    say(f"linear_f32 M={M} K={K} N={N} bias={has_bias}")
+    x, w = gen((M, K), 80), gen((N, K), 81)
+    b = gen((N,), 82) if has_bias else None
+    check_close(run_linear(x, w, b), oracle.linear(x, w, b), K, 1.0, f"linear {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 96, 80), (129, 257, 131), (256, 1024, 384)])
+def test_linear_integer_bitwise(M, K, N):
+    say(f"linear_f32 integer M={M} K={K} N={N}")
+    x, w, b = gen((M, K), 83, "I"), gen((N, K), 84, "I"), gen((N,), 85, "I")
+    check_bitwise(run_linear(x, w, b), oracle.linear(x, w, b), "linear integer")
+
+
+@pytest.mark.parametrize("spec", TILE_SPECS)
+def test_linear_forced_tile_configs(spec, monkeypatch):
+    monkeypatch.setenv("BAIM_TILE", spec)
+    for M, K, N in [(130, 300, 257), (77, 1000, 65), (33, 45, 70)]:
+        say(f"BAIM_TILE={spec} linear_f32 M={M} K={K} N={N}")
+        x, w, b = gen((M, K), 86), gen((N, K), 87), gen((N,), 88)
+        check_close(run_linear(x, w, b), oracle.linear(x, w, b), K, 1.0, f"linear {spec}")
+    x, w, b = gen((129, 520), 89, "I"), gen((200, 520), 90, "I"), gen((200,), 91, "I")
+    check_bitwise(run_linear(x, w, b), oracle.linear(x, w, b), f"linear integer {spec}")
+
+
+def test_linear_leading_dims_and_unaligned():
+    """x [..., K] is flattened; operands 4 bytes off a 16-byte boundary use
+    the 4-byte-load variant."""
+    import bias_addmm_im2col_amd as baim
+    say("linear_f32 leading dims / unaligned")
+    x, w, b = gen((2, 3, 50, 68), 92), gen((90, 68), 93), gen((90,), 94)
+    out = baim.linear(dev(x), dev(w), dev(b))
+    assert tuple(out.shape) == (2, 3, 50, 90)
+    check_close(out.reshape(-1, 90).cpu().numpy(), oracle.linear(x.reshape(-1, 68), w, b), 68, 1.0,
+                "linear leading dims")
+    xb = torch.empty(300 * 68 + 1, device="cuda")
+    xb[1:] = dev(x).reshape(-1)
+    out = torch.empty(300, 90, device="cuda")
+    baim.linear_f32(out, xb[1:].view(300, 68), dev(w), dev(b))
+    torch.cuda.synchronize()
+    check_close(out.cpu().numpy(), oracle.linear(x.reshape(-1, 68), w, b), 68, 1.0, "linear unaligned")
+
+
+@pytest.mark.parametrize("name", list(I.LINEAR_CASES))
+def test_workload_linear(name):
+    import bias_addmm_im2col_amd as baim
+    c = I.LINEAR_CASES[name]
+    say(f"workload {name}: linear_f32 M={c.M} K={c.K} N={c.N}")
+    x, w, b = I.linear_inputs(c)
+    out = baim.linear(dev(x), dev(w), dev(b))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    rows, cols = addmm_sample(c.M, c.N)
+    ratio = check_close(out[rows, cols], oracle.linear_at(x, w, b, rows, cols), c.K, 1.0, name)
+    say(f"{name}: {rows.size} sampled outputs, max err/tol = {ratio:.3f}")
