@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (datasheet)
+HBM_GBS = 8000.0     # MI355X HBM3E bandwidth (datasheet)
 METRIC = "fp32 TFLOP/s (addmm, im2col conv2d) and % of MI355X fp32 MFMA peak"
 STEP_CASES = ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2",
               "up_proj_4096x1024x4096", "down_proj_4096x4096x1024",
@@ -91,7 +92,7 @@ def load_traffic(kernel: str):
 class Case:
     def __init__(self, name, torch, baim, I):
         self.name = name
-        c = I.CASES[name] if name in I.CASES else I.LINEAR_CASES[name]
+        c = (I.CASES.get(name) or I.LINEAR_CASES.get(name) or I.GROUPED_CASES[name])
         self.c = c
         self.op = c.kind
         self.flops = c.flops
@@ -126,7 +127,10 @@ class Case:
             self.out = torch.empty((c.B, c.OC, OH, OW), dtype=torch.float32, device="cuda")
             self.K = c.IC * c.KH * c.KW
             self.run = lambda: baim.conv2d_gemm_f32(self.out, self.x, self.w, self.bias,
-                                                    c.stride, c.padding, c.dilation, 1)
+                                                    c.stride, c.padding, c.dilation, c.groups)
+            self.bytes = 4 * (x.numel() + w.numel() + bias.numel() + self.out.numel())
+            if c.groups > 1 and not (c.OC // c.groups >= 32 and c.IC // c.groups * c.KH * c.KW >= 32):
+                self.kernel = "baim::conv_direct_kernel"
 
 
 def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
@@ -135,7 +139,7 @@ def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
     first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
     switch to new buffers)."""
     rows = []
-    for name in I.LINEAR_CASES:
+    for name in list(I.LINEAR_CASES) + list(I.GROUPED_CASES):
         cs = Case(name, torch, baim, I)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < warmup_s:
@@ -150,8 +154,14 @@ def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / iters * 1e3
         tf = cs.flops / us / 1e6
-        rows.append({"case": name, "op": "linear", "kernel": cs.kernel, "us": round(us, 2),
-                     "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)})
+        row = {"case": name, "op": cs.op, "kernel": cs.kernel, "us": round(us, 2),
+               "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
+        if cs.kernel == "baim::conv_direct_kernel":
+            # memory-bound: achieved bandwidth on the algorithmic bytes
+            gbs = cs.bytes / us / 1e3
+            row.update({"bound": "hbm", "gbytes_per_s": round(gbs, 1),
+                        "frac_of_hbm": round(gbs / HBM_GBS, 4)})
+        rows.append(row)
     return rows
 
 

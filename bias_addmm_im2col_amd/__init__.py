@@ -10,9 +10,10 @@ arguments and allocates outputs with torch:
 * ``linear(x, weight, bias=None)`` -- ``x @ weight^T + bias`` with weight
   ``[N,K]``, the linear_fp32 form the addmm page shares its GEMM with.
 * ``conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1,
-  groups=1)`` -- groups==1 NCHW convolution as an implicit-im2col GEMM
+  groups=1)`` -- NCHW convolution; groups==1 as an implicit-im2col GEMM
   ("et_vk conv2d: route standard (groups==1) conv through an im2col tiled
-  GEMM", Solution/Implementation).
+  GEMM", Solution/Implementation), grouped convs as one such GEMM per group
+  or, when the groups are small (e.g. depthwise), on a direct kernel.
 
 ``addmm_f32`` and ``conv2d_gemm_f32`` are the same-named entry points of the
 C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
@@ -239,11 +240,8 @@ def conv2d_gemm_f32(out, input, weight, bias=None, stride=1, padding=0, dilation
 
 
 def conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1, groups=1):
-    """groups==1 NCHW conv2d through the implicit-im2col GEMM, new output."""
+    """NCHW conv2d (weight [OC, IC/groups, KH, KW]) as a new output."""
     import torch
-    if int(groups) != 1:
-        raise BaimUnsupportedError(_capi.BAIM_ERR_UNSUPPORTED,
-                                   f"groups={groups}: only groups == 1 is routed through the GEMM")
     x, w = _dev_f32(input, "input"), _dev_f32(weight, "weight")
     if x.dim() != 4 or w.dim() != 4:
         raise ValueError("input and weight must be 4-D")

@@ -202,17 +202,19 @@ baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
   int64_t OH = 0, OW = 0;
   const baim_status hs = baim_conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, &OH, &OW);
   if (hs != BAIM_OK) return hs;  // message already set
-  if (groups != 1)
-    return fail(BAIM_ERR_UNSUPPORTED,
-                "conv2d: groups=%lld is not routed through the im2col GEMM (groups == 1 only)",
-                (long long)groups);
-  const int64_t n_x = elems({B, IC, H, W}), n_w = elems({OC, IC, KH, KW});
-  const int64_t n_out = elems({B, OC, OH, OW}), K = elems({IC, KH, KW});
+  if (IC % groups != 0 || OC % groups != 0)
+    return fail(BAIM_ERR_SHAPE, "conv2d: groups=%lld must divide IC=%lld and OC=%lld",
+                (long long)groups, (long long)IC, (long long)OC);
+  const int64_t icg = IC / groups;
+  const int64_t n_x = elems({B, IC, H, W}), n_w = elems({OC, icg, KH, KW});
+  const int64_t n_out = elems({B, OC, OH, OW}), K = elems({icg, KH, KW});
   if (n_x < 0 || n_w < 0 || n_out < 0 || n_x >= kMaxElems || n_w >= kMaxElems ||
       n_out >= kMaxElems)
     return fail(BAIM_ERR_TOO_LARGE, "conv2d: every tensor must have fewer than 2^31 elements");
   if (n_x >= kMaxConvInput) return fail(BAIM_ERR_TOO_LARGE, "conv2d: input must have fewer than 2^29 elements");
-  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d: IC*KH*KW must be below 2^21");
+  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d: (IC/groups)*KH*KW must be below 2^21");
+  if (groups > 65535 || OC > 65535 || B > 65535)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d: groups, OC and B must be at most 65535");
   // In-kernel tap offsets (ih*W + iw over the padded plane) are 32-bit.
   const int64_t n_pad = elems({H + 2 * pH, W + 2 * pW});
   if (n_pad < 0 || n_pad >= kMaxElems)
@@ -242,6 +244,9 @@ baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
   q.dW = (int)dW;
   q.OH = (int)OH;
   q.OW = (int)OW;
+  q.groups = (int)groups;
+  if (!baim::conv_uses_gemm(q))
+    return launched(baim::launch_conv2d_direct(q, (hipStream_t)stream), "conv2d_gemm_f32");
   return launched(baim::launch_conv2d(q, (hipStream_t)stream), "conv2d_gemm_f32");
 }
 

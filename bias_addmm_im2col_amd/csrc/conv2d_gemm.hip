@@ -25,8 +25,9 @@ struct ConvArgs {
   const float* w;
   const float* bias;
   int IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
-  int M, N, K;
+  int M, N, K;  // per group: OC/G, B*OH*OW, (IC/G)*KH*KW
   int x_elems;  // B*IC*H*W
+  int groups, ICg, OCg;  // groups, channels per group
   FastDiv div_khw, div_kw, div_p, div_ow;
   Sched sched;
 };
@@ -61,7 +62,7 @@ struct ImColTileLoader {
   int q0, col, cbase, ih0, iw0;
   f32x4 reg[2][NQ];  // two register slots (prefetch depth up to 2)
 
-  __device__ void init(const ConvArgs& args, int n0, int4* table) {
+  __device__ void init(const ConvArgs& args, int n0, int4* table, int g) {
     a = &args;
     tbl = table;
     col = threadIdx.x % T::BN;
@@ -75,7 +76,8 @@ struct ImColTileLoader {
     const uint32_t ow = pix - oh * args.div_ow.d;
     ih0 = (int)oh * args.sH - args.pH;
     iw0 = cok ? (int)ow * args.sW - args.pW : -(args.dW * (args.KW - 1)) - 1;
-    cbase = (int)b * args.IC * args.H * args.W + ih0 * args.W + iw0;
+    // image b, first input channel of group g
+    cbase = ((int)b * args.IC + g * args.ICg) * args.H * args.W + ih0 * args.W + iw0;
   }
   __device__ void meta(int t) {
     if (threadIdx.x < T::BK) {
@@ -127,15 +129,18 @@ struct ImColTileLoader {
   }
 };
 
+// A grouped conv runs one GEMM per group g = blockIdx.y: rows m of the
+// group's weight slice, input channels g*IC/G.., output channels g*OC/G...
 template <class T, int VA>
 __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m0, int n0, int tb, int te,
                                   int epi) {
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
+  const int g = blockIdx.y;
   RowTileLoader<T, VA> al;
-  al.init(p.w, m0, p.M, p.K);
+  al.init(p.w + (size_t)g * p.OCg * p.K, m0, p.M, p.K);
   ImColTileLoader<T> bl;
-  bl.init(p, n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE));
+  bl.init(p, n0, reinterpret_cast<int4*>(smem + 2 * T::STAGE), g);
   Accum<T> acc;
   mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
@@ -167,7 +172,7 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
           other[i][j][r] = kPieceSentinel;
           if (n < p.N && oc < p.M)
             other[i][j][r] = atomicExch(
-                reinterpret_cast<unsigned int*>(&p.out[obase[j] + (size_t)oc * P]),
+                reinterpret_cast<unsigned int*>(&p.out[obase[j] + (size_t)(g * p.OCg + oc) * P]),
                 __float_as_uint(acc.c[i][j][r]));
         }
 #pragma unroll
@@ -178,8 +183,9 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
         for (int r = 0; r < 16; ++r) {
           const int n = n0 + ws.wn0 + 32 * j + c, oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
           if (n >= p.N || oc >= p.M || other[i][j][r] == kPieceSentinel) continue;
+          const int ocx = g * p.OCg + oc;
           const float v = __uint_as_float(other[i][j][r]) + acc.c[i][j][r];
-          p.out[obase[j] + (size_t)oc * P] = v + (p.bias ? p.bias[oc] : 0.0f);
+          p.out[obase[j] + (size_t)ocx * P] = v + (p.bias ? p.bias[ocx] : 0.0f);
         }
     return;
   }
@@ -193,11 +199,12 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
       for (int r = 0; r < 16; ++r) {
         const int oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
         if (oc >= p.M) continue;
-        float* o = &p.out[obase[j] + (size_t)oc * P];
+        const int ocx = g * p.OCg + oc;
+        float* o = &p.out[obase[j] + (size_t)ocx * P];
         if (epi == EPI_ATOMIC)
           unsafeAtomicAdd(o, acc.c[i][j][r]);
         else
-          *o = acc.c[i][j][r] + (p.bias ? p.bias[oc] : 0.0f);
+          *o = acc.c[i][j][r] + (p.bias ? p.bias[ocx] : 0.0f);
       }
   }
 }
@@ -258,7 +265,8 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
 
 template <class T, int VA, int MODE>
 static hipError_t launch_t(const ConvArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA, MODE>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((conv2d_gemm_kernel<T, VA, MODE>), dim3(nblocks, a.groups), dim3(T::NT), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -318,9 +326,12 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.dW = q.dW;
   a.OH = q.OH;
   a.OW = q.OW;
-  a.M = q.OC;
+  a.groups = q.groups;
+  a.ICg = q.IC / q.groups;
+  a.OCg = q.OC / q.groups;
+  a.M = a.OCg;
   a.N = q.B * q.OH * q.OW;
-  a.K = q.IC * q.KH * q.KW;
+  a.K = a.ICg * q.KH * q.KW;
   a.x_elems = q.B * q.IC * q.H * q.W;
   a.div_khw = make_fastdiv((uint32_t)(q.KH * q.KW));
   a.div_kw = make_fastdiv((uint32_t)q.KW);
@@ -332,7 +343,7 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.sched = Sched{plan.tiles_m, plan.tiles_n, 8, plan.nkt, plan.splits, plan.kt_per_split};
   const int nblocks = (int)plan_blocks(plan);
   if (plan_needs_init(plan)) {
-    const uint32_t total = (uint32_t)a.M * (uint32_t)a.N;
+    const uint32_t total = (uint32_t)q.OC * (uint32_t)a.N;
     const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
     hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias,
                        plan_uses_exchange(plan) ? 1 : 0, total, a.div_p, (uint32_t)q.OC);

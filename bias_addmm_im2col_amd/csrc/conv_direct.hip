@@ -1,0 +1,153 @@
+// conv_direct.hip -- grouped / depthwise NCHW conv whose per-group GEMM is
+// too small for the matrix cores (fewer than 32 output channels or 32 taps
+// per group, e.g. depthwise), computed directly: one thread per output
+// element, summing the IC/G input channels of its group over the
+// (kh, kw) taps.  The conv page keeps grouped and depthwise convs on
+// direct kernels ("et_vk conv2d: route standard (groups==1) conv through
+// an im2col tiled GEMM", Solution paragraph); this is that path on gfx950.
+//
+// Memory-bound.  The main kernel gives a block a 32-row x 64-column tile of
+// one (image, output channel) plane: for each input channel of the group it
+// stages the input rows and columns the tile's taps touch (with the halo,
+// zero-filled outside the input) in LDS with coalesced loads all in flight
+// at once, then each thread sums its outputs' taps from LDS; the weights
+// are uniform across the block (scalar loads).  Tiles whose input window
+// would exceed 64 KB of LDS (large strides or dilations) use a plain kernel
+// that reads the input directly.  The fp32 sum runs in (ic, kh, kw) order
+// with fused multiply-adds in both.
+#include <hip/hip_runtime.h>
+
+#include "index_math.hpp"
+#include "launch.hpp"
+
+namespace baim {
+
+struct ConvDirectArgs {
+  float* out;
+  const float* x;
+  const float* w;
+  const float* bias;
+  int IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
+  int ICg, OCg;
+  FastDiv div_ow;
+};
+
+constexpr int kTileW = 64, kTileH = 32;  // outputs per block tile (8 per thread)
+constexpr int kMaxWindow = 16384;        // floats of LDS for the input window
+
+__global__ __launch_bounds__(256) void conv_direct_tiled_kernel(ConvDirectArgs p, int tiles_w,
+                                                                int win_h, int win_w) {
+  extern __shared__ float win[];  // win_h x win_w floats
+  const int oc = blockIdx.y, b = blockIdx.z;
+  const int th = blockIdx.x / tiles_w, tw = blockIdx.x - th * tiles_w;
+  const int oy0 = th * kTileH, ox0 = tw * kTileW;
+  const int iy0 = oy0 * p.sH - p.pH, ix0 = ox0 * p.sW - p.pW;  // window origin
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;         // column, row group
+  const int g = oc / p.OCg;
+  const float* xg = p.x + ((size_t)b * p.IC + (size_t)g * p.ICg) * p.H * p.W;
+  const float* wo = p.w + (size_t)oc * p.ICg * p.KH * p.KW;
+  float acc[kTileH / 4] = {};
+  for (int icl = 0; icl < p.ICg; ++icl) {
+    const float* xc = xg + (size_t)icl * p.H * p.W;
+    for (int wy = ty; wy < win_h; wy += 4) {
+      const int iy = iy0 + wy;
+      const bool yok = (unsigned)iy < (unsigned)p.H;
+      for (int wx = tx; wx < win_w; wx += 64) {
+        const int ix = ix0 + wx;
+        win[wy * win_w + wx] = (yok && (unsigned)ix < (unsigned)p.W) ? xc[iy * p.W + ix] : 0.0f;
+      }
+    }
+    __syncthreads();
+    // tap-major: one weight load per tap feeds the thread's 8 outputs
+    // (rows ty, ty+4, ..., ty+28 of the tile), independent FMAs
+    const float* wc = wo + icl * p.KH * p.KW;
+    const float* base = win + (ty * p.sH) * win_w + tx * p.sW;
+    const int rstep = 4 * p.sH * win_w;
+    for (int kh = 0; kh < p.KH; ++kh)
+      for (int kw = 0; kw < p.KW; ++kw) {
+        const float wv = wc[kh * p.KW + kw];
+        const float* r = base + kh * p.dH * win_w + kw * p.dW;
+#pragma unroll
+        for (int i = 0; i < kTileH / 4; ++i) acc[i] = fmaf(wv, r[i * rstep], acc[i]);
+      }
+    __syncthreads();
+  }
+  const int P = p.OH * p.OW;
+  const float bv = p.bias ? p.bias[oc] : 0.0f;
+  float* o = p.out + ((size_t)b * p.OC + oc) * P;
+  const int ox = ox0 + tx;
+#pragma unroll
+  for (int i = 0; i < kTileH / 4; ++i) {
+    const int oy = oy0 + ty + 4 * i;
+    if (ox < p.OW && oy < p.OH) o[oy * p.OW + ox] = acc[i] + bv;
+  }
+}
+
+__global__ __launch_bounds__(256) void conv_direct_kernel(ConvDirectArgs p) {
+  const int P = p.OH * p.OW;
+  const int pix = blockIdx.x * 256 + threadIdx.x;
+  const int oc = blockIdx.y, b = blockIdx.z;
+  if (pix >= P) return;
+  const int oh = (int)fdiv((uint32_t)pix, p.div_ow);
+  const int ow = pix - oh * p.OW;
+  const int g = oc / p.OCg;
+  const int ih0 = oh * p.sH - p.pH, iw0 = ow * p.sW - p.pW;
+  const float* xg = p.x + ((size_t)b * p.IC + (size_t)g * p.ICg) * p.H * p.W;
+  const float* wo = p.w + (size_t)oc * p.ICg * p.KH * p.KW;
+  float acc = 0.0f;
+  for (int icl = 0; icl < p.ICg; ++icl) {
+    const float* xc = xg + (size_t)icl * p.H * p.W;
+    const float* wc = wo + icl * p.KH * p.KW;
+    for (int kh = 0; kh < p.KH; ++kh) {
+      const int ih = ih0 + kh * p.dH;
+      if ((unsigned)ih >= (unsigned)p.H) continue;
+      for (int kw = 0; kw < p.KW; ++kw) {
+        const int iw = iw0 + kw * p.dW;
+        if ((unsigned)iw >= (unsigned)p.W) continue;
+        acc = fmaf(wc[kh * p.KW + kw], xc[ih * p.W + iw], acc);
+      }
+    }
+  }
+  p.out[((size_t)b * p.OC + oc) * P + pix] = acc + (p.bias ? p.bias[oc] : 0.0f);
+}
+
+hipError_t launch_conv2d_direct(const ConvProblem& q, hipStream_t stream) {
+  ConvDirectArgs a;
+  a.out = q.out;
+  a.x = q.x;
+  a.w = q.w;
+  a.bias = q.bias;
+  a.IC = q.IC;
+  a.H = q.H;
+  a.W = q.W;
+  a.OC = q.OC;
+  a.KH = q.KH;
+  a.KW = q.KW;
+  a.sH = q.sH;
+  a.sW = q.sW;
+  a.pH = q.pH;
+  a.pW = q.pW;
+  a.dH = q.dH;
+  a.dW = q.dW;
+  a.OH = q.OH;
+  a.OW = q.OW;
+  a.ICg = q.IC / q.groups;
+  a.OCg = q.OC / q.groups;
+  a.div_ow = make_fastdiv((uint32_t)q.OW);
+  // input window of one output tile: rows / columns its taps touch
+  const int64_t win_h = (int64_t)(kTileH - 1) * q.sH + (int64_t)(q.KH - 1) * q.dH + 1;
+  const int64_t win_w = (int64_t)(kTileW - 1) * q.sW + (int64_t)(q.KW - 1) * q.dW + 1;
+  if (win_h * win_w <= kMaxWindow) {
+    const int tiles_w = (q.OW + kTileW - 1) / kTileW, tiles_h = (q.OH + kTileH - 1) / kTileH;
+    hipLaunchKernelGGL(conv_direct_tiled_kernel, dim3(tiles_w * tiles_h, q.OC, q.B), dim3(256),
+                       (size_t)(win_h * win_w) * sizeof(float), stream, a, tiles_w, (int)win_h,
+                       (int)win_w);
+    return hipGetLastError();
+  }
+  const int P = q.OH * q.OW;
+  hipLaunchKernelGGL(conv_direct_kernel, dim3((P + 255) / 256, q.OC, q.B), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace baim

@@ -24,9 +24,18 @@ struct ConvProblem {
   const float* w;
   const float* bias;  // may be NULL
   int B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
+  int groups;  // >= 1, dividing IC and OC; weight is [OC, IC/groups, KH, KW]
 };
+
+// Whether a grouped conv runs as one implicit-im2col GEMM per group (true)
+// or on the direct kernel (per-group GEMMs too small for the matrix cores).
+inline bool conv_uses_gemm(const ConvProblem& q) {
+  const int icg = q.IC / q.groups, ocg = q.OC / q.groups;
+  return q.groups == 1 || (ocg >= 32 && icg * q.KH * q.KW >= 32);
+}
 
 hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
+hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 
 }  // namespace baim

@@ -55,6 +55,7 @@ class ConvCase:
     w: tuple
     bias: tuple | None
     seed: int = 0
+    groups: int = 1
     kind: str = field(default="conv", init=False)
 
     def out_hw(self):
@@ -66,13 +67,15 @@ class ConvCase:
 
     @property
     def gemm_mnk(self):
+        """Per-group GEMM: (OC/G, B*OH*OW, (IC/G)*KH*KW)."""
         OH, OW = self.out_hw()
-        return self.OC, self.B * OH * OW, self.IC * self.KH * self.KW
+        return (self.OC // self.groups, self.B * OH * OW,
+                self.IC // self.groups * self.KH * self.KW)
 
     @property
     def flops(self) -> int:
         M, N, K = self.gemm_mnk
-        return 2 * M * N * K
+        return 2 * M * N * K * self.groups
 
 
 @dataclass(frozen=True)
@@ -128,6 +131,15 @@ LINEAR_CASES = {c.name: c for c in [
     LinearCase("linear_ragged_577x1024x4096_nobias", 577, 1024, 4096, N(1), N(0.02), None),
 ]}
 
+# Grouped convs on the 3x3 mid-stage shape: 8 groups of 32 channels (one
+# GEMM per group) and depthwise (the direct kernel).
+GROUPED_CASES = {c.name: c for c in [
+    ConvCase("conv3x3_56_g8", 4, 256, 56, 56, 256, 3, 3, (1, 1), (1, 1), (1, 1),
+             N(1), N(0.05), N(0.02), groups=8),
+    ConvCase("dwconv3x3_56", 4, 256, 56, 56, 256, 3, 3, (1, 1), (1, 1), (1, 1),
+             N(1), N(0.2), N(0.02), groups=256),
+]}
+
 # Groups of cases as the workload list states them (small / FFN / stem /
 # 3x3 mid-stage / large and ragged projections).
 GROUPS = {
@@ -167,7 +179,7 @@ def conv_inputs(case: ConvCase):
     """(input [B,IC,H,W], weight [OC,IC,KH,KW], bias [OC] or None)."""
     g = torch.Generator("cpu").manual_seed(case.seed)
     x = draw((case.B, case.IC, case.H, case.W), case.x, g)
-    w = draw((case.OC, case.IC, case.KH, case.KW), case.w, g)
+    w = draw((case.OC, case.IC // case.groups, case.KH, case.KW), case.w, g)
     b = None if case.bias is None else draw((case.OC,), case.bias, g)
     return x, w, b
 

@@ -38,7 +38,7 @@ typedef enum {
   BAIM_OK = 0,
   BAIM_ERR_NULL = 1,        /* a required pointer is NULL                    */
   BAIM_ERR_SHAPE = 2,       /* a size/stride/flag is out of its domain       */
-  BAIM_ERR_UNSUPPORTED = 3, /* valid conv, but not one this path computes    */
+  BAIM_ERR_UNSUPPORTED = 3, /* valid call this library does not compute      */
   BAIM_ERR_TOO_LARGE = 4,   /* a tensor has 2^31 or more elements            */
   BAIM_ERR_ALIAS = 5,       /* out overlaps an input                         */
   BAIM_ERR_LAUNCH = 6       /* the HIP launch itself failed                  */
@@ -90,28 +90,36 @@ baim_status linear_f32(float* out, const float* x, const float* weight,
                        void* stream);
 
 /*
- * conv2d_gemm_f32: out = conv2d(input, weight, bias) for groups == 1,
- * computed as the GEMM  out[oc, n] = sum_kk weight[oc, kk] * col[kk, n]
- * + bias[oc], with M = OC, N = B*OH*OW, K = IC*KH*KW and col the implicit
- * im2col of the input (never materialised).
+ * conv2d_gemm_f32: out = conv2d(input, weight, bias), NCHW, with `groups`.
+ *
+ * groups == 1 is computed as the GEMM  out[oc, n] = sum_kk weight[oc, kk] *
+ * col[kk, n] + bias[oc], with M = OC, N = B*OH*OW, K = IC*KH*KW and col the
+ * implicit im2col of the input (never materialised).
  *
  * Defined by "et_vk conv2d: route standard (groups==1) conv through an
  * im2col tiled GEMM" (PR #20873), Solution and Implementation paragraphs:
  * n decodes to (b, oh, ow) and kk to (ic, kh, kw); the input is sampled at
  * ih = oh*sH - pH + kh*dH, iw = ow*sW - pW + kw*dW, and a tap outside the
  * input reads 0 (zero padding); bias is added per output channel; the
- * output is NCHW.  Grouped, depthwise and transposed convolutions are not
- * routed through this GEMM (the page keeps them on other kernels), so
- * groups != 1 returns BAIM_ERR_UNSUPPORTED.
+ * output is NCHW.
+ *
+ * groups > 1 (the page keeps grouped and depthwise convs on its direct
+ * kernels): output channel oc of group g = oc / (OC/groups) sums over the
+ * input channels g*IC/groups .. (g+1)*IC/groups - 1 only.  When a group has
+ * at least 32 output channels and 32 taps ((IC/groups)*KH*KW) it runs as
+ * one implicit-im2col GEMM per group; otherwise (e.g. depthwise) on a
+ * direct kernel, one thread per output.
  *
  *  out     [B,OC,OH,OW] fp32 NCHW, written in full; OH, OW as given by
  *          baim_conv2d_out_hw().
  *  input   [B,IC,H,W] fp32 NCHW.
- *  weight  [OC,IC,KH,KW] fp32 (read as the row-major [OC, IC*KH*KW] matrix).
+ *  weight  [OC,IC/groups,KH,KW] fp32 (per group, the row-major
+ *          [OC/groups, (IC/groups)*KH*KW] matrix).
  *  bias    [OC] fp32, or NULL for no bias.
  *  sizes   B, IC, H, W, OC, KH, KW >= 1; strides sH, sW >= 1;
  *          paddings pH, pW >= 0; dilations dH, dW >= 1; OH, OW >= 1.
- *  groups  must be 1.
+ *  groups  >= 1 and dividing IC and OC (else BAIM_ERR_SHAPE); groups, OC
+ *          and B at most 65535.
  *  stream  hipStream_t or NULL.
  */
 baim_status conv2d_gemm_f32(float* out, const float* input,

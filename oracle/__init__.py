@@ -82,6 +82,10 @@ def _load():
     lib.oracle_conv2d.restype = ctypes.c_int
     lib.oracle_conv2d_at.argtypes = [_i64] * 13 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
     lib.oracle_conv2d_at.restype = ctypes.c_int
+    lib.oracle_conv2d_grouped.argtypes = [_i64] * 14 + [_fp, _fp, _fp, _dp, _dp]
+    lib.oracle_conv2d_grouped.restype = ctypes.c_int
+    lib.oracle_conv2d_grouped_at.argtypes = [_i64] * 14 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
+    lib.oracle_conv2d_grouped_at.restype = ctypes.c_int
     lib.oracle_im2col.argtypes = [_i64] * 12 + [_fp, _dp]
     lib.oracle_im2col.restype = ctypes.c_int
     _lib = lib
@@ -195,10 +199,10 @@ def conv_out_size(size, k, stride, pad, dil) -> int:
     return int(_load().oracle_conv_out_size(size, k, stride, pad, dil))
 
 
-def _conv_args(x, w, stride, padding, dilation):
+def _conv_args(x, w, stride, padding, dilation, groups=1):
     B, IC, H, W = x.shape
     OC, IC2, KH, KW = w.shape
-    assert IC == IC2, "groups == 1 only"
+    assert IC == IC2 * groups, "weight must be [OC, IC/groups, KH, KW]"
     (sH, sW), (pH, pW), (dH, dW) = _pair(stride), _pair(padding), _pair(dilation)
     return (B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW)
 
@@ -235,6 +239,44 @@ def conv2d_at(x, w, bias, stride, padding, dilation, idx) -> Result:
     sabs = np.empty(n, np.float64)
     rc = _load().oracle_conv2d_at(*a, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp), n,
                                   _ptr(idx, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    oc = (idx // (OH * OW)) % OC
+    bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])
+    return Result(ref, sabs, bb)
+
+
+def conv2d_grouped(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1) -> Result:
+    """Full NCHW reference of the grouped direct conv plus bias[oc]."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _conv_args(x, w, stride, padding, dilation, groups)
+    B, OC = a[0], a[4]
+    OH = conv_out_size(a[2], a[5], a[7], a[9], a[11])
+    OW = conv_out_size(a[3], a[6], a[8], a[10], a[12])
+    if OH <= 0 or OW <= 0:
+        raise ValueError("empty conv output")
+    ref = np.empty((B, OC, OH, OW), np.float64)
+    sabs = np.empty((B, OC, OH, OW), np.float64)
+    rc = _load().oracle_conv2d_grouped(*a, groups, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp),
+                                       _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    bb = np.zeros(OC) if bias is None else np.abs(bias.astype(np.float64))
+    return Result(ref, sabs, np.broadcast_to(bb[None, :, None, None], ref.shape))
+
+
+def conv2d_grouped_at(x, w, bias, stride, padding, dilation, groups, idx) -> Result:
+    """Grouped conv reference at sampled flat NCHW output indices."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _conv_args(x, w, stride, padding, dilation, groups)
+    B, OC = a[0], a[4]
+    OH = conv_out_size(a[2], a[5], a[7], a[9], a[11])
+    OW = conv_out_size(a[3], a[6], a[8], a[10], a[12])
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert (idx >= 0).all() and (idx < B * OC * OH * OW).all()
+    n = idx.size
+    ref = np.empty(n, np.float64)
+    sabs = np.empty(n, np.float64)
+    rc = _load().oracle_conv2d_grouped_at(*a, groups, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp),
+                                          n, _ptr(idx, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
     assert rc == 0
     oc = (idx // (OH * OW)) % OC
     bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])

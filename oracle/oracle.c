@@ -16,6 +16,10 @@
  *  - the same page, Implementation paragraph: the addmm kernel shares its
  *    tiled-GEMM skeleton with linear_fp32, which reads a transposed [N,K]
  *    weight: linear computes out[m,n] = sum_k x[m,k] * weight[n,k] + bias[n].
+ *  - grouped conv (the same conv page keeps grouped and depthwise convs on
+ *    its direct kernels): with G groups, output channel oc belongs to
+ *    group g = oc / (OC/G) and sums over input channels
+ *    g*(IC/G) .. (g+1)*(IC/G)-1 only; the weight is [OC, IC/G, KH, KW].
  *  - "et_vk conv2d: route standard (groups==1) conv through an im2col tiled
  *    GEMM" (pytorch/executorch PR #20873), Solution and Implementation
  *    paragraphs: groups==1 conv is a GEMM with M=OC, N=B*OH*OW, K=IC*KH*KW;
@@ -214,6 +218,71 @@ int oracle_conv2d_at(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
     int64_t oc = (o / (c.OW * c.OH)) % OC, b = o / (c.OW * c.OH * OC);
     conv_one(&c, b, oc, oh, ow, x, w, bias, &ref[s], &sabs[s]);
   }
+  return 0;
+}
+
+/* One grouped-conv output element out[b, oc, oh, ow]: the direct sum over
+ * the IC/G input channels of oc's group and the (kh, kw) taps. */
+static void conv_one_grouped(const conv_shape* c, int64_t G, int64_t b,
+                             int64_t oc, int64_t oh, int64_t ow,
+                             const float* x, const float* w,
+                             const float* bias, double* ref, double* sabs) {
+  const int64_t icg = c->IC / G, ocg = c->OC / G, g = oc / ocg;
+  double acc = 0.0, aabs = 0.0;
+  for (int64_t icl = 0; icl < icg; ++icl)
+    for (int64_t kh = 0; kh < c->KH; ++kh)
+      for (int64_t kw = 0; kw < c->KW; ++kw) {
+        int64_t ih = oh * c->sH - c->pH + kh * c->dH;
+        int64_t iw = ow * c->sW - c->pW + kw * c->dW;
+        if (ih < 0 || ih >= c->H || iw < 0 || iw >= c->W) continue;
+        int64_t ic = g * icg + icl;
+        double xv = (double)x[((b * c->IC + ic) * c->H + ih) * c->W + iw];
+        double wv = (double)w[((oc * icg + icl) * c->KH + kh) * c->KW + kw];
+        acc += wv * xv;
+        aabs += fabs(wv * xv);
+      }
+  *ref = (bias ? (double)bias[oc] : 0.0) + acc;
+  *sabs = aabs;
+}
+
+/* Grouped direct conv at n sampled flat NCHW output indices.  Returns -1 if
+ * the output is empty or G does not divide IC and OC. */
+int oracle_conv2d_grouped_at(int64_t B, int64_t IC, int64_t H, int64_t W,
+                             int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                             int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                             int64_t dW, int64_t G, const float* x,
+                             const float* w, const float* bias, int64_t n,
+                             const int64_t* idx, double* ref, double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0 || G < 1 || IC % G || OC % G) return -1;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < n; ++s) {
+    int64_t o = idx[s];
+    int64_t ow = o % c.OW, oh = (o / c.OW) % c.OH;
+    int64_t oc = (o / (c.OW * c.OH)) % OC, b = o / (c.OW * c.OH * OC);
+    conv_one_grouped(&c, G, b, oc, oh, ow, x, w, bias, &ref[s], &sabs[s]);
+  }
+  return 0;
+}
+
+/* Full grouped direct conv: ref and sabs are [B, OC, OH, OW] doubles. */
+int oracle_conv2d_grouped(int64_t B, int64_t IC, int64_t H, int64_t W,
+                          int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                          int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                          int64_t dW, int64_t G, const float* x,
+                          const float* w, const float* bias, double* ref,
+                          double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0 || G < 1 || IC % G || OC % G) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t oc = 0; oc < OC; ++oc)
+      for (int64_t oh = 0; oh < c.OH; ++oh)
+        for (int64_t ow = 0; ow < c.OW; ++ow) {
+          int64_t o = ((b * OC + oc) * c.OH + oh) * c.OW + ow;
+          conv_one_grouped(&c, G, b, oc, oh, ow, x, w, bias, &ref[o],
+                           &sabs[o]);
+        }
   return 0;
 }
 

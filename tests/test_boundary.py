@@ -128,7 +128,10 @@ def conv(out=O, x=A, w=Bp, bias=S, B=1, IC=3, H=8, W=8, OC=4, KH=3, KW=3, sH=1, 
     (dict(H=2, KH=5, pH=0), _capi.BAIM_ERR_SHAPE),      # kernel larger than input
     (dict(H=5, KH=3, dH=3, pH=0), _capi.BAIM_ERR_SHAPE),  # dilated kernel too large
     (dict(groups=0), _capi.BAIM_ERR_SHAPE),
-    (dict(groups=3), _capi.BAIM_ERR_UNSUPPORTED),
+    (dict(groups=3), _capi.BAIM_ERR_SHAPE),          # 3 does not divide OC = 4
+    (dict(groups=2, IC=3, OC=4), _capi.BAIM_ERR_SHAPE),  # 2 does not divide IC = 3
+    (dict(groups=70000, IC=70000, OC=70000, KH=1, KW=1, pH=0, pW=0, H=1, W=1),
+     _capi.BAIM_ERR_TOO_LARGE),
     (dict(out=None), _capi.BAIM_ERR_NULL),
     (dict(x=None), _capi.BAIM_ERR_NULL),
     (dict(w=None), _capi.BAIM_ERR_NULL),
@@ -184,5 +187,5 @@ def test_python_layer_checks_before_the_library():
         baim.addmm(torch.zeros(3), torch.zeros(2, 3, dtype=torch.float64), torch.zeros(3, 3))
     with pytest.raises(ValueError):
         baim.addmm(torch.zeros(3), torch.zeros(2, 3), torch.zeros(3, 3))  # CPU tensors
-    with pytest.raises(NotImplementedError):
+    with pytest.raises(ValueError):  # CPU tensors
         baim.conv2d(torch.zeros(1, 4, 5, 5), torch.zeros(4, 2, 3, 3), groups=2)

@@ -457,3 +457,57 @@ def test_sampled_linear_equals_full():
     at = oracle.linear_at(x, w, b, rows, cols)
     assert np.array_equal(at.ref, full.ref[rows, cols])
     assert np.array_equal(at.selfabs, full.selfabs[rows, cols])
+
+
+# ------------------------------------------------------------ grouped conv
+
+def test_grouped_conv_with_one_group_is_the_conv():
+    x, w, b = rand32((2, 6, 9, 8), 76), rand32((5, 6, 3, 2), 77), rand32((5,), 78)
+    r1 = oracle.conv2d(x, w, b, (2, 1), (1, 0), (1, 2))
+    rg = oracle.conv2d_grouped(x, w, b, (2, 1), (1, 0), (1, 2), groups=1)
+    assert np.array_equal(r1.ref, rg.ref) and np.array_equal(r1.sabs, rg.sabs)
+
+
+def test_grouped_conv_is_per_group_convs():
+    """Closed form: group g's outputs are the ungrouped conv of its channel
+    slice of the input with its slice of the weight."""
+    G, B, IC, OC, H, W = 3, 2, 6, 9, 10, 7
+    x, w, b = rand32((B, IC, H, W), 79), rand32((OC, IC // G, 3, 3), 80), rand32((OC,), 81)
+    r = oracle.conv2d_grouped(x, w, b, 1, 1, 1, groups=G)
+    icg, ocg = IC // G, OC // G
+    for g in range(G):
+        rg = oracle.conv2d(np.ascontiguousarray(x[:, g * icg:(g + 1) * icg]),
+                           np.ascontiguousarray(w[g * ocg:(g + 1) * ocg]),
+                           np.ascontiguousarray(b[g * ocg:(g + 1) * ocg]), 1, 1, 1)
+        assert np.array_equal(r.ref[:, g * ocg:(g + 1) * ocg], rg.ref)
+
+
+@pytest.mark.parametrize("G,IC,OC,stride,pad,dil", [(2, 4, 6, 1, 1, 1), (4, 8, 8, 2, 1, 1),
+                                                    (8, 8, 16, 1, 2, 2), (3, 3, 3, (2, 1), (0, 1), 1)])
+def test_grouped_conv_vs_torch_float64(G, IC, OC, stride, pad, dil):
+    x, w, b = rand32((2, IC, 11, 9), 82), rand32((OC, IC // G, 3, 3), 83), rand32((OC,), 84)
+    r = oracle.conv2d_grouped(x, w, b, stride, pad, dil, groups=G)
+    t = F.conv2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                 torch.from_numpy(b).double(), stride, pad, dil, G).numpy()
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+
+
+def test_depthwise_delta_kernel_shifts_each_channel():
+    """Depthwise (G = IC = OC), each channel's kernel a delta at (2, 0): the
+    output is the input shifted by (2 - 1, 0 - 1) with zero fill."""
+    C = 5
+    x = rand32((1, C, 7, 6), 85)
+    w = np.zeros((C, 1, 3, 3), np.float32)
+    w[:, 0, 2, 0] = 1.0
+    r = oracle.conv2d_grouped(x, w, None, 1, 1, 1, groups=C)
+    expect = np.zeros((1, C, 7, 6))
+    expect[:, :, 0:6, 1:6] = x[:, :, 1:7, 0:5]
+    assert np.array_equal(r.ref, expect)
+
+
+def test_sampled_grouped_conv_equals_full():
+    x, w, b = rand32((2, 6, 9, 8), 86), rand32((9, 2, 3, 3), 87), rand32((9,), 88)
+    full = oracle.conv2d_grouped(x, w, b, (2, 1), 1, (1, 2), groups=3)
+    idx = np.random.default_rng(3).integers(0, full.ref.size, 150)
+    at = oracle.conv2d_grouped_at(x, w, b, (2, 1), 1, (1, 2), 3, idx)
+    assert np.array_equal(at.ref, full.ref.reshape(-1)[idx])

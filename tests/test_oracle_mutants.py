@@ -33,6 +33,8 @@ MUTANTS = {
     "out_size_off_by_one": ("return span / s + 1;", "return (span + 1) / s + 1;"),
     "linear_weight_k_misindexed": ("(double)w[n * K + k]", "(double)w[n * K + (K - 1 - k)]"),
     "linear_bias_dropped": ("*ref = (bias ? (double)bias[n] : 0.0) + acc;", "*ref = acc;"),
+    "grouped_input_channel_ignores_group": ("int64_t ic = g * icg + icl;", "int64_t ic = icl;"),
+    "grouped_weight_index": ("w[((oc * icg + icl) * c->KH", "w[((oc * icg + (icg - 1 - icl)) * c->KH"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
 }

@@ -420,3 +420,72 @@ def test_workload_linear(name):
     rows, cols = addmm_sample(c.M, c.N)
     ratio = check_close(out[rows, cols], oracle.linear_at(x, w, b, rows, cols), c.K, 1.0, name)
     say(f"{name}: {rows.size} sampled outputs, max err/tol = {ratio:.3f}")
+
+
+# ------------------------------------------------------------ grouped conv
+# Per-group GEMM when a group has >= 32 output channels and >= 32 taps,
+# else the direct kernel (depthwise and other small groups).
+
+def run_gconv(x, w, bias, stride, pad, dil, groups):
+    import bias_addmm_im2col_amd as baim
+    out = baim.conv2d(dev(x), dev(w), dev(bias), stride, pad, dil, groups)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+GCONV_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, dil, groups, bias   (path)
+    (2, 64, 17, 19, 128, 3, 3, 1, 1, 1, 2, True),     # GEMM, 64 out ch / group
+    (2, 128, 15, 13, 128, 3, 3, 2, 1, 1, 4, True),    # GEMM, 32 / group, stride 2
+    (1, 96, 14, 14, 96, 3, 3, 1, 2, 2, 3, False),     # GEMM, dilation 2
+    (2, 32, 17, 19, 32, 3, 3, 1, 1, 1, 32, True),     # depthwise: direct
+    (2, 8, 21, 20, 16, 3, 3, 1, 1, 1, 8, True),       # channel multiplier 2: direct
+    (1, 16, 30, 31, 24, 5, 5, (2, 1), 2, (1, 2), 4, True),  # small groups: direct
+    (2, 12, 9, 9, 12, 1, 1, 1, 0, 1, 3, True),        # grouped 1x1: direct
+    (1, 8, 70, 70, 8, 3, 3, 8, 1, 1, 8, True),        # stride 8: window > LDS, plain direct
+    (2, 16, 70, 130, 16, 3, 3, 1, 1, 1, 16, False),   # depthwise, several tiles per plane
+]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,groups,has_bias", GCONV_SHAPES)
+def test_grouped_conv_full(B, IC, H, W, OC, KH, KW, stride, pad, dil, groups, has_bias):
+    say(f"conv2d_gemm_f32 groups={groups} x=[{B},{IC},{H},{W}] w=[{OC},{IC // groups},{KH},{KW}]")
+    x, w = gen((B, IC, H, W), 95), gen((OC, IC // groups, KH, KW), 96)
+    bias = gen((OC,), 97) if has_bias else None
+    out = run_gconv(x, w, bias, stride, pad, dil, groups)
+    check_close(out, oracle.conv2d_grouped(x, w, bias, stride, pad, dil, groups),
+                IC // groups * KH * KW, 1.0, f"grouped conv g={groups}")
+
+
+@pytest.mark.parametrize("groups,OC", [(2, 128), (8, 256), (64, 64), (16, 32)])
+def test_grouped_conv_integer_bitwise(groups, OC):
+    say(f"conv2d_gemm_f32 integer groups={groups}")
+    IC = 64 if groups <= 8 else groups
+    x, w, bias = gen((2, IC, 15, 14), 98, "I"), gen((OC, IC // groups, 3, 3), 99, "I"), gen((OC,), 100, "I")
+    out = run_gconv(x, w, bias, 1, 1, 1, groups)
+    check_bitwise(out, oracle.conv2d_grouped(x, w, bias, 1, 1, 1, groups), f"grouped integer g={groups}")
+
+
+@pytest.mark.parametrize("spec", ["1", "3", "6,2", "3,s7", "7,3"])
+def test_grouped_gemm_forced_tile_configs(spec, monkeypatch):
+    monkeypatch.setenv("BAIM_TILE", spec)
+    say(f"BAIM_TILE={spec} grouped conv")
+    x, w, bias = gen((2, 64, 13, 12), 101), gen((96, 32, 3, 3), 102), gen((96,), 103)
+    out = run_gconv(x, w, bias, 1, 1, 1, 2)
+    check_close(out, oracle.conv2d_grouped(x, w, bias, 1, 1, 1, 2), 32 * 9, 1.0, f"grouped {spec}")
+
+
+@pytest.mark.parametrize("name", list(I.GROUPED_CASES))
+def test_workload_grouped_conv(name):
+    import bias_addmm_im2col_amd as baim
+    c = I.GROUPED_CASES[name]
+    say(f"workload {name}: conv2d_gemm_f32 groups={c.groups}")
+    x, w, bias = I.conv_inputs(c)
+    out = baim.conv2d(dev(x), dev(w), dev(bias), c.stride, c.padding, c.dilation, c.groups)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    OH, OW = c.out_hw()
+    idx = conv_sample(c.B, c.OC, OH, OW)
+    res = oracle.conv2d_grouped_at(x, w, bias, c.stride, c.padding, c.dilation, c.groups, idx)
+    ratio = check_close(out.reshape(-1)[idx], res, c.IC // c.groups * c.KH * c.KW, 1.0, name)
+    say(f"{name}: {idx.size} sampled outputs, max err/tol = {ratio:.3f}")
