@@ -95,6 +95,33 @@ class LinearCase:
         return 2 * self.M * self.N * self.K
 
 
+@dataclass(frozen=True)
+class SdpaCase:
+    """Non-causal attention: q [B,H,Sq,D], k and v [B,H,Skv,D], optional
+    additive mask [B,H,Sq,Skv].  ``key_pad`` gives each batch entry b a
+    valid key length L_b drawn uniformly from [Skv/2, Skv]; mask entries for
+    keys >= L_b are -inf (padding of a variable-length key sequence)."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Skv: int
+    D: int
+    q: tuple
+    k: tuple
+    v: tuple
+    mask: tuple | None = None
+    key_pad: bool = False
+    scale: float | None = None  # None: 1/sqrt(D)
+    seed: int = 0
+    kind: str = field(default="sdpa", init=False)
+
+    @property
+    def flops(self) -> int:
+        """q @ k^T and p @ v: 4*B*H*Sq*Skv*D (the softmax is not counted)."""
+        return 4 * self.B * self.H * self.Sq * self.Skv * self.D
+
+
 U11 = ("U", -1.0, 1.0)
 U01 = ("U", 0.0, 1.0)
 
@@ -138,6 +165,20 @@ GROUPED_CASES = {c.name: c for c in [
              N(1), N(0.05), N(0.02), groups=8),
     ConvCase("dwconv3x3_56", 4, 256, 56, 56, 256, 3, 3, (1, 1), (1, 1), (1, 1),
              N(1), N(0.2), N(0.02), groups=256),
+]}
+
+# Non-causal attention in vision encoders and cross-attention: ViT-B/16 at
+# 224 px (196 patches + class token, 12 heads of 64), a 1024-token encoder
+# with 16 heads of 128, cross-attention from 64 queries to 577 image tokens
+# with an additive mask and padded keys, and pooled-query attention
+# (Sq = Skv/4).  q and k ~ N(0,1), so with scale 1/sqrt(D) the logits are
+# about N(0,1); v ~ N(0,1).
+SDPA_CASES = {c.name: c for c in [
+    SdpaCase("sdpa_vit_b32_h12_s197_d64", 32, 12, 197, 197, 64, N(1), N(1), N(1)),
+    SdpaCase("sdpa_b4_h16_s1024_d128", 4, 16, 1024, 1024, 128, N(1), N(1), N(1)),
+    SdpaCase("sdpa_xattn_b8_h12_q64_kv577_d64_mask", 8, 12, 64, 577, 64, N(1), N(1), N(1),
+             mask=N(1), key_pad=True),
+    SdpaCase("sdpa_pooled_b1_h8_q1024_kv4096_d64", 1, 8, 1024, 4096, 64, N(1), N(1), N(1)),
 ]}
 
 # Groups of cases as the workload list states them (small / FFN / stem /
@@ -193,7 +234,26 @@ def linear_inputs(case: LinearCase):
     return x, w, b
 
 
+def sdpa_inputs(case: SdpaCase):
+    """(q, k, v, mask or None) as fp32 CPU tensors, drawn in that order; the
+    key lengths (with key_pad) are drawn last."""
+    g = torch.Generator("cpu").manual_seed(case.seed)
+    q = draw((case.B, case.H, case.Sq, case.D), case.q, g)
+    k = draw((case.B, case.H, case.Skv, case.D), case.k, g)
+    v = draw((case.B, case.H, case.Skv, case.D), case.v, g)
+    mask = None
+    if case.mask is not None:
+        mask = draw((case.B, case.H, case.Sq, case.Skv), case.mask, g)
+        if case.key_pad:
+            lens = torch.randint(case.Skv // 2, case.Skv + 1, (case.B,), generator=g)
+            for b in range(case.B):
+                mask[b, :, :, int(lens[b]):] = float("-inf")
+    return q, k, v, mask
+
+
 def inputs(case):
+    if case.kind == "sdpa":
+        return sdpa_inputs(case)
     if case.kind == "addmm":
         return addmm_inputs(case)
     if case.kind == "linear":

@@ -18,6 +18,10 @@ marshals numpy arrays.  Definitions followed:
   tiled GEMM" (PR #20873), Solution/Implementation: direct sum over
   (ic, kh, kw) taps at ih = oh*sH - pH + kh*dH (and the W analogue),
   out-of-range taps read 0, per-OC bias, NCHW output.
+* sdpa -- "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),
+  Problem/Solution: non-causal ``softmax(q @ k^T * scale + mask) @ v`` over
+  [B,H,S,D] tensors, optional additive mask [B,H,Sq,Skv], Sq may differ from
+  Skv, scale 1/sqrt(D) when not given.
 
 Acceptance bound used by the parity tests (stated with the workload):
 ``|out - ref| <= 4e-6 * sqrt(K) * (|alpha|*sabs + |beta*self|)`` where
@@ -39,6 +43,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.environ.get("BAIM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 Result = namedtuple("Result", ["ref", "sabs", "selfabs"])
+SdpaResult = namedtuple("SdpaResult", ["ref", "err"])
 
 _i64 = ctypes.c_int64
 _fp = ctypes.POINTER(ctypes.c_float)
@@ -86,6 +91,10 @@ def _load():
     lib.oracle_conv2d_grouped.restype = ctypes.c_int
     lib.oracle_conv2d_grouped_at.argtypes = [_i64] * 14 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
     lib.oracle_conv2d_grouped_at.restype = ctypes.c_int
+    lib.oracle_sdpa.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _dp, _dp]
+    lib.oracle_sdpa.restype = ctypes.c_int
+    lib.oracle_sdpa_rows.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _i64, _lp, _dp, _dp]
+    lib.oracle_sdpa_rows.restype = ctypes.c_int
     lib.oracle_im2col.argtypes = [_i64] * 12 + [_fp, _dp]
     lib.oracle_im2col.restype = ctypes.c_int
     _lib = lib
@@ -300,3 +309,54 @@ def im2col(x, KH, KW, stride=1, padding=0, dilation=1):
 def tolerance(res: Result, K: int, alpha: float = 1.0):
     """Elementwise acceptance bound 4e-6*sqrt(K)*(|alpha|*sabs + |beta*self|)."""
     return 4e-6 * np.sqrt(K) * (abs(float(np.float32(alpha))) * res.sabs + res.selfabs)
+
+
+def _sdpa_args(q, k, v, mask, scale):
+    q, k, v, mask = _f32(q), _f32(k), _f32(v), _f32(mask)
+    assert q.ndim >= 3 and k.ndim == q.ndim and v.shape == k.shape
+    assert q.shape[:-2] == k.shape[:-2] and q.shape[-1] == k.shape[-1]
+    Sq, D = q.shape[-2:]
+    Skv = k.shape[-2]
+    BH = int(np.prod(q.shape[:-2]))
+    if mask is not None:
+        assert mask.shape == q.shape[:-1] + (Skv,), "mask must be [..., Sq, Skv]"
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    return q, k, v, mask, float(np.float32(scale)), BH, Sq, Skv, D
+
+
+def sdpa(q, k, v, mask=None, scale=None) -> SdpaResult:
+    """Full reference of softmax(q @ k^T * scale + mask) @ v in fp64.
+
+    q [..., Sq, D], k and v [..., Skv, D], mask [..., Sq, Skv] or None;
+    scale None means 1/sqrt(D) (rounded to fp32, the value a kernel sees).
+    """
+    q, k, v, mask, scale, BH, Sq, Skv, D = _sdpa_args(q, k, v, mask, scale)
+    ref = np.empty(q.shape, np.float64)
+    err = np.empty(q.shape, np.float64)
+    rc = _load().oracle_sdpa(BH, Sq, Skv, D, _ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp),
+                             _ptr(mask, _fp), scale, _ptr(ref, _dp), _ptr(err, _dp))
+    if rc != 0:
+        raise ValueError("attention over an empty key set")
+    return SdpaResult(ref, err)
+
+
+def sdpa_rows(q, k, v, mask, scale, rows) -> SdpaResult:
+    """Reference at sampled query rows (flat index bh*Sq + i): [n, D]."""
+    q, k, v, mask, scale, BH, Sq, Skv, D = _sdpa_args(q, k, v, mask, scale)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    assert rows.ndim == 1 and (rows >= 0).all() and (rows < BH * Sq).all()
+    n = rows.size
+    ref = np.empty((n, D), np.float64)
+    err = np.empty((n, D), np.float64)
+    rc = _load().oracle_sdpa_rows(BH, Sq, Skv, D, _ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp),
+                                  _ptr(mask, _fp), scale, n, _ptr(rows, _lp), _ptr(ref, _dp),
+                                  _ptr(err, _dp))
+    if rc != 0:
+        raise ValueError("attention over an empty key set")
+    return SdpaResult(ref, err)
+
+
+def sdpa_tolerance(res: SdpaResult):
+    """Elementwise acceptance bound 4e-6 * err (err in fp32 rounding units)."""
+    return 4e-6 * res.err

@@ -1,6 +1,6 @@
 /*
- * oracle.c -- plain, slow, fp64 CPU definition of the fp32 "bias addmm" and
- * groups==1 conv2d-as-GEMM computations.
+ * oracle.c -- plain, slow, fp64 CPU definition of the fp32 "bias addmm",
+ * linear, conv2d-as-GEMM and non-causal attention computations.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
  * calls this file; only the test-suite, the smoke check and the CPU-baseline
@@ -26,6 +26,10 @@
  *    the B operand is the input sampled at ih = oh*sH - pH + kh*dH (and the
  *    same along W), with out-of-range taps reading 0 (this is the padding);
  *    bias is added per output channel (row) and the output is NCHW.
+ *
+ *  - "[ExecuTorch][WebGPU] Add optimized SDPA op" (pytorch/executorch PR
+ *    #20851): non-causal attention softmax(q @ k^T * scale + mask) @ v; see
+ *    the section at the end of this file.
  *
  * Arithmetic: every product and sum is done in double from the fp32 inputs
  * widened to double; the sum over k (or over the (ic,kh,kw) taps) runs in
@@ -310,5 +314,107 @@ int oracle_im2col(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t KH,
               col[kk * N + n] = v;
             }
       }
+  return 0;
+}
+
+/* ---- Scaled dot-product attention (non-causal) -------------------------
+ * "[ExecuTorch][WebGPU] Add optimized SDPA op" (pytorch/executorch PR
+ * #20851), Problem and Solution paragraphs: over row-major [B,H,S,D]
+ * tensors, out = softmax(q @ k^T * scale + attn_mask) @ v, the softmax taken
+ * along the key axis.  q is [.., Sq, D]; k and v are [.., Skv, D] (Sq may
+ * differ from Skv); the optional additive mask is [.., Sq, Skv]; the scale
+ * is supplied by the caller (1/sqrt(D) when the op's argument is absent).
+ * The leading batch and head dimensions are flattened to BH.
+ *
+ * Per query row (bh, i):
+ *   s_j  = scale * sum_d q[i,d] k[j,d] + mask[i,j]
+ *   w_j  = exp(s_j - max_j s_j) / sum_j exp(s_j - max_j s_j)
+ *   out[i,d] = sum_j w_j v[j,d]
+ * A row whose logits are all -inf has no softmax; the formula then gives NaN
+ * (as the plain definition and aten do), and so does the oracle.
+ *
+ * Next to out the oracle returns an error scale
+ *   err[i,d] = sum_j w_j (|v[j,d]| + |out[i,d]|)
+ *              * (sqrt(D) a_j + |s_j - max s| + sqrt(Skv) + 1),
+ *   a_j = |scale| sum_d |q[i,d] k[j,d]| + |mask[i,j]|,
+ * the first-order size of an fp32 evaluation's error in units of the fp32
+ * rounding unit: the logit's dot product (a_j), the exponent's argument
+ * (|s_j - max|), the sums over keys (Skv) and the final division.  The
+ * parity bound is |out - ref| <= 4e-6 * err. */
+static void sdpa_row(int64_t bh, int64_t i, int64_t Sq, int64_t Skv, int64_t D,
+                     const float* q, const float* k, const float* v,
+                     const float* mask, float scale, double* s, double* a,
+                     double* out, double* err) {
+  const float* qi = q + (bh * Sq + i) * D;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < Skv; ++j) {
+    const float* kj = k + (bh * Skv + j) * D;
+    double dot = 0.0, dabs = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+      double p = (double)qi[d] * (double)kj[d];
+      dot += p;
+      dabs += fabs(p);
+    }
+    double mk = mask ? (double)mask[(bh * Sq + i) * Skv + j] : 0.0;
+    s[j] = (double)scale * dot + mk;
+    a[j] = fabs((double)scale) * dabs + fabs(mk);
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < Skv; ++j) l += exp(s[j] - m);
+  for (int64_t d = 0; d < D; ++d) {
+    double o = 0.0;
+    for (int64_t j = 0; j < Skv; ++j)
+      o += exp(s[j] - m) / l * (double)v[(bh * Skv + j) * D + d];
+    out[d] = o;
+  }
+  double sd = sqrt((double)D), ss = sqrt((double)Skv);
+  for (int64_t d = 0; d < D; ++d) {
+    double e = 0.0;
+    for (int64_t j = 0; j < Skv; ++j) {
+      double w = exp(s[j] - m) / l;
+      if (!(w > 0.0)) continue; /* a key with weight 0 adds no error */
+      e += w * (fabs((double)v[(bh * Skv + j) * D + d]) + fabs(out[d])) *
+           (sd * a[j] + fabs(s[j] - m) + ss + 1.0);
+    }
+    err[d] = (m == -INFINITY) ? NAN : e;
+  }
+}
+
+/* Full reference: out and err are [BH, Sq, D]. */
+int oracle_sdpa(int64_t BH, int64_t Sq, int64_t Skv, int64_t D, const float* q,
+                const float* k, const float* v, const float* mask, float scale,
+                double* out, double* err) {
+  if (Skv <= 0) return -1;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * 2 * (size_t)Skv);
+#pragma omp for collapse(2) schedule(static)
+    for (int64_t bh = 0; bh < BH; ++bh)
+      for (int64_t i = 0; i < Sq; ++i)
+        sdpa_row(bh, i, Sq, Skv, D, q, k, v, mask, scale, s, s + Skv,
+                 out + (bh * Sq + i) * D, err + (bh * Sq + i) * D);
+    free(s);
+  }
+  return 0;
+}
+
+/* Reference at sampled query rows: rows[r] = bh*Sq + i; out and err are
+ * [n, D]. */
+int oracle_sdpa_rows(int64_t BH, int64_t Sq, int64_t Skv, int64_t D,
+                     const float* q, const float* k, const float* v,
+                     const float* mask, float scale, int64_t n,
+                     const int64_t* rows, double* out, double* err) {
+  if (Skv <= 0) return -1;
+  (void)BH;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * 2 * (size_t)Skv);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+      sdpa_row(rows[r] / Sq, rows[r] % Sq, Sq, Skv, D, q, k, v, mask, scale, s,
+               s + Skv, out + r * D, err + r * D);
+    free(s);
+  }
   return 0;
 }

@@ -511,3 +511,148 @@ def test_sampled_grouped_conv_equals_full():
     idx = np.random.default_rng(3).integers(0, full.ref.size, 150)
     at = oracle.conv2d_grouped_at(x, w, b, (2, 1), 1, (1, 2), 3, idx)
     assert np.array_equal(at.ref, full.ref.reshape(-1)[idx])
+
+
+# ------------------------------------------------------------------ attention
+# "[ExecuTorch][WebGPU] Add optimized SDPA op", Problem/Solution paragraphs:
+# out = softmax(q @ k^T * scale + attn_mask) @ v over [B,H,S,D], softmax along
+# the keys, optional additive [B,H,Sq,Skv] mask, Sq may differ from Skv,
+# scale 1/sqrt(D) by default.
+
+def _qkv(BH, Sq, Skv, D, seed, mask=False):
+    q = rand32((BH, Sq, D), seed)
+    k = rand32((BH, Skv, D), seed + 1)
+    v = rand32((BH, Skv, D), seed + 2)
+    m = rand32((BH, Sq, Skv), seed + 3, -2.0, 2.0) if mask else None
+    return q, k, v, m
+
+
+def test_sdpa_zero_scale_averages_the_values():
+    q, k, v, _ = _qkv(3, 5, 7, 8, 10)
+    r = oracle.sdpa(q, k, v, None, scale=0.0)
+    want = np.broadcast_to(v.astype(np.float64).mean(axis=1, keepdims=True), r.ref.shape)
+    np.testing.assert_allclose(r.ref, want, rtol=0, atol=1e-15)
+
+
+def test_sdpa_one_hot_mask_selects_one_value_row():
+    BH, Sq, Skv, D = 2, 6, 9, 4
+    q, k, v, _ = _qkv(BH, Sq, Skv, D, 20)
+    pick = np.random.default_rng(3).integers(0, Skv, size=(BH, Sq))
+    mask = np.full((BH, Sq, Skv), -np.inf, np.float32)
+    for b in range(BH):
+        for i in range(Sq):
+            mask[b, i, pick[b, i]] = 0.0
+    r = oracle.sdpa(q, k, v, mask)
+    for b in range(BH):
+        for i in range(Sq):
+            assert (r.ref[b, i] == v[b, pick[b, i]].astype(np.float64)).all()
+
+
+def test_sdpa_two_keys_is_a_logistic_blend():
+    # With two keys the softmax weight of key 0 is 1 / (1 + exp(s1 - s0)).
+    q, k, v, m = _qkv(1, 4, 2, 6, 30, mask=True)
+    scale = np.float32(0.375)
+    r = oracle.sdpa(q, k, v, m, scale=scale)
+    for i in range(4):
+        s = [float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(q[0, i], k[0, j]))
+                   * Fraction(float(scale)) + Fraction(float(m[0, i, j]))) for j in range(2)]
+        w0 = 1.0 / (1.0 + np.exp(s[1] - s[0]))
+        want = w0 * v[0, 0].astype(np.float64) + (1.0 - w0) * v[0, 1].astype(np.float64)
+        np.testing.assert_allclose(r.ref[0, i], want, rtol=0, atol=1e-14)
+
+
+def test_sdpa_single_key_returns_its_value():
+    q, k, v, m = _qkv(2, 5, 1, 8, 40, mask=True)
+    r = oracle.sdpa(q, k, v, m)
+    assert (r.ref == np.broadcast_to(v.astype(np.float64), r.ref.shape)).all()
+
+
+def test_sdpa_values_of_ones_give_ones():
+    q, k, _, m = _qkv(2, 5, 11, 8, 50, mask=True)
+    v = np.ones((2, 11, 8), np.float32)
+    r = oracle.sdpa(q, k, v, m)
+    np.testing.assert_allclose(r.ref, 1.0, rtol=0, atol=4e-16)
+
+
+@pytest.mark.parametrize("shape,masked,scale", [
+    ((2, 3, 5, 5, 8), False, None), ((1, 4, 7, 13, 16), True, None),
+    ((3, 1, 9, 4, 12), True, 0.3), ((2, 2, 33, 65, 64), True, None), ((1, 1, 1, 3, 4), False, 2.0)])
+def test_sdpa_vs_torch_float64(shape, masked, scale):
+    B, H, Sq, Skv, D = shape
+    q = rand32((B, H, Sq, D), 60)
+    k = rand32((B, H, Skv, D), 61)
+    v = rand32((B, H, Skv, D), 62)
+    m = rand32((B, H, Sq, Skv), 63, -3, 3) if masked else None
+    r = oracle.sdpa(q, k, v, m, scale)
+    sc = float(np.float32(1.0 / np.sqrt(D) if scale is None else scale))
+    t = F.scaled_dot_product_attention(
+        torch.from_numpy(q).double(), torch.from_numpy(k).double(), torch.from_numpy(v).double(),
+        attn_mask=None if m is None else torch.from_numpy(m).double(), scale=sc).numpy()
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-14)
+
+
+def test_sdpa_default_scale_is_inverse_sqrt_d():
+    q, k, v, _ = _qkv(2, 4, 6, 36, 70)
+    a = oracle.sdpa(q, k, v).ref
+    b = oracle.sdpa(q, k, v, scale=np.float32(1.0 / 6.0)).ref
+    assert (a == b).all()
+    assert not np.allclose(a, oracle.sdpa(q, k, v, scale=np.float32(1.0 / 36.0)).ref)
+
+
+def test_sdpa_row_offset_of_the_mask_cancels():
+    q, k, v, m = _qkv(2, 5, 9, 8, 80, mask=True)
+    shift = rand32((2, 5, 1), 81, -4, 4)
+    a = oracle.sdpa(q, k, v, m).ref
+    b = oracle.sdpa(q, k, v, (m + shift).astype(np.float32)).ref
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-6)  # the shifted mask is rounded to fp32
+
+
+def test_sdpa_key_permutation_invariance():
+    q, k, v, m = _qkv(2, 5, 9, 8, 90, mask=True)
+    perm = np.random.default_rng(5).permutation(9)
+    a = oracle.sdpa(q, k, v, m).ref
+    b = oracle.sdpa(q, k[:, perm].copy(), v[:, perm].copy(), m[:, :, perm].copy()).ref
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+def test_sdpa_masked_rows():
+    q, k, v, m = _qkv(1, 4, 6, 4, 100, mask=True)
+    m[0, 1, :] = -np.inf                      # every key masked: no softmax
+    m[0, 2, :3] = -np.inf                     # first keys masked
+    m[0, 3, 3:] = -np.inf                     # last keys masked
+    r = oracle.sdpa(q, k, v, m)
+    assert np.isnan(r.ref[0, 1]).all() and np.isnan(r.err[0, 1]).all()
+    assert np.isfinite(r.ref[0, [0, 2, 3]]).all() and np.isfinite(r.err[0, [0, 2, 3]]).all()
+    r2 = oracle.sdpa(q[:, 2:3], k[:, 3:], v[:, 3:], m[:, 2:3, 3:].copy())
+    np.testing.assert_allclose(r.ref[0, 2], r2.ref[0, 0], rtol=0, atol=1e-15)
+    r3 = oracle.sdpa(q[:, 3:4], k[:, :3], v[:, :3], m[:, 3:4, :3].copy())
+    np.testing.assert_allclose(r.ref[0, 3], r3.ref[0, 0], rtol=0, atol=1e-15)
+
+
+def test_sdpa_sampled_rows_equal_full():
+    q, k, v, m = _qkv(3, 7, 10, 12, 110, mask=True)
+    full = oracle.sdpa(q, k, v, m, 0.5)
+    rows = np.array([0, 6, 7, 13, 20])
+    s = oracle.sdpa_rows(q, k, v, m, 0.5, rows)
+    assert (s.ref == full.ref.reshape(-1, 12)[rows]).all()
+    assert (s.err == full.err.reshape(-1, 12)[rows]).all()
+
+
+def test_sdpa_error_scale_covers_an_fp32_evaluation():
+    # A plain float32 evaluation (numpy, one order of summation) must sit
+    # inside the acceptance bound 4e-6 * err, with room to spare.
+    B, H, Sq, Skv, D = 2, 2, 48, 300, 64
+    g = torch.Generator("cpu").manual_seed(120)
+    q = (torch.randn(B, H, Sq, D, generator=g) * 1.5).numpy()
+    k = (torch.randn(B, H, Skv, D, generator=g) * 1.5).numpy()
+    v = torch.randn(B, H, Skv, D, generator=g).numpy()
+    m = (torch.randn(B, H, Sq, Skv, generator=g)).numpy()
+    r = oracle.sdpa(q, k, v, m)
+    sc = np.float32(1.0 / 8.0)
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * sc + m
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    f32 = np.matmul(p / p.sum(axis=-1, keepdims=True), v)
+    assert f32.dtype == np.float32
+    bound = oracle.sdpa_tolerance(r)
+    assert (np.abs(f32 - r.ref) <= 0.25 * bound).all()
+    assert (r.err > 0).all()

@@ -35,6 +35,15 @@ MUTANTS = {
     "linear_bias_dropped": ("*ref = (bias ? (double)bias[n] : 0.0) + acc;", "*ref = acc;"),
     "grouped_input_channel_ignores_group": ("int64_t ic = g * icg + icl;", "int64_t ic = icl;"),
     "grouped_weight_index": ("w[((oc * icg + icl) * c->KH", "w[((oc * icg + (icg - 1 - icl)) * c->KH"),
+    "sdpa_scale_dropped": ("s[j] = (double)scale * dot + mk;", "s[j] = dot + mk;"),
+    "sdpa_mask_dropped": ("double mk = mask ? (double)mask[(bh * Sq + i) * Skv + j] : 0.0;",
+                          "double mk = 0.0;"),
+    "sdpa_mask_transposed": ("(double)mask[(bh * Sq + i) * Skv + j]", "(double)mask[(bh * Skv + j) * Sq + i]"),
+    "sdpa_keys_reversed": ("const float* kj = k + (bh * Skv + j) * D;",
+                           "const float* kj = k + (bh * Skv + (Skv - 1 - j)) * D;"),
+    "sdpa_not_normalised": ("o += exp(s[j] - m) / l *", "o += exp(s[j] - m) *"),
+    "sdpa_value_transposed": ("* (double)v[(bh * Skv + j) * D + d];", "* (double)v[(bh * D + d) * Skv + j];"),
+    "sdpa_scale_applied_after_mask": ("s[j] = (double)scale * dot + mk;", "s[j] = (double)scale * (dot + mk);"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
 }
