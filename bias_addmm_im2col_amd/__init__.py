@@ -15,16 +15,21 @@ arguments and allocates outputs with torch:
   GEMM", Solution/Implementation), grouped convs as one such GEMM per group
   or, when the groups are small (e.g. depthwise), on a direct kernel.
 
-``addmm_f32`` and ``conv2d_gemm_f32`` are the same-named entry points of the
-C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
+* ``sdpa(q, k, v, attn_mask=None, scale=None)`` -- non-causal attention
+  ``softmax(q @ k^T * scale + attn_mask) @ v`` over [..., S, D] tensors
+  ("[ExecuTorch][WebGPU] Add optimized SDPA op", Problem/Solution), in one
+  fused pass.
+
+``addmm_f32``, ``linear_f32``, ``conv2d_gemm_f32`` and ``sdpa_f32`` are the
+same-named entry points of the C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
 on the same ROCm device; work is enqueued on the current torch stream.
 """
 from __future__ import annotations
 
 from . import _capi
 
-__all__ = ["addmm", "linear", "conv2d", "addmm_f32", "linear_f32", "conv2d_gemm_f32",
-           "conv2d_out_hw", "gemm_plan",
+__all__ = ["addmm", "linear", "conv2d", "sdpa", "addmm_f32", "linear_f32", "conv2d_gemm_f32",
+           "sdpa_f32", "conv2d_out_hw", "gemm_plan",
            "BaimError", "library_path"]
 
 
@@ -249,3 +254,50 @@ def conv2d(input, weight, bias=None, stride=1, padding=0, dilation=1, groups=1):
                            dilation)
     out = torch.empty((x.shape[0], w.shape[0], OH, OW), dtype=torch.float32, device=x.device)
     return conv2d_gemm_f32(out, x, w, bias, stride, padding, dilation, groups)
+
+
+def sdpa_f32(out, q, k, v, attn_mask=None, scale=None):
+    """out = softmax(q @ k^T * scale + attn_mask) @ v, written into ``out``.
+
+    q [..., Sq, D]; k, v [..., Skv, D] with the same leading dims; attn_mask
+    [..., Sq, Skv] or None; scale None means 1/sqrt(D).  out is like q."""
+    import torch
+    out, q, k, v = (_dev_f32(out, "out"), _dev_f32(q, "q"), _dev_f32(k, "k"), _dev_f32(v, "v"))
+    if q.dim() < 3:
+        raise ValueError("q must have rank >= 3 ([..., S, D])")
+    if k.shape != v.shape or k.dim() != q.dim():
+        raise ValueError("k and v must have the same shape and q's rank")
+    if k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
+        raise ValueError("q, k and v must share leading dims and D")
+    if out.shape != q.shape:
+        raise ValueError(f"out must be {list(q.shape)}")
+    Sq, D = q.shape[-2], q.shape[-1]
+    Skv = k.shape[-2]
+    BH = 1
+    for n in q.shape[:-2]:
+        BH *= int(n)
+    devs = {out.device, q.device, k.device, v.device}
+    mask_ptr = None
+    if attn_mask is not None:
+        attn_mask = _dev_f32(attn_mask, "attn_mask")
+        if attn_mask.shape != q.shape[:-1] + (Skv,):
+            raise ValueError(f"attn_mask must be {list(q.shape[:-1]) + [Skv]}")
+        mask_ptr = attn_mask.data_ptr()
+        devs.add(attn_mask.device)
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    sc = None if scale is None else float(scale)
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.sdpa_f32(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), mask_ptr,
+                            BH, Sq, Skv, D, sc, _stream(dev))
+    _check(st)
+    return out
+
+
+def sdpa(q, k, v, attn_mask=None, scale=None):
+    """Non-causal scaled-dot-product attention as a new tensor shaped like q."""
+    import torch
+    q = _dev_f32(q, "q")
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    return sdpa_f32(out, q, k, v, attn_mask, scale)

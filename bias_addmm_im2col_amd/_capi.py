@@ -25,8 +25,8 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/baim.h declares.
-EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "baim_conv2d_out_hw", "baim_gemm_plan",
-           "baim_last_error", "baim_version")
+EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "sdpa_f32", "baim_conv2d_out_hw",
+           "baim_gemm_plan", "baim_last_error", "baim_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -50,6 +50,8 @@ def lib():
     L.linear_f32.restype = ctypes.c_int
     L.conv2d_gemm_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 14 + [_vp]
     L.conv2d_gemm_f32.restype = ctypes.c_int
+    L.sdpa_f32.argtypes = [_vp] * 5 + [_i64] * 4 + [ctypes.POINTER(ctypes.c_float), _vp]
+    L.sdpa_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
     L.baim_conv2d_out_hw.restype = ctypes.c_int
     L.baim_gemm_plan.argtypes = [_i64] * 3 + [ctypes.POINTER(ctypes.c_int)] * 7
@@ -72,6 +74,11 @@ def addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream) -> i
 
 def linear_f32(out, x, w, bias, M, N, K, stream) -> int:
     return lib().linear_f32(out, x, w, bias, M, N, K, stream)
+
+
+def sdpa_f32(out, q, k, v, mask, BH, Sq, Skv, D, scale, stream) -> int:
+    sc = None if scale is None else ctypes.byref(ctypes.c_float(scale))
+    return lib().sdpa_f32(out, q, k, v, mask, BH, Sq, Skv, D, sc, stream)
 
 
 def conv2d_gemm_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,

@@ -5,6 +5,7 @@
 // both dispatch grids before any buffer is allocated so that a throw cannot
 // leak; here nothing is allocated at all).  Validation makes no HIP call,
 // which keeps it testable on a machine without a GPU.
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -27,6 +28,9 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive
 constexpr int64_t kMaxK = (int64_t)1 << 21;
 constexpr int64_t kMaxAddmmN = (int64_t)1 << 23;
 constexpr int64_t kMaxConvInput = (int64_t)1 << 29;
+// Attention addresses one (batch, head) slice of each tensor with 32-bit
+// byte offsets.
+constexpr int64_t kMaxSlice = (int64_t)1 << 29;
 
 baim_status fail(baim_status s, const char* fmt, ...) {
   char buf[512];
@@ -251,3 +255,44 @@ baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
 }
 
 }  // extern "C"
+
+extern "C" baim_status sdpa_f32(float* out, const float* q, const float* k, const float* v,
+                                const float* attn_mask, int64_t BH, int64_t Sq, int64_t Skv,
+                                int64_t D, const float* scale, void* stream) {
+  g_err.clear();
+  if (BH < 0 || Sq < 0 || Skv < 0 || D < 0)
+    return fail(BAIM_ERR_SHAPE, "sdpa: sizes must be >= 0 (BH=%lld Sq=%lld Skv=%lld D=%lld)",
+                (long long)BH, (long long)Sq, (long long)Skv, (long long)D);
+  const int64_t n_q = elems({BH, Sq, D}), n_kv = elems({BH, Skv, D});
+  const int64_t n_m = elems({BH, Sq, Skv});
+  if (n_q < 0 || n_kv < 0 || n_m < 0 || n_q >= kMaxElems || n_kv >= kMaxElems ||
+      (attn_mask && n_m >= kMaxElems))
+    return fail(BAIM_ERR_TOO_LARGE, "sdpa: every tensor must have fewer than 2^31 elements");
+  if (elems({Sq, D}) >= kMaxSlice || elems({Skv, D}) >= kMaxSlice ||
+      (attn_mask && elems({Sq, Skv}) >= kMaxSlice))
+    return fail(BAIM_ERR_TOO_LARGE, "sdpa: Sq*D, Skv*D and Sq*Skv must be below 2^29");
+  if (n_q == 0) return BAIM_OK;
+  if (Skv == 0) return fail(BAIM_ERR_SHAPE, "sdpa: Skv must be >= 1 (no softmax over no keys)");
+  if (D % 4 != 0 || D > 128)
+    return fail(BAIM_ERR_UNSUPPORTED, "sdpa: D=%lld must be a multiple of 4 and at most 128",
+                (long long)D);
+  if (!out || !q || !k || !v) return fail(BAIM_ERR_NULL, "sdpa: out/q/k/v is NULL");
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) != 0)
+    return fail(BAIM_ERR_UNSUPPORTED, "sdpa: q, k and v must start on 16-byte boundaries");
+  if (overlap(out, n_q, q, n_q) || overlap(out, n_q, k, n_kv) || overlap(out, n_q, v, n_kv) ||
+      overlap(out, n_q, attn_mask, n_m))
+    return fail(BAIM_ERR_ALIAS, "sdpa: out overlaps an input");
+
+  baim::SdpaProblem p;
+  p.out = out;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.mask = attn_mask;
+  p.BH = (int)BH;
+  p.Sq = (int)Sq;
+  p.Skv = (int)Skv;
+  p.D = (int)D;
+  p.scale = scale ? *scale : (float)(1.0 / sqrt((double)D));
+  return launched(baim::launch_sdpa(p, (hipStream_t)stream), "sdpa_f32");
+}

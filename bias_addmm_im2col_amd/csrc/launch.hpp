@@ -27,6 +27,16 @@ struct ConvProblem {
   int groups;  // >= 1, dividing IC and OC; weight is [OC, IC/groups, KH, KW]
 };
 
+struct SdpaProblem {
+  float* out;          // [BH, Sq, D]
+  const float* q;      // [BH, Sq, D]
+  const float* k;      // [BH, Skv, D]
+  const float* v;      // [BH, Skv, D]
+  const float* mask;   // [BH, Sq, Skv] additive, or NULL
+  int BH, Sq, Skv, D;  // D % 4 == 0, D <= 128; Skv >= 1
+  float scale;
+};
+
 // Whether a grouped conv runs as one implicit-im2col GEMM per group (true)
 // or on the direct kernel (per-group GEMMs too small for the matrix cores).
 inline bool conv_uses_gemm(const ConvProblem& q) {
@@ -37,5 +47,6 @@ inline bool conv_uses_gemm(const ConvProblem& q) {
 hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
+hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);
 
 }  // namespace baim

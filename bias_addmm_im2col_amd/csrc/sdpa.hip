@@ -1,0 +1,290 @@
+// sdpa.hip -- non-causal scaled-dot-product attention, fp32, on the gfx950
+// matrix cores.
+//
+// "[ExecuTorch][WebGPU] Add optimized SDPA op" (pytorch/executorch PR
+// #20851), Problem and Solution paragraphs: over row-major [B,H,S,D]
+// tensors, out = softmax(q @ k^T * scale + attn_mask) @ v, with an optional
+// additive [B,H,Sq,Skv] mask, Sq and Skv free to differ, and scale 1/sqrt(D)
+// when not given.  The page chains three dispatches through two
+// B*H*Sq*Skv scratch buffers (scores, then softmax).  Here one kernel
+// streams 64-key tiles of k and v through LDS and keeps a running softmax
+// per query row (maximum and sum rescaled as the maximum grows), so the
+// scores stay in registers and nothing is allocated.
+//
+// Work split: a block of four waves owns 128 query rows of one (batch, head);
+// each wave owns 32 of them.  Per key tile a wave computes
+//   S^T[kv, q] = K[kv, :] . Q[q, :]        (two 32x32 blocks, k = d)
+// on v_mfma_f32_32x32x2_f32 with K as the A operand (16-byte LDS reads) and
+// Q as the B operand (kept in registers for the whole pass), then
+//   O[q, d] += P[q, kv] V[kv, d]           (DP/32 blocks, k = kv)
+// with P as the A operand.  In the MFMA lane layout (lane l, c = l % 32,
+// h = l / 32) accumulator register j of S^T holds key 8*(j/4) + 4*h + j%4
+// of query c, and the A operand of step s is row c, k-index h; visiting the
+// keys of a 32-key block in the order 8*(s/4) + 4*h + s%4 makes step s of
+// the second product take register s of the first as its A value: the
+// probabilities never move between lanes.  Each query's row statistics
+// (maximum, sum) live in lanes c and c+32; the per-row rescale factors the
+// O rows need are passed through a 32-float LDS slot per wave.
+//
+// Ragged edges: q rows past Sq load as 0 and are not stored; keys past Skv
+// get the logit -inf (weight 0) and their k/v rows load as 0; d past D (D
+// is padded to DP, a multiple of 32) loads as 0 and is not stored.  A row
+// whose logits are all -inf ends with sum 0 and gives 0 * (1/0) = NaN, the
+// value of the plain definition.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "gemm_core.hpp"
+#include "index_math.hpp"
+#include "launch.hpp"
+
+namespace baim {
+
+namespace {
+
+constexpr int kSdpaWaves = 4;
+constexpr int kSdpaBQ = 32 * kSdpaWaves;  // query rows per block
+constexpr int kSdpaBKV = 64;              // keys per tile
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct SdpaArgs {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* mask;
+  float* out;
+  int Sq, Skv, D;
+  int qblocks, nblocks;
+  float scale;
+};
+
+template <int DP>
+struct SdpaShape {
+  static constexpr int KS = DP + 4;   // LDS row stride (floats) of the k and v tiles
+  static constexpr int CH = DP / 4;   // 16-byte chunks per row
+  static constexpr int NCH = kSdpaBKV * CH / (64 * kSdpaWaves);  // chunks per thread
+  static constexpr int ND = DP / 32;  // 32-wide d blocks of O
+  static constexpr int NQ = DP / 8;   // Q chunks per lane
+  static constexpr int LDS_FLOATS = 2 * kSdpaBKV * KS + 32 * kSdpaWaves;
+  static_assert(DP % 32 == 0 && DP <= 128, "D is padded to 32, 64, 96 or 128");
+  static_assert((kSdpaBKV * CH) % (64 * kSdpaWaves) == 0, "tile splits evenly");
+};
+
+// Multiply row r = 8*(j/4) + 4*h + j%4 of a wave's 32x32 O blocks by f[r],
+// where f[q] is held by lanes q and q + 32.
+template <int ND>
+__device__ __forceinline__ void scale_rows(f32x16 (&o)[ND], float f, float* slot, int c, int h) {
+  if (h == 0) slot[c] = f;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  f32x4 r[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) r[g] = *reinterpret_cast<const f32x4*>(slot + 8 * g + 4 * h);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] *= r[j / 4][j % 4];
+}
+
+template <int DP, bool MASK, int MV>
+__global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a) {
+  using S = SdpaShape<DP>;
+  __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
+  float* Ks = smem;
+  float* Vs = smem + kSdpaBKV * S::KS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* slot = Vs + kSdpaBKV * S::KS + 32 * wave;
+  const int c = lane & 31, h = lane >> 5;
+
+  const int lid = xcd_linear(blockIdx.x, a.nblocks);
+  const int bh = lid / a.qblocks, qb = lid - bh * a.qblocks;
+  const int Sq = a.Sq, Skv = a.Skv, D = a.D;
+  const int qrow0 = qb * kSdpaBQ + wave * 32;  // first query row of this wave
+  const int q = qrow0 + c;                     // this lane's query (column of S^T)
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (size_t)bh * Sq * D, (int64_t)Sq * D);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k + (size_t)bh * Skv * D, (int64_t)Skv * D);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v + (size_t)bh * Skv * D, (int64_t)Skv * D);
+  __amdgpu_buffer_rsrc_t mr;
+  if constexpr (MASK) mr = make_rsrc(a.mask + (size_t)bh * Sq * Skv, (int64_t)Sq * Skv);
+
+  // Q fragments: chunk t holds Q[q][8t + 4h .. 8t + 4h + 3].
+  f32x4 qf[S::NQ];
+#pragma unroll
+  for (int t = 0; t < S::NQ; ++t) {
+    const int d = 8 * t + 4 * h;
+    const uint32_t off = (q < Sq && d < D) ? (uint32_t)(q * D + d) * 4u : kOOB;
+    qf[t] = Vec<4>::load(qr, off);
+  }
+
+  // k/v tile loads: chunk i of thread tid is row idx / CH, column 4*(idx % CH).
+  f32x4 kreg[S::NCH], vreg[S::NCH];
+  auto fetch = [&](int kv0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < S::NCH; ++i) {
+      const int idx = i * 64 * kSdpaWaves + tid;
+      const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
+      const int kv = kv0 + row;
+      const uint32_t off = (kv < Skv && d < D) ? (uint32_t)(kv * D + d) * 4u : kOOB;
+      kreg[i] = Vec<4>::load(kr, off);
+      vreg[i] = Vec<4>::load(vr, off);
+    }
+  };
+  auto put = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < S::NCH; ++i) {
+      const int idx = i * 64 * kSdpaWaves + tid;
+      const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
+      *reinterpret_cast<f32x4*>(Ks + row * S::KS + d) = kreg[i];
+      *reinterpret_cast<f32x4*>(Vs + row * S::KS + d) = vreg[i];
+    }
+  };
+
+  f32x16 o[S::ND];
+#pragma unroll
+  for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[db][j] = 0.0f;
+  float m_run = -INFINITY, l_lane = 0.0f;
+  const int ntiles = (Skv + kSdpaBKV - 1) / kSdpaBKV;
+
+  fetch(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * kSdpaBKV;
+    if (t > 0) __syncthreads();  // every wave is done with the previous tile
+    put();
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(kv0 + kSdpaBKV);
+
+    // Mask values of this lane's 32 (query, key) pairs: keys
+    // kv0 + 32*kb + 8*g + 4*h + r, r = 0..3.
+    f32x4 mk[2][4];
+    if constexpr (MASK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kv = kv0 + 32 * kb + 8 * g + 4 * h;
+          if constexpr (MV == 4) {
+            const uint32_t off = (q < Sq && kv < Skv) ? (uint32_t)(q * Skv + kv) * 4u : kOOB;
+            mk[kb][g] = Vec<4>::load(mr, off);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t off =
+                  (q < Sq && kv + r < Skv) ? (uint32_t)(q * Skv + kv + r) * 4u : kOOB;
+              mk[kb][g][r] = Vec<1>::load(mr, off);
+            }
+          }
+        }
+    }
+
+    // S^T = K Q^T for the tile's two 32-key blocks.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
+      const float* krow = Ks + (32 * kb + c) * S::KS + 4 * h;
+#pragma unroll
+      for (int t2 = 0; t2 < S::NQ; ++t2) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + 8 * t2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[r], qf[t2][r], s[kb], 0, 0, 0);
+      }
+    }
+
+    // Logits, running maximum and sum.
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kv = kv0 + 32 * kb + 8 * (j / 4) + 4 * h + (j % 4);
+        float x = s[kb][j] * a.scale;
+        if constexpr (MASK) x += mk[kb][j / 4][j % 4];
+        x = kv < Skv ? x : -INFINITY;
+        s[kb][j] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * kLog2e);
+    float ps = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f((s[kb][j] - m_use) * kLog2e);
+        s[kb][j] = p;
+        ps += p;
+      }
+    l_lane = l_lane * alpha + ps;
+    m_run = m_new;
+    scale_rows(o, alpha, slot, c, h);
+
+    // O += P V: step st of key block kb takes key 32*kb + 8*(st/4) + 4*h + st%4.
+#pragma unroll
+    for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+          const int kv = 32 * kb + 8 * (st / 4) + 4 * h + (st % 4);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[kb][st], Vs[kv * S::KS + 32 * db + c],
+                                                       o[db], 0, 0, 0);
+        }
+  }
+
+  const float l = l_lane + __shfl_xor(l_lane, 32);
+  scale_rows(o, 1.0f / l, slot, c, h);
+  float* out = a.out + (size_t)bh * Sq * D;
+#pragma unroll
+  for (int db = 0; db < S::ND; ++db) {
+    const int d = 32 * db + c;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = qrow0 + 8 * (j / 4) + 4 * h + (j % 4);
+      if (row < Sq && d < D) out[(size_t)row * D + d] = o[db][j];
+    }
+  }
+}
+
+template <int DP>
+hipError_t launch_dp(const SdpaArgs& a, bool mask_vec, hipStream_t s) {
+  const dim3 grid(a.nblocks), block(64 * kSdpaWaves);
+  if (!a.mask)
+    hipLaunchKernelGGL((sdpa_kernel<DP, false, 4>), grid, block, 0, s, a);
+  else if (mask_vec)
+    hipLaunchKernelGGL((sdpa_kernel<DP, true, 4>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((sdpa_kernel<DP, true, 1>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream) {
+  SdpaArgs a;
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.mask = p.mask;
+  a.out = p.out;
+  a.Sq = p.Sq;
+  a.Skv = p.Skv;
+  a.D = p.D;
+  a.scale = p.scale;
+  a.qblocks = (p.Sq + kSdpaBQ - 1) / kSdpaBQ;
+  a.nblocks = p.BH * a.qblocks;
+  // 16-byte mask loads need rows that start on 16-byte boundaries.
+  const bool mask_vec = p.mask && p.Skv % 4 == 0 && ((uintptr_t)p.mask & 15) == 0;
+  if (p.D <= 32) return launch_dp<32>(a, mask_vec, stream);
+  if (p.D <= 64) return launch_dp<64>(a, mask_vec, stream);
+  if (p.D <= 96) return launch_dp<96>(a, mask_vec, stream);
+  return launch_dp<128>(a, mask_vec, stream);
+}
+
+}  // namespace baim

@@ -130,6 +130,37 @@ baim_status conv2d_gemm_f32(float* out, const float* input,
                             int64_t groups, void* stream);
 
 /*
+ * sdpa_f32: out = softmax(q @ k^T * scale + attn_mask) @ v, non-causal.
+ *
+ * Defined by "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),
+ * Problem and Solution paragraphs: row-major [B,H,S,D] tensors with the
+ * softmax along the key axis, an optional additive mask of shape
+ * [B,H,Sq,Skv], Sq and Skv free to differ, scale 1/sqrt(D) when not given,
+ * fp32 only, D a multiple of 4.  The leading batch and head dimensions are
+ * passed flattened as BH.  Computed in one pass with a running softmax per
+ * query row; no scores buffer is allocated.
+ *
+ *  out        [BH,Sq,D] fp32, written in full.
+ *  q          [BH,Sq,D] fp32.   k, v  [BH,Skv,D] fp32.
+ *             q, k and v must start on 16-byte boundaries.
+ *  attn_mask  [BH,Sq,Skv] fp32 added to the scaled logits, or NULL.  -inf
+ *             entries drop keys; a query row with every key dropped comes
+ *             out NaN (there is no softmax over an empty set).
+ *  BH,Sq,D    >= 0; any of them 0: nothing to do, BAIM_OK.
+ *  Skv        >= 1 (BAIM_ERR_SHAPE otherwise, unless the output is empty).
+ *  D          a multiple of 4 and at most 128 (BAIM_ERR_UNSUPPORTED).
+ *  scale      host pointer to the multiplier of q.k, or NULL for
+ *             1/sqrt(D) rounded to fp32.
+ *  stream     hipStream_t or NULL.
+ * Limits: Sq*D, Skv*D and Sq*Skv below 2^29; every tensor below 2^31
+ * elements (BAIM_ERR_TOO_LARGE).
+ */
+baim_status sdpa_f32(float* out, const float* q, const float* k,
+                     const float* v, const float* attn_mask, int64_t BH,
+                     int64_t Sq, int64_t Skv, int64_t D, const float* scale,
+                     void* stream);
+
+/*
  * baim_conv2d_out_hw: the output size of the conv above,
  * OH = floor((H + 2*pH - dH*(KH-1) - 1) / sH) + 1 and likewise OW (the
  * pages print no formula; this is the standard one, which gives a 192x192

@@ -179,6 +179,44 @@ def test_gemm_plan(lib, monkeypatch):
     assert (p["bm"], p["bn"], p["splits"], p["stream_blocks"]) == (128, 64, 1, 256)
 
 
+M5 = 5 * P  # fake mask address
+
+
+def sdpa(out=O, q=A, k=Bp, v=S, mask=None, BH=2, Sq=8, Skv=8, D=16, scale=None):
+    return _capi.sdpa_f32(out, q, k, v, mask, BH, Sq, Skv, D, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(BH=-1), _capi.BAIM_ERR_SHAPE),
+    (dict(Skv=-3), _capi.BAIM_ERR_SHAPE),
+    (dict(Skv=0), _capi.BAIM_ERR_SHAPE),
+    (dict(D=6), _capi.BAIM_ERR_UNSUPPORTED),
+    (dict(D=132), _capi.BAIM_ERR_UNSUPPORTED),
+    (dict(out=None), _capi.BAIM_ERR_NULL),
+    (dict(v=None), _capi.BAIM_ERR_NULL),
+    (dict(q=A + 4), _capi.BAIM_ERR_UNSUPPORTED),   # not on a 16-byte boundary
+    (dict(k=Bp + 8), _capi.BAIM_ERR_UNSUPPORTED),
+    (dict(out=A + 64), _capi.BAIM_ERR_ALIAS),      # out inside q
+    (dict(out=S - 4), _capi.BAIM_ERR_ALIAS),       # out runs into v
+    (dict(mask=M5, out=M5 + 4), _capi.BAIM_ERR_ALIAS),
+    (dict(BH=1 << 20, Sq=1 << 11, D=8), _capi.BAIM_ERR_TOO_LARGE),
+    (dict(BH=1, Sq=1 << 27, D=4), _capi.BAIM_ERR_TOO_LARGE),       # Sq*D = 2^29
+    (dict(BH=1, Sq=1 << 15, Skv=1 << 14, D=4, mask=M5), _capi.BAIM_ERR_TOO_LARGE),
+])
+def test_sdpa_rejects(lib, kw, status):
+    st = sdpa(**kw)
+    assert st == status, (st, _capi.last_error())
+    assert _capi.last_error()
+
+
+def test_sdpa_empty_output_is_ok_without_launch(lib):
+    assert sdpa(Sq=0) == _capi.BAIM_OK
+    assert sdpa(BH=0, Skv=0) == _capi.BAIM_OK
+    assert sdpa(D=0, out=None, q=None, k=None, v=None) == _capi.BAIM_OK
+    # a large mask is fine when no mask is passed
+    assert sdpa(BH=1, Sq=1 << 15, Skv=1 << 14, D=4, out=None) == _capi.BAIM_ERR_NULL
+
+
 def test_python_layer_checks_before_the_library():
     """Dtype/device/shape errors of the torch wrapper, raised on the CPU."""
     import torch
@@ -189,3 +227,7 @@ def test_python_layer_checks_before_the_library():
         baim.addmm(torch.zeros(3), torch.zeros(2, 3), torch.zeros(3, 3))  # CPU tensors
     with pytest.raises(ValueError):  # CPU tensors
         baim.conv2d(torch.zeros(1, 4, 5, 5), torch.zeros(4, 2, 3, 3), groups=2)
+    with pytest.raises(TypeError):
+        baim.sdpa(torch.zeros(1, 2, 4, dtype=torch.float64), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))
+    with pytest.raises(ValueError):  # CPU tensors
+        baim.sdpa(torch.zeros(1, 2, 4), torch.zeros(1, 2, 4), torch.zeros(1, 2, 4))
