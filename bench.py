@@ -92,10 +92,22 @@ def load_traffic(kernel: str):
 class Case:
     def __init__(self, name, torch, baim, I):
         self.name = name
-        c = (I.CASES.get(name) or I.LINEAR_CASES.get(name) or I.GROUPED_CASES[name])
+        c = (I.CASES.get(name) or I.LINEAR_CASES.get(name) or I.GROUPED_CASES.get(name)
+             or I.SDPA_CASES[name])
         self.c = c
         self.op = c.kind
         self.flops = c.flops
+        if c.kind == "sdpa":
+            q, k, v, m = I.sdpa_inputs(c)
+            self.host = (q, k, v, m)
+            self.q, self.k, self.v = q.cuda(), k.cuda(), v.cuda()
+            self.m = None if m is None else m.cuda()
+            self.out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+            dp = -(-c.D // 32) * 32
+            self.kernel = f"baim::sdpa_kernel<D {dp}{', mask' if m is not None else ''}>"
+            self.run = lambda: baim.sdpa_f32(self.out, self.q, self.k, self.v, self.m, c.scale)
+            self.bytes = 4 * sum(t.numel() for t in (q, k, v, self.out) + ((m,) if m is not None else ()))
+            return
         M, N, K = (c.M, c.N, c.K) if c.kind != "conv" else c.gemm_mnk
         p = baim.gemm_plan(M, N, K)
         self.plan = p
@@ -134,12 +146,13 @@ class Case:
 
 
 def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
-    """Ops beyond the step's workload (linear, weight [N,K]), timed the same
-    way but reported separately: they are not part of `value`.  Each case
+    """Ops beyond the step's workload (linear with weight [N,K], grouped and
+    depthwise conv, attention), timed the same way but reported separately:
+    they are not part of `value`.  Each case
     first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
     switch to new buffers)."""
     rows = []
-    for name in list(I.LINEAR_CASES) + list(I.GROUPED_CASES):
+    for name in list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.SDPA_CASES):
         cs = Case(name, torch, baim, I)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < warmup_s:

@@ -11,9 +11,14 @@
 // per query row (maximum and sum rescaled as the maximum grows), so the
 // scores stay in registers and nothing is allocated.
 //
-// Work split: a block of four waves owns 128 query rows of one (batch, head);
-// each wave owns 32 of them.  Per key tile a wave computes
-//   S^T[kv, q] = K[kv, :] . Q[q, :]        (two 32x32 blocks, k = d)
+// Work split: a block of four waves owns 32*QW query rows of one (batch,
+// head): QW query groups of 32 rows times KW key groups (QW*KW = 4).  The
+// block stages tiles of 32*NB*KW keys; in each, key group g takes the NB
+// 32-key blocks g*NB .. g*NB+NB-1, and keeps its own running softmax, so a
+// short query range still keeps four waves busy.  At the end the key groups'
+// (maximum, sum, O) are merged through LDS in group order.  Per 32-key block
+// a wave computes
+//   S^T[kv, q] = K[kv, :] . Q[q, :]        (a 32x32 block, k = d)
 // on v_mfma_f32_32x32x2_f32 with K as the A operand (16-byte LDS reads) and
 // Q as the B operand (kept in registers for the whole pass), then
 //   O[q, d] += P[q, kv] V[kv, d]           (DP/32 blocks, k = kv)
@@ -33,18 +38,17 @@
 // value of the plain definition.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include "gemm_core.hpp"
 #include "index_math.hpp"
 #include "launch.hpp"
+#include "tile_select.hpp"
 
 namespace baim {
 
 namespace {
 
-constexpr int kSdpaWaves = 4;
-constexpr int kSdpaBQ = 32 * kSdpaWaves;  // query rows per block
-constexpr int kSdpaBKV = 64;              // keys per tile
 constexpr float kLog2e = 1.44269504088896340736f;
 
 struct SdpaArgs {
@@ -58,16 +62,27 @@ struct SdpaArgs {
   float scale;
 };
 
-template <int DP>
+template <int DP, int QW, int KW, int NB>
 struct SdpaShape {
-  static constexpr int KS = DP + 4;   // LDS row stride (floats) of the k and v tiles
-  static constexpr int CH = DP / 4;   // 16-byte chunks per row
-  static constexpr int NCH = kSdpaBKV * CH / (64 * kSdpaWaves);  // chunks per thread
-  static constexpr int ND = DP / 32;  // 32-wide d blocks of O
-  static constexpr int NQ = DP / 8;   // Q chunks per lane
-  static constexpr int LDS_FLOATS = 2 * kSdpaBKV * KS + 32 * kSdpaWaves;
+  static constexpr int NT = 64 * QW * KW;
+  static constexpr int BQ = 32 * QW;        // query rows per block
+  static constexpr int BKV = 32 * NB * KW;  // keys per tile
+  static constexpr int KS = DP + 4;         // LDS row stride (floats) of the k and v tiles
+  static constexpr int CH = DP / 4;         // 16-byte chunks per row
+  static constexpr int NCH = BKV * CH / NT; // chunks per thread and tile
+  static constexpr int ND = DP / 32;        // 32-wide d blocks of O
+  static constexpr int NQ = DP / 8;         // Q chunks per lane
+  static constexpr int TILE_FLOATS = 2 * BKV * KS;
+  // merge of the key groups: partial O of groups 1..KW-1, then (max, sum)
+  // of every group, both over the (dead) tile area
+  static constexpr int RED_FLOATS = (KW - 1) * QW * 32 * DP;
+  static constexpr int STAT_FLOATS = 2 * KW * BQ;
+  static constexpr int MERGE_FLOATS = RED_FLOATS + STAT_FLOATS;
+  static constexpr int SLOT_OFS = TILE_FLOATS > MERGE_FLOATS ? TILE_FLOATS : MERGE_FLOATS;
+  static constexpr int LDS_FLOATS = SLOT_OFS + 32 * QW * KW;
   static_assert(DP % 32 == 0 && DP <= 128, "D is padded to 32, 64, 96 or 128");
-  static_assert((kSdpaBKV * CH) % (64 * kSdpaWaves) == 0, "tile splits evenly");
+  static_assert(QW * KW == 4, "four waves per block");
+  static_assert((BKV * CH) % NT == 0, "tile splits evenly");
 };
 
 // Multiply row r = 8*(j/4) + 4*h + j%4 of a wave's 32x32 O blocks by f[r],
@@ -86,22 +101,24 @@ __device__ __forceinline__ void scale_rows(f32x16 (&o)[ND], float f, float* slot
     for (int j = 0; j < 16; ++j) o[db][j] *= r[j / 4][j % 4];
 }
 
-template <int DP, bool MASK, int MV>
-__global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a) {
-  using S = SdpaShape<DP>;
+template <int DP, int QW, int KW, int NB, bool MASK, int MV>
+__global__ __launch_bounds__(256, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a) {
+  using S = SdpaShape<DP, QW, KW, NB>;
   __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
   float* Ks = smem;
-  float* Vs = smem + kSdpaBKV * S::KS;
+  float* Vs = smem + S::BKV * S::KS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float* slot = Vs + kSdpaBKV * S::KS + 32 * wave;
+  const int qg = wave % QW, kg = wave / QW;  // query group, key group
+  float* slot = smem + S::SLOT_OFS + 32 * wave;
   const int c = lane & 31, h = lane >> 5;
 
   const int lid = xcd_linear(blockIdx.x, a.nblocks);
   const int bh = lid / a.qblocks, qb = lid - bh * a.qblocks;
   const int Sq = a.Sq, Skv = a.Skv, D = a.D;
-  const int qrow0 = qb * kSdpaBQ + wave * 32;  // first query row of this wave
-  const int q = qrow0 + c;                     // this lane's query (column of S^T)
+  const int qrow0 = qb * S::BQ + qg * 32;  // first query row of this wave
+  const int q = qrow0 + c;                 // this lane's query (column of S^T)
+  const bool active = qrow0 < Sq;          // wave-uniform
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + (size_t)bh * Sq * D, (int64_t)Sq * D);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(a.k + (size_t)bh * Skv * D, (int64_t)Skv * D);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(a.v + (size_t)bh * Skv * D, (int64_t)Skv * D);
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
   auto fetch = [&](int kv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
-      const int idx = i * 64 * kSdpaWaves + tid;
+      const int idx = i * S::NT + tid;
       const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
       const int kv = kv0 + row;
       const uint32_t off = (kv < Skv && d < D) ? (uint32_t)(kv * D + d) * 4u : kOOB;
@@ -133,7 +150,7 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
   auto put = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
-      const int idx = i * 64 * kSdpaWaves + tid;
+      const int idx = i * S::NT + tid;
       const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
       *reinterpret_cast<f32x4*>(Ks + row * S::KS + d) = kreg[i];
       *reinterpret_cast<f32x4*>(Vs + row * S::KS + d) = vreg[i];
@@ -146,65 +163,73 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[db][j] = 0.0f;
   float m_run = -INFINITY, l_lane = 0.0f;
-  const int ntiles = (Skv + kSdpaBKV - 1) / kSdpaBKV;
+  const int ntiles = (Skv + S::BKV - 1) / S::BKV;
 
   fetch(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int kv0 = t * kSdpaBKV;
+    const int kv0 = t * S::BKV;
     if (t > 0) __syncthreads();  // every wave is done with the previous tile
     put();
     __syncthreads();
-    if (t + 1 < ntiles) fetch(kv0 + kSdpaBKV);
+    if (t + 1 < ntiles) fetch(kv0 + S::BKV);
 
-    // Mask values of this lane's 32 (query, key) pairs: keys
-    // kv0 + 32*kb + 8*g + 4*h + r, r = 0..3.
-    f32x4 mk[2][4];
+    // This wave's key blocks: keys kb0 + 32*kb + (0..31) of the tile, in
+    // the order 8*(j/4) + 4*h + j%4 (register j of S^T).
+    const int kb0 = 32 * NB * kg;
+    bool blk[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) blk[kb] = active && kv0 + kb0 + 32 * kb < Skv;
+
+    f32x4 mk[NB][4];
     if constexpr (MASK) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int kv = kv0 + 32 * kb + 8 * g + 4 * h;
+          const int kv = kv0 + kb0 + 32 * kb + 8 * g + 4 * h;
+          const bool row_ok = blk[kb] && q < Sq;
           if constexpr (MV == 4) {
-            const uint32_t off = (q < Sq && kv < Skv) ? (uint32_t)(q * Skv + kv) * 4u : kOOB;
+            const uint32_t off = (row_ok && kv < Skv) ? (uint32_t)(q * Skv + kv) * 4u : kOOB;
             mk[kb][g] = Vec<4>::load(mr, off);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const uint32_t off =
-                  (q < Sq && kv + r < Skv) ? (uint32_t)(q * Skv + kv + r) * 4u : kOOB;
+                  (row_ok && kv + r < Skv) ? (uint32_t)(q * Skv + kv + r) * 4u : kOOB;
               mk[kb][g][r] = Vec<1>::load(mr, off);
             }
           }
         }
     }
 
-    // S^T = K Q^T for the tile's two 32-key blocks.
-    f32x16 s[2];
+    // S^T = K Q^T per key block.
+    f32x16 s[NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
-      const float* krow = Ks + (32 * kb + c) * S::KS + 4 * h;
+      if (blk[kb]) {
+        const float* krow = Ks + (kb0 + 32 * kb + c) * S::KS + 4 * h;
 #pragma unroll
-      for (int t2 = 0; t2 < S::NQ; ++t2) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + 8 * t2);
+        for (int t2 = 0; t2 < S::NQ; ++t2) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + 8 * t2);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[r], qf[t2][r], s[kb], 0, 0, 0);
+          for (int r = 0; r < 4; ++r)
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[r], qf[t2][r], s[kb], 0, 0, 0);
+        }
       }
     }
 
     // Logits, running maximum and sum.
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int kv = kv0 + 32 * kb + 8 * (j / 4) + 4 * h + (j % 4);
+        const int kv = kv0 + kb0 + 32 * kb + 8 * (j / 4) + 4 * h + (j % 4);
         float x = s[kb][j] * a.scale;
         if constexpr (MASK) x += mk[kb][j / 4][j % 4];
-        x = kv < Skv ? x : -INFINITY;
+        x = (blk[kb] && kv < Skv) ? x : -INFINITY;
         s[kb][j] = x;
         mt = fmaxf(mt, x);
       }
@@ -214,7 +239,7 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * kLog2e);
     float ps = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float p = __builtin_amdgcn_exp2f((s[kb][j] - m_use) * kLog2e);
@@ -225,21 +250,68 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
     m_run = m_new;
     scale_rows(o, alpha, slot, c, h);
 
-    // O += P V: step st of key block kb takes key 32*kb + 8*(st/4) + 4*h + st%4.
+    // O += P V: step st of key block kb takes key kb0 + 32*kb + 8*(st/4) + 4*h + st%4.
 #pragma unroll
-    for (int db = 0; db < S::ND; ++db)
+    for (int kb = 0; kb < NB; ++kb)
+      if (blk[kb]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < S::ND; ++db)
 #pragma unroll
-        for (int st = 0; st < 16; ++st) {
-          const int kv = 32 * kb + 8 * (st / 4) + 4 * h + (st % 4);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[kb][st], Vs[kv * S::KS + 32 * db + c],
-                                                       o[db], 0, 0, 0);
-        }
+          for (int st = 0; st < 16; ++st) {
+            const int kv = kb0 + 32 * kb + 8 * (st / 4) + 4 * h + (st % 4);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(s[kb][st], Vs[kv * S::KS + 32 * db + c],
+                                                         o[db], 0, 0, 0);
+          }
+      }
   }
 
-  const float l = l_lane + __shfl_xor(l_lane, 32);
-  scale_rows(o, 1.0f / l, slot, c, h);
+  float inv;
+  if constexpr (KW == 1) {
+    inv = 1.0f / (l_lane + __shfl_xor(l_lane, 32));
+  } else {
+    // Merge the key groups of each query row: with M the largest group
+    // maximum, O = sum_g O_g e^(m_g - M) / sum_g l_g e^(m_g - M), summed in
+    // group order.
+    float* red = smem;
+    float* stat_m = smem + S::RED_FLOATS;
+    float* stat_l = stat_m + KW * S::BQ;
+    const float l_w = l_lane + __shfl_xor(l_lane, 32);
+    __syncthreads();  // the tile area is reused below
+    if (h == 0) {
+      stat_m[kg * S::BQ + 32 * qg + c] = m_run;
+      stat_l[kg * S::BQ + 32 * qg + c] = l_w;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < KW; ++g) mx = fmaxf(mx, stat_m[g * S::BQ + 32 * qg + c]);
+    const float m_use = mx == -INFINITY ? 0.0f : mx;
+    float L = 0.0f;
+#pragma unroll
+    for (int g = 0; g < KW; ++g)
+      L += stat_l[g * S::BQ + 32 * qg + c] *
+           __builtin_amdgcn_exp2f((stat_m[g * S::BQ + 32 * qg + c] - m_use) * kLog2e);
+    scale_rows(o, __builtin_amdgcn_exp2f((m_run - m_use) * kLog2e), slot, c, h);
+    if (kg > 0) {
+      float* mine = red + ((kg - 1) * QW + qg) * 32 * DP;
+#pragma unroll
+      for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mine[(db * 16 + j) * 64 + lane] = o[db][j];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KW; ++g) {
+      const float* other = red + ((g - 1) * QW + qg) * 32 * DP;
+#pragma unroll
+      for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] += other[(db * 16 + j) * 64 + lane];
+    }
+    inv = 1.0f / L;
+  }
+  scale_rows(o, inv, slot, c, h);
   float* out = a.out + (size_t)bh * Sq * D;
 #pragma unroll
   for (int db = 0; db < S::ND; ++db) {
@@ -252,16 +324,31 @@ __global__ __launch_bounds__(64 * kSdpaWaves, DP <= 64 ? 2 : 1) void sdpa_kernel
   }
 }
 
-template <int DP>
-hipError_t launch_dp(const SdpaArgs& a, bool mask_vec, hipStream_t s) {
-  const dim3 grid(a.nblocks), block(64 * kSdpaWaves);
+template <int DP, int QW, int KW, int NB>
+hipError_t launch_cfg(SdpaArgs a, bool mask_vec, hipStream_t s) {
+  using S = SdpaShape<DP, QW, KW, NB>;
+  a.qblocks = (a.Sq + S::BQ - 1) / S::BQ;
+  a.nblocks = (int)((int64_t)(a.nblocks) * a.qblocks);  // nblocks carries BH in
+  const dim3 grid(a.nblocks), block(S::NT);
   if (!a.mask)
-    hipLaunchKernelGGL((sdpa_kernel<DP, false, 4>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sdpa_kernel<DP, QW, KW, NB, false, 4>), grid, block, 0, s, a);
   else if (mask_vec)
-    hipLaunchKernelGGL((sdpa_kernel<DP, true, 4>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sdpa_kernel<DP, QW, KW, NB, true, 4>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((sdpa_kernel<DP, true, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((sdpa_kernel<DP, QW, KW, NB, true, 1>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <int DP>
+hipError_t launch_dp(const SdpaArgs& a, int cfg, bool mask_vec, hipStream_t s) {
+  static_assert(kSdpaQW[SDPA_Q4] == 4 && kSdpaKW[SDPA_Q4] == 1 && kSdpaNB[SDPA_Q4] == 2, "");
+  static_assert(kSdpaQW[SDPA_Q2K2] == 2 && kSdpaKW[SDPA_Q2K2] == 2 && kSdpaNB[SDPA_Q2K2] == 1, "");
+  static_assert(kSdpaQW[SDPA_K4] == 1 && kSdpaKW[SDPA_K4] == 4 && kSdpaNB[SDPA_K4] == 1, "");
+  switch (cfg) {
+    case SDPA_Q2K2: return launch_cfg<DP, 2, 2, 1>(a, mask_vec, s);
+    case SDPA_K4: return launch_cfg<DP, 1, 4, 1>(a, mask_vec, s);
+    default: return launch_cfg<DP, 4, 1, 2>(a, mask_vec, s);
+  }
 }
 
 }  // namespace
@@ -277,14 +364,15 @@ hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream) {
   a.Skv = p.Skv;
   a.D = p.D;
   a.scale = p.scale;
-  a.qblocks = (p.Sq + kSdpaBQ - 1) / kSdpaBQ;
-  a.nblocks = p.BH * a.qblocks;
+  a.qblocks = 0;
+  a.nblocks = p.BH;
+  const int cfg = plan_sdpa(p.BH, p.Sq, p.Skv, getenv("BAIM_SDPA"));
   // 16-byte mask loads need rows that start on 16-byte boundaries.
   const bool mask_vec = p.mask && p.Skv % 4 == 0 && ((uintptr_t)p.mask & 15) == 0;
-  if (p.D <= 32) return launch_dp<32>(a, mask_vec, stream);
-  if (p.D <= 64) return launch_dp<64>(a, mask_vec, stream);
-  if (p.D <= 96) return launch_dp<96>(a, mask_vec, stream);
-  return launch_dp<128>(a, mask_vec, stream);
+  if (p.D <= 32) return launch_dp<32>(a, cfg, mask_vec, stream);
+  if (p.D <= 64) return launch_dp<64>(a, cfg, mask_vec, stream);
+  if (p.D <= 96) return launch_dp<96>(a, cfg, mask_vec, stream);
+  return launch_dp<128>(a, cfg, mask_vec, stream);
 }
 
 }  // namespace baim

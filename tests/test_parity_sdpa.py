@@ -85,6 +85,39 @@ def test_sdpa_small_full(B, H, Sq, Skv, D, masked, scale):
                f"sdpa {B}x{H}x{Sq}x{Skv}x{D}")
 
 
+CFG_SHAPES = [
+    # BH, Sq, Skv, D, mask
+    (3, 33, 65, 32, True), (2, 130, 200, 64, False), (2, 70, 129, 64, True),
+    (1, 100, 300, 96, True), (2, 65, 257, 128, False), (1, 5, 1000, 64, True),
+    (2, 40, 31, 128, True),
+]
+
+
+@pytest.mark.parametrize("cfg", ["0", "1", "2"])
+def test_sdpa_forced_block_shapes(cfg, monkeypatch):
+    """Every block shape (query groups x key groups) on ragged sizes, forced
+    through BAIM_SDPA: 128 query rows; 64 rows with two key groups; 32 rows
+    with four key groups merged at the end."""
+    monkeypatch.setenv("BAIM_SDPA", cfg)
+    for i, (BH, Sq, Skv, D, masked) in enumerate(CFG_SHAPES):
+        say(f"BAIM_SDPA={cfg} sdpa_f32 BH={BH} Sq={Sq} Skv={Skv} D={D} mask={masked}")
+        q, k, v = gen((BH, Sq, D), 30 + i), gen((BH, Skv, D), 40 + i), gen((BH, Skv, D), 50 + i)
+        m = gen((BH, Sq, Skv), 60 + i, 2.0) if masked else None
+        if masked:
+            m[:, 1, :] = float("-inf")          # a row with no keys
+            m[:, 2, : Skv // 2] = float("-inf")  # leading keys dropped
+        check_sdpa(run_sdpa(q, k, v, m), oracle.sdpa(q, k, v, m), f"cfg {cfg} shape {i}")
+    # exact case: zero scale, one key kept per row (out = that value row)
+    BH, Sq, Skv, D = 2, 50, 300, 64
+    pick = np.random.default_rng(int(cfg)).integers(0, Skv, size=(BH, Sq))
+    mask = np.full((BH, Sq, Skv), -np.inf, np.float32)
+    for b in range(BH):
+        mask[b, np.arange(Sq), pick[b]] = 0.0
+    q, k, v = gen((BH, Sq, D), 70), gen((BH, Skv, D), 71), gen((BH, Skv, D), 72)
+    out = run_sdpa(q, k, v, torch.from_numpy(mask), 0.0)
+    assert (out == np.stack([v.numpy()[b][pick[b]] for b in range(BH)])).all()
+
+
 @pytest.mark.parametrize("Skv,D", [(64, 64), (100, 32), (333, 128), (8, 96)])
 def test_sdpa_uniform_weights_bitwise(Skv, D):
     """Zero scale and a 0/-inf mask leaving 2^n keys per row: every weight
