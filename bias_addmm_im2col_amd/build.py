@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbaim.so")
-SOURCES = ["api.cpp", "tile_select.cpp", "addmm.hip", "conv2d_gemm.hip", "conv_direct.hip",
+SOURCES = ["api.cpp", "tile_select.cpp", "sdpa_plan.cpp", "addmm.hip", "conv2d_gemm.hip", "conv_direct.hip",
            "sdpa.hip"]
 ARCH = "gfx950"
 

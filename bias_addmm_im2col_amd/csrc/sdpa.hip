@@ -43,7 +43,7 @@
 #include "gemm_core.hpp"
 #include "index_math.hpp"
 #include "launch.hpp"
-#include "tile_select.hpp"
+#include "sdpa_plan.hpp"
 
 namespace baim {
 

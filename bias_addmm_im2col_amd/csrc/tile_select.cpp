@@ -129,24 +129,4 @@ GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K) {
   return make(p.cfg, M, N, K, 1);
 }
 
-int plan_sdpa(int64_t BH, int64_t Sq, int64_t Skv, const char* override_spec) {
-  if (override_spec && override_spec[0] >= '0' && override_spec[0] < '0' + SDPA_NCFG &&
-      override_spec[1] == 0)
-    return override_spec[0] - '0';
-  int best = SDPA_Q4;
-  double best_t = 0.0;
-  for (int cfg = 0; cfg < SDPA_NCFG; ++cfg) {
-    const int64_t bq = 32 * kSdpaQW[cfg], bkv = 32 * kSdpaNB[cfg] * kSdpaKW[cfg];
-    const int64_t blocks = BH * ((Sq + bq - 1) / bq);
-    const int64_t tiles = (Skv + bkv - 1) / bkv;
-    const int64_t rounds = (blocks + kNumCUs - 1) / kNumCUs;
-    const double t = (double)rounds * (double)tiles * (kSdpaNB[cfg] + 0.3);
-    if (cfg == 0 || t < best_t) {
-      best = cfg;
-      best_t = t;
-    }
-  }
-  return best;
-}
-
 }  // namespace baim

@@ -23,3 +23,13 @@ def test_tile_select(tmp_path):
                            os.path.join(csrc, "tile_select.cpp"), "-o", str(exe)])
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout
+
+
+def test_sdpa_plan(tmp_path):
+    exe = tmp_path / "sdpa_plan_check"
+    csrc = os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-Wall", "-I", csrc,
+                           os.path.join(ROOT, "tests", "sdpa_plan_check.cpp"),
+                           os.path.join(csrc, "sdpa_plan.cpp"), "-o", str(exe)])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout
