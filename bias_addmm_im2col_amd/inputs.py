@@ -56,6 +56,7 @@ class ConvCase:
     bias: tuple | None
     seed: int = 0
     groups: int = 1
+    channels_last: bool = False  # x [B,H,W,IC], w [OC,KH,KW,IC], out [B,OH,OW,OC]
     kind: str = field(default="conv", init=False)
 
     def out_hw(self):
@@ -167,6 +168,14 @@ GROUPED_CASES = {c.name: c for c in [
              N(1), N(0.2), N(0.02), groups=256),
 ]}
 
+# Channels-last (NHWC) convs: the 3x3 mid-stage shape and the 3-channel stem.
+NHWC_CASES = {c.name: c for c in [
+    ConvCase("conv3x3_56_s1_nhwc", 4, 256, 56, 56, 256, 3, 3, (1, 1), (1, 1), (1, 1),
+             N(1), N(0.02), N(0.02), channels_last=True),
+    ConvCase("stem_conv7x7_s4_768_nhwc", 1, 3, 768, 768, 128, 7, 7, (4, 4), (3, 3), (1, 1),
+             U01, N(0.05), N(0.02), channels_last=True),
+]}
+
 # Non-causal attention in vision encoders and cross-attention: ViT-B/16 at
 # 224 px (196 patches + class token, 12 heads of 64), a 1024-token encoder
 # with 16 heads of 128, cross-attention from 64 queries to 577 image tokens
@@ -217,8 +226,14 @@ def addmm_inputs(case: AddmmCase):
 
 
 def conv_inputs(case: ConvCase):
-    """(input [B,IC,H,W], weight [OC,IC,KH,KW], bias [OC] or None)."""
+    """(input [B,IC,H,W], weight [OC,IC/groups,KH,KW], bias [OC] or None);
+    channels-last cases draw input [B,H,W,IC] and weight [OC,KH,KW,IC]."""
     g = torch.Generator("cpu").manual_seed(case.seed)
+    if case.channels_last:
+        x = draw((case.B, case.H, case.W, case.IC), case.x, g)
+        w = draw((case.OC, case.KH, case.KW, case.IC // case.groups), case.w, g)
+        b = None if case.bias is None else draw((case.OC,), case.bias, g)
+        return x, w, b
     x = draw((case.B, case.IC, case.H, case.W), case.x, g)
     w = draw((case.OC, case.IC // case.groups, case.KH, case.KW), case.w, g)
     b = None if case.bias is None else draw((case.OC,), case.bias, g)

@@ -18,6 +18,10 @@ marshals numpy arrays.  Definitions followed:
   tiled GEMM" (PR #20873), Solution/Implementation: direct sum over
   (ic, kh, kw) taps at ih = oh*sH - pH + kh*dH (and the W analogue),
   out-of-range taps read 0, per-OC bias, NCHW output.
+* conv2d_nhwc -- the same conv page, Constraints paragraph (the NCHW channel
+  stride is not contiguous, so K cannot be read four at a time): the conv
+  with channels-last tensors, input [B,H,W,IC], weight [OC,KH,KW,IC],
+  output [B,OH,OW,OC], taps summed in (kh, kw, ic) order.
 * sdpa -- "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),
   Problem/Solution: non-causal ``softmax(q @ k^T * scale + mask) @ v`` over
   [B,H,S,D] tensors, optional additive mask [B,H,Sq,Skv], Sq may differ from
@@ -91,6 +95,10 @@ def _load():
     lib.oracle_conv2d_grouped.restype = ctypes.c_int
     lib.oracle_conv2d_grouped_at.argtypes = [_i64] * 14 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
     lib.oracle_conv2d_grouped_at.restype = ctypes.c_int
+    lib.oracle_conv2d_nhwc.argtypes = [_i64] * 13 + [_fp, _fp, _fp, _dp, _dp]
+    lib.oracle_conv2d_nhwc.restype = ctypes.c_int
+    lib.oracle_conv2d_nhwc_at.argtypes = [_i64] * 13 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
+    lib.oracle_conv2d_nhwc_at.restype = ctypes.c_int
     lib.oracle_sdpa.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _dp, _dp]
     lib.oracle_sdpa.restype = ctypes.c_int
     lib.oracle_sdpa_rows.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _i64, _lp, _dp, _dp]
@@ -289,6 +297,52 @@ def conv2d_grouped_at(x, w, bias, stride, padding, dilation, groups, idx) -> Res
     assert rc == 0
     oc = (idx // (OH * OW)) % OC
     bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])
+    return Result(ref, sabs, bb)
+
+
+def _nhwc_args(x, w, stride, padding, dilation):
+    B, H, W, IC = x.shape
+    OC, KH, KW, IC2 = w.shape
+    assert IC == IC2, "weight must be [OC, KH, KW, IC]"
+    (sH, sW), (pH, pW), (dH, dW) = _pair(stride), _pair(padding), _pair(dilation)
+    return (B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW)
+
+
+def conv2d_nhwc(x, w, bias=None, stride=1, padding=0, dilation=1) -> Result:
+    """Full [B,OH,OW,OC] reference of the channels-last conv: x [B,H,W,IC],
+    w [OC,KH,KW,IC], bias [OC]."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _nhwc_args(x, w, stride, padding, dilation)
+    B, OC = a[0], a[4]
+    OH = conv_out_size(a[2], a[5], a[7], a[9], a[11])
+    OW = conv_out_size(a[3], a[6], a[8], a[10], a[12])
+    if OH <= 0 or OW <= 0:
+        raise ValueError("empty conv output")
+    ref = np.empty((B, OH, OW, OC), np.float64)
+    sabs = np.empty((B, OH, OW, OC), np.float64)
+    rc = _load().oracle_conv2d_nhwc(*a, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp),
+                                    _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    bb = np.zeros(OC) if bias is None else np.abs(bias.astype(np.float64))
+    return Result(ref, sabs, np.broadcast_to(bb, ref.shape))
+
+
+def conv2d_nhwc_at(x, w, bias, stride, padding, dilation, idx) -> Result:
+    """Channels-last conv reference at sampled flat NHWC output indices."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _nhwc_args(x, w, stride, padding, dilation)
+    B, OC = a[0], a[4]
+    OH = conv_out_size(a[2], a[5], a[7], a[9], a[11])
+    OW = conv_out_size(a[3], a[6], a[8], a[10], a[12])
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert (idx >= 0).all() and (idx < B * OH * OW * OC).all()
+    n = idx.size
+    ref = np.empty(n, np.float64)
+    sabs = np.empty(n, np.float64)
+    rc = _load().oracle_conv2d_nhwc_at(*a, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp), n,
+                                       _ptr(idx, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[idx % OC])
     return Result(ref, sabs, bb)
 
 

@@ -418,3 +418,73 @@ int oracle_sdpa_rows(int64_t BH, int64_t Sq, int64_t Skv, int64_t D,
   }
   return 0;
 }
+
+/* ---- Channels-last conv2d (NHWC input and output, OHWI weight) ---------
+ * The same convolution as oracle_conv2d (groups == 1) with the tensors laid
+ * out channels-last: input x[b, ih, iw, ic] ([B,H,W,IC]), weight
+ * w[oc, kh, kw, ic] ([OC,KH,KW,IC]) and output out[b, oh, ow, oc]
+ * ([B,OH,OW,OC]).  "et_vk conv2d: route standard (groups==1) conv through
+ * an im2col tiled GEMM", Constraints paragraph: in NCHW the channel stride
+ * is not contiguous, so the GEMM's K dimension cannot be read four at a
+ * time; channels-last makes the input channels, and with K ordered as
+ * (kh, kw, ic) each tap's K run, contiguous.  Taps are summed in
+ * (kh, kw, ic) order; out-of-range taps read 0; bias per output channel. */
+static void conv_one_nhwc(const conv_shape* c, int64_t b, int64_t oh,
+                          int64_t ow, int64_t oc, const float* x,
+                          const float* w, const float* bias, double* ref,
+                          double* sabs) {
+  double acc = 0.0, aabs = 0.0;
+  for (int64_t kh = 0; kh < c->KH; ++kh) {
+    int64_t ih = oh * c->sH - c->pH + kh * c->dH;
+    if (ih < 0 || ih >= c->H) continue;
+    for (int64_t kw = 0; kw < c->KW; ++kw) {
+      int64_t iw = ow * c->sW - c->pW + kw * c->dW;
+      if (iw < 0 || iw >= c->W) continue;
+      for (int64_t ic = 0; ic < c->IC; ++ic) {
+        double p = (double)x[((b * c->H + ih) * c->W + iw) * c->IC + ic] *
+                   (double)w[((oc * c->KH + kh) * c->KW + kw) * c->IC + ic];
+        acc += p;
+        aabs += fabs(p);
+      }
+    }
+  }
+  *ref = (bias ? (double)bias[oc] : 0.0) + acc;
+  *sabs = aabs;
+}
+
+int oracle_conv2d_nhwc(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
+                       int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                       int64_t pH, int64_t pW, int64_t dH, int64_t dW,
+                       const float* x, const float* w, const float* bias,
+                       double* ref, double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0) return -1;
+#pragma omp parallel for collapse(3) schedule(static)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t oh = 0; oh < c.OH; ++oh)
+      for (int64_t ow = 0; ow < c.OW; ++ow)
+        for (int64_t oc = 0; oc < OC; ++oc) {
+          int64_t o = ((b * c.OH + oh) * c.OW + ow) * OC + oc;
+          conv_one_nhwc(&c, b, oh, ow, oc, x, w, bias, &ref[o], &sabs[o]);
+        }
+  return 0;
+}
+
+/* Sampled channels-last conv at flat NHWC output indices idx[s]. */
+int oracle_conv2d_nhwc_at(int64_t B, int64_t IC, int64_t H, int64_t W,
+                          int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                          int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                          int64_t dW, const float* x, const float* w,
+                          const float* bias, int64_t n, const int64_t* idx,
+                          double* ref, double* sabs) {
+  conv_shape c = make_shape(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW);
+  if (c.OH <= 0 || c.OW <= 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < n; ++s) {
+    int64_t o = idx[s];
+    int64_t oc = o % OC, ow = (o / OC) % c.OW, oh = (o / (OC * c.OW)) % c.OH;
+    int64_t b = o / (OC * c.OW * c.OH);
+    conv_one_nhwc(&c, b, oh, ow, oc, x, w, bias, &ref[s], &sabs[s]);
+  }
+  return 0;
+}

@@ -656,3 +656,57 @@ def test_sdpa_error_scale_covers_an_fp32_evaluation():
     bound = oracle.sdpa_tolerance(r)
     assert (np.abs(f32 - r.ref) <= 0.25 * bound).all()
     assert (r.err > 0).all()
+
+
+# ------------------------------------------------------- channels-last conv
+# The conv page's Constraints paragraph: NCHW keeps the GEMM's K dimension
+# strided; channels-last (input [B,H,W,IC], weight [OC,KH,KW,IC], output
+# [B,OH,OW,OC]) makes it contiguous.  Same convolution, other layout.
+
+def _nchw(t):
+    return np.ascontiguousarray(np.transpose(t, (0, 3, 1, 2)))
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil", [
+    (2, 4, 9, 7, 5, 3, 3, 1, 1, 1), (1, 3, 12, 11, 6, 7, 7, 4, 3, 1),
+    (2, 8, 10, 10, 4, 3, 2, (2, 1), (1, 0), (2, 3)), (1, 5, 6, 6, 3, 1, 1, 1, 0, 1)])
+def test_nhwc_conv_is_the_nchw_conv_in_another_layout(B, IC, H, W, OC, KH, KW, stride, pad, dil):
+    x = rand32((B, H, W, IC), 140)
+    w = rand32((OC, KH, KW, IC), 141)
+    b = rand32((OC,), 142)
+    r = oracle.conv2d_nhwc(x, w, b, stride, pad, dil)
+    n = oracle.conv2d(_nchw(x), _nchw(w), b, stride, pad, dil)
+    np.testing.assert_allclose(r.ref, np.transpose(n.ref, (0, 2, 3, 1)), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(r.sabs, np.transpose(n.sabs, (0, 2, 3, 1)), rtol=1e-13, atol=0)
+    t = F.conv2d(torch.from_numpy(_nchw(x)).double(), torch.from_numpy(_nchw(w)).double(),
+                 torch.from_numpy(b).double(), stride, pad, dil).permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+
+
+def test_nhwc_conv_1x1_is_a_matmul():
+    x, w, b = rand32((2, 5, 4, 6), 143), rand32((7, 1, 1, 6), 144), rand32((7,), 145)
+    r = oracle.conv2d_nhwc(x, w, b)
+    want = x.reshape(-1, 6).astype(np.float64) @ w.reshape(7, 6).T.astype(np.float64) + b
+    np.testing.assert_allclose(r.ref.reshape(-1, 7), want, rtol=1e-14, atol=1e-14)
+
+
+def test_nhwc_conv_delta_kernel_shifts_input():
+    # w[oc, kh0, kw0, ic] = delta(oc, ic): out[b, oh, ow, c] = x[b, oh*s - p + kh0*d, ..., c]
+    C, KH, KW, kh0, kw0 = 4, 3, 3, 2, 0
+    x = rand32((2, 8, 9, C), 146)
+    w = np.zeros((C, KH, KW, C), np.float32)
+    for c in range(C):
+        w[c, kh0, kw0, c] = 1.0
+    r = oracle.conv2d_nhwc(x, w, None, 1, 1, 2)
+    xp = np.pad(x.astype(np.float64), ((0, 0), (1, 1), (1, 1), (0, 0)))
+    OH, OW = r.ref.shape[1:3]
+    want = xp[:, kh0 * 2: kh0 * 2 + OH, kw0 * 2: kw0 * 2 + OW, :]
+    assert (r.ref == want).all()
+
+
+def test_sampled_nhwc_conv_equals_full():
+    x, w, b = rand32((2, 7, 6, 4), 147), rand32((5, 3, 3, 4), 148), rand32((5,), 149)
+    full = oracle.conv2d_nhwc(x, w, b, 2, 1, 1)
+    idx = np.array([0, 3, 17, full.ref.size - 1, full.ref.size // 2])
+    s = oracle.conv2d_nhwc_at(x, w, b, 2, 1, 1, idx)
+    assert (s.ref == full.ref.reshape(-1)[idx]).all() and (s.sabs == full.sabs.reshape(-1)[idx]).all()

@@ -44,6 +44,12 @@ MUTANTS = {
     "sdpa_not_normalised": ("o += exp(s[j] - m) / l *", "o += exp(s[j] - m) *"),
     "sdpa_value_transposed": ("* (double)v[(bh * Skv + j) * D + d];", "* (double)v[(bh * D + d) * Skv + j];"),
     "sdpa_scale_applied_after_mask": ("s[j] = (double)scale * dot + mk;", "s[j] = (double)scale * (dot + mk);"),
+    "nhwc_input_read_as_nchw": ("x[((b * c->H + ih) * c->W + iw) * c->IC + ic]",
+                                "x[((b * c->IC + ic) * c->H + ih) * c->W + iw]"),
+    "nhwc_weight_read_as_oihw": ("w[((oc * c->KH + kh) * c->KW + kw) * c->IC + ic]",
+                                 "w[((oc * c->IC + ic) * c->KH + kh) * c->KW + kw]"),
+    "nhwc_output_written_as_nchw": ("int64_t o = ((b * c.OH + oh) * c.OW + ow) * OC + oc;",
+                                    "int64_t o = ((b * OC + oc) * c.OH + oh) * c.OW + ow;"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
 }
