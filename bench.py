@@ -93,7 +93,7 @@ class Case:
     def __init__(self, name, torch, baim, I):
         self.name = name
         c = (I.CASES.get(name) or I.LINEAR_CASES.get(name) or I.GROUPED_CASES.get(name)
-             or I.SDPA_CASES[name])
+             or I.NHWC_CASES.get(name) or I.SDPA_CASES[name])
         self.c = c
         self.op = c.kind
         self.flops = c.flops
@@ -109,10 +109,13 @@ class Case:
             self.bytes = 4 * sum(t.numel() for t in (q, k, v, self.out) + ((m,) if m is not None else ()))
             return
         M, N, K = (c.M, c.N, c.K) if c.kind != "conv" else c.gemm_mnk
+        if c.kind == "conv" and c.channels_last:  # out[B*OH*OW, OC]: the linear-shaped GEMM
+            M, N = N, M
         p = baim.gemm_plan(M, N, K)
         self.plan = p
         # one kernel instance per (op, block tile, waves, wave groups, K split)
-        self.kernel = (f"baim::{'conv2d_gemm_kernel' if c.kind == 'conv' else 'addmm_kernel'}"
+        kname = "conv2d_gemm_kernel" if c.kind == "conv" and not c.channels_last else "addmm_kernel"
+        self.kernel = (f"baim::{kname}"
                        f"<Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
                        f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else "")
                        + (f" stream {p['stream_blocks']}" if p['stream_blocks'] > 0 else ""))
@@ -140,6 +143,11 @@ class Case:
             self.K = c.IC * c.KH * c.KW
             self.run = lambda: baim.conv2d_gemm_f32(self.out, self.x, self.w, self.bias,
                                                     c.stride, c.padding, c.dilation, c.groups)
+            if c.channels_last:
+                self.out = torch.empty((c.B, OH, OW, c.OC), dtype=torch.float32, device="cuda")
+                self.kernel += " (im2col NHWC)"
+                self.run = lambda: baim.conv2d_nhwc_f32(self.out, self.x, self.w, self.bias,
+                                                        c.stride, c.padding, c.dilation)
             self.bytes = 4 * (x.numel() + w.numel() + bias.numel() + self.out.numel())
             if c.groups > 1 and not (c.OC // c.groups >= 32 and c.IC // c.groups * c.KH * c.KW >= 32):
                 self.kernel = "baim::conv_direct_kernel"
@@ -147,12 +155,13 @@ class Case:
 
 def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
     """Ops beyond the step's workload (linear with weight [N,K], grouped and
-    depthwise conv, attention), timed the same way but reported separately:
+    depthwise conv, channels-last conv, attention), timed the same way but reported separately:
     they are not part of `value`.  Each case
     first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
     switch to new buffers)."""
     rows = []
-    for name in list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.SDPA_CASES):
+    for name in (list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.NHWC_CASES)
+                 + list(I.SDPA_CASES)):
         cs = Case(name, torch, baim, I)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < warmup_s:

@@ -15,12 +15,17 @@ arguments and allocates outputs with torch:
   GEMM", Solution/Implementation), grouped convs as one such GEMM per group
   or, when the groups are small (e.g. depthwise), on a direct kernel.
 
+* ``conv2d_nhwc(input, weight, bias=None, stride=1, padding=0, dilation=1)``
+  -- the same conv (groups == 1) on channels-last tensors: input [B,H,W,IC],
+  weight [OC,KH,KW,IC], output [B,OH,OW,OC]; the implicit im2col then reads
+  K (a tap's input channels) contiguously.
 * ``sdpa(q, k, v, attn_mask=None, scale=None)`` -- non-causal attention
   ``softmax(q @ k^T * scale + attn_mask) @ v`` over [..., S, D] tensors
   ("[ExecuTorch][WebGPU] Add optimized SDPA op", Problem/Solution), in one
   fused pass.
 
-``addmm_f32``, ``linear_f32``, ``conv2d_gemm_f32`` and ``sdpa_f32`` are the
+``addmm_f32``, ``linear_f32``, ``conv2d_gemm_f32``, ``conv2d_nhwc_f32`` and
+``sdpa_f32`` are the
 same-named entry points of the C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
 on the same ROCm device; work is enqueued on the current torch stream.
 """
@@ -28,8 +33,8 @@ from __future__ import annotations
 
 from . import _capi
 
-__all__ = ["addmm", "linear", "conv2d", "sdpa", "addmm_f32", "linear_f32", "conv2d_gemm_f32",
-           "sdpa_f32", "conv2d_out_hw", "gemm_plan",
+__all__ = ["addmm", "linear", "conv2d", "conv2d_nhwc", "sdpa", "addmm_f32", "linear_f32",
+           "conv2d_gemm_f32", "conv2d_nhwc_f32", "sdpa_f32", "conv2d_out_hw", "gemm_plan",
            "BaimError", "library_path"]
 
 
@@ -301,3 +306,51 @@ def sdpa(q, k, v, attn_mask=None, scale=None):
     q = _dev_f32(q, "q")
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     return sdpa_f32(out, q, k, v, attn_mask, scale)
+
+
+def conv2d_nhwc_f32(out, input, weight, bias=None, stride=1, padding=0, dilation=1):
+    """Channels-last conv2d written into ``out`` [B, OH, OW, OC]: input
+    [B, H, W, IC], weight [OC, KH, KW, IC], bias [OC] or None."""
+    import torch
+    out, x, w = _dev_f32(out, "out"), _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4 or out.dim() != 4:
+        raise ValueError("input, weight and out must be 4-D (NHWC / OHWI)")
+    B, H, W, IC = x.shape
+    OC, KH, KW, IC2 = w.shape
+    if IC2 != IC:
+        raise ValueError(f"weight must be [OC, KH, KW, IC={IC}], got {list(w.shape)}")
+    (sH, sW), (pH, pW), (dH, dW) = (_pair(stride, "stride"), _pair(padding, "padding"),
+                                    _pair(dilation, "dilation"))
+    bias_ptr = None
+    devs = {out.device, x.device, w.device}
+    if bias is not None:
+        bias = _dev_f32(bias, "bias")
+        if tuple(bias.shape) != (OC,):
+            raise ValueError(f"bias must be [{OC}]")
+        bias_ptr = bias.data_ptr()
+        devs.add(bias.device)
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    st, OH, OW = _capi.conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW)
+    _check(st)
+    if tuple(out.shape) != (B, OH, OW, OC):
+        raise ValueError(f"out must be [{B}, {OH}, {OW}, {OC}], got {list(out.shape)}")
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.conv2d_nhwc_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
+                                   B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, _stream(dev))
+    _check(st)
+    return out
+
+
+def conv2d_nhwc(input, weight, bias=None, stride=1, padding=0, dilation=1):
+    """Channels-last conv2d (input [B,H,W,IC], weight [OC,KH,KW,IC]) as a new
+    [B, OH, OW, OC] tensor."""
+    import torch
+    x, w = _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("input and weight must be 4-D")
+    OH, OW = conv2d_out_hw(x.shape[1], x.shape[2], w.shape[1], w.shape[2], stride, padding,
+                           dilation)
+    out = torch.empty((x.shape[0], OH, OW, w.shape[0]), dtype=torch.float32, device=x.device)
+    return conv2d_nhwc_f32(out, x, w, bias, stride, padding, dilation)

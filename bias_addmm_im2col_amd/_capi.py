@@ -25,7 +25,8 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/baim.h declares.
-EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "sdpa_f32", "baim_conv2d_out_hw",
+EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32", "sdpa_f32",
+           "baim_conv2d_out_hw",
            "baim_gemm_plan", "baim_last_error", "baim_version")
 
 _lib = None
@@ -50,6 +51,8 @@ def lib():
     L.linear_f32.restype = ctypes.c_int
     L.conv2d_gemm_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 14 + [_vp]
     L.conv2d_gemm_f32.restype = ctypes.c_int
+    L.conv2d_nhwc_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 13 + [_vp]
+    L.conv2d_nhwc_f32.restype = ctypes.c_int
     L.sdpa_f32.argtypes = [_vp] * 5 + [_i64] * 4 + [ctypes.POINTER(ctypes.c_float), _vp]
     L.sdpa_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
@@ -74,6 +77,12 @@ def addmm_f32(out, self, self_2d, mat1, mat2, M, N, K, beta, alpha, stream) -> i
 
 def linear_f32(out, x, w, bias, M, N, K, stream) -> int:
     return lib().linear_f32(out, x, w, bias, M, N, K, stream)
+
+
+def conv2d_nhwc_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
+                    stream) -> int:
+    return lib().conv2d_nhwc_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH,
+                                 dW, stream)
 
 
 def sdpa_f32(out, q, k, v, mask, BH, Sq, Skv, D, scale, stream) -> int:

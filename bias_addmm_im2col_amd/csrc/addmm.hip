@@ -6,6 +6,10 @@
 // linear, out = x @ weight^T + bias with weight [N,K] (the page's
 // linear_fp32 reads that transposed weight), when instantiated with WNK:
 // the weight's K-contiguous rows load straight into the transposed B tile.
+// With WNK and AK = A_NHWC it computes the channels-last conv: the A tile is
+// then gathered from the NHWC input as rows of the implicit im2col matrix
+// (im2col_nhwc.hpp), the weight [OC,KH,KW,IC] is the [N,K] B operand and
+// the bias is self [N].
 //
 // Work split (see gemm_core.hpp): one tile per block; or K slices; or
 // stream pieces.  A tile cut into exactly two pieces is combined without a
@@ -20,6 +24,7 @@
 #include <type_traits>
 
 #include "gemm_core.hpp"
+#include "im2col_nhwc.hpp"
 #include "launch.hpp"
 #include "tile_select.hpp"
 
@@ -34,15 +39,22 @@ struct AddmmArgs {
   int self_mode;  // 0: beta == 0 (self not read); 1: self [N]; 2: self [M,N]
   float beta, alpha;
   Sched sched;
+  NhwcGeom g;  // A_NHWC only
 };
 
-template <class T, int VA, int VB, bool WNK>
+// Where the A tile comes from.
+enum { A_ROWS = 0, A_NHWC = 1 };
+
+template <class T, int VA, int VB, bool WNK, int AK>
 __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int m0, int n0, int tb,
                                    int te, int epi) {
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
-  RowTileLoader<T, VA> al;
-  al.init(p.A, m0, p.M, p.K);
+  typename std::conditional<AK == A_NHWC, NhwcRowLoader<T, VA>, RowTileLoader<T, VA>>::type al;
+  if constexpr (AK == A_NHWC)
+    al.init(p.A, p.g, m0, p.M, p.K);
+  else
+    al.init(p.A, m0, p.M, p.K);
   typename std::conditional<WNK, KRowLoader<T, VB, T::BN, true>, ColTileLoader<T, VB>>::type bl;
   bl.init(p.B, n0, p.N, p.K);
   Accum<T> acc;
@@ -115,11 +127,11 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
   }
 }
 
-template <class T, int VA, int VB, int MODE, bool WNK>
+template <class T, int VA, int VB, int MODE, bool WNK, int AK>
 __global__ __launch_bounds__(T::NT) void addmm_kernel(AddmmArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
   for_each_piece<MODE>(p.sched, T::BM, T::BN, [&](int m0, int n0, int tb, int te, int epi) __attribute__((always_inline)) {
-    addmm_piece<T, VA, VB, WNK>(p, smem, m0, n0, tb, te, epi);
+    addmm_piece<T, VA, VB, WNK, AK>(p, smem, m0, n0, tb, te, epi);
   });
 }
 
@@ -177,26 +189,30 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
                   same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
               "tile table out of sync with the compiled tiles");
 
-template <class T, int VA, int VB, int MODE, bool WNK = false>
+template <class T, int VA, int VB, int MODE, bool WNK = false, int AK = A_ROWS>
 static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE, WNK>), dim3(nblocks), dim3(T::NT), 0, s, a);
+  hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE, WNK, AK>), dim3(nblocks), dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
 // Stream pieces are compiled for aligned operands only (the launcher falls
 // back to one tile per block otherwise).
 // Linear (WNK) is compiled with 16-byte loads of both operands or with
-// 4-byte loads of both (its x and weight rows share K).
-template <class T, int CFG, int MODE, bool WNK>
+// 4-byte loads of both (its x and weight rows share K); so is the
+// channels-last conv.
+template <class T, int CFG, int MODE, bool WNK, int AK>
 static hipError_t launch_vec(const AddmmArgs& a, int nblocks, bool va, bool vb, hipStream_t s) {
   if constexpr (MODE == MODE_STREAM) {
-    if constexpr (kTileStream[CFG]) return launch_t<T, 4, 4, MODE_STREAM, WNK>(a, nblocks, s);
+    if constexpr (kTileStream[CFG]) return launch_t<T, 4, 4, MODE_STREAM, WNK, AK>(a, nblocks, s);
     return hipErrorInvalidValue;  // never planned
   } else if constexpr (MODE == MODE_SLICES && !kTileSlices[CFG]) {
     return hipErrorInvalidValue;  // never planned
   } else if constexpr (WNK) {
-    if (va && vb) return launch_t<T, 4, 4, MODE, true>(a, nblocks, s);
-    return launch_t<T, 1, 1, MODE, true>(a, nblocks, s);
+    if (va && vb) return launch_t<T, 4, 4, MODE, true, AK>(a, nblocks, s);
+    // The 4-byte channels-last gather does not fit the 16-wave 128x128
+    // tile's registers; the launcher never plans it.
+    if constexpr (AK == A_NHWC && CFG == TILE_128x128_K2) return hipErrorInvalidValue;
+    else return launch_t<T, 1, 1, MODE, true, AK>(a, nblocks, s);
   } else {
     if (va && vb) return launch_t<T, 4, 4, MODE>(a, nblocks, s);
     if (va) return launch_t<T, 4, 1, MODE>(a, nblocks, s);
@@ -205,37 +221,37 @@ static hipError_t launch_vec(const AddmmArgs& a, int nblocks, bool va, bool vb, 
   }
 }
 
-template <int MODE, bool WNK>
+template <int MODE, bool WNK, int AK = A_ROWS>
 static hipError_t launch_cfg(int cfg, const AddmmArgs& a, int nblocks, bool va, bool vb,
                              hipStream_t s) {
   switch (cfg) {
     case TILE_128x64:
-      return launch_vec<T128x64, TILE_128x64, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64, TILE_128x64, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_64x128:
-      return launch_vec<T64x128, TILE_64x128, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T64x128, TILE_64x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_64x64:
-      return launch_vec<T64x64, TILE_64x64, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64, TILE_64x64, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_128x128_K2:
-      return launch_vec<T128x128K2, TILE_128x128_K2, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128K2, TILE_128x128_K2, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_128x64_K2:
-      return launch_vec<T128x64K2, TILE_128x64_K2, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T128x64K2, TILE_128x64_K2, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_64x64_K2:
-      return launch_vec<T64x64K2, TILE_64x64_K2, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K2, TILE_64x64_K2, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_64x64_K4:
-      return launch_vec<T64x64K4, TILE_64x64_K4, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T64x64K4, TILE_64x64_K4, MODE, WNK, AK>(a, nblocks, va, vb, s);
     default:
-      return launch_vec<T128x128, TILE_128x128, MODE, WNK>(a, nblocks, va, vb, s);
+      return launch_vec<T128x128, TILE_128x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
   }
 }
 
-hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
-  // 16-byte vector loads need the contiguous dim (K for mat1 and for a
-  // [N,K] weight, N for mat2 [K,N]) divisible by 4 and aligned bases.
-  const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
-  const bool vb = (p.weight_nk ? p.K : p.N) % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
+// Plan, initialise out if the plan splits tiles, and launch.
+template <int AK>
+static hipError_t launch_gemm(const AddmmProblem& p, AddmmArgs& a, bool va, bool vb,
+                              hipStream_t stream) {
   GemmPlan plan = plan_gemm(p.M, p.N, p.K, getenv("BAIM_TILE"));
   if (plan.mode == MODE_STREAM && !(va && vb)) plan = plan_tiles_only(plan, p.M, p.N, p.K);
-  AddmmArgs a;
+  if (AK == A_NHWC && !(va && vb) && plan.cfg == TILE_128x128_K2)
+    plan = plan_gemm(p.M, p.N, p.K, "0");  // same block tile, 8 waves
   a.out = p.out;
   a.self = p.self;
   a.A = p.mat1;
@@ -257,24 +273,75 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (p.weight_nk) {
+  if (AK == A_NHWC || p.weight_nk) {
     switch (plan.mode) {
       case MODE_SLICES:
-        return launch_cfg<MODE_SLICES, true>(plan.cfg, a, nblocks, va, vb, stream);
+        return launch_cfg<MODE_SLICES, true, AK>(plan.cfg, a, nblocks, va, vb, stream);
       case MODE_STREAM:
-        return launch_cfg<MODE_STREAM, true>(plan.cfg, a, nblocks, va, vb, stream);
+        return launch_cfg<MODE_STREAM, true, AK>(plan.cfg, a, nblocks, va, vb, stream);
       default:
-        return launch_cfg<MODE_TILE, true>(plan.cfg, a, nblocks, va, vb, stream);
+        return launch_cfg<MODE_TILE, true, AK>(plan.cfg, a, nblocks, va, vb, stream);
     }
   }
-  switch (plan.mode) {
-    case MODE_SLICES:
-      return launch_cfg<MODE_SLICES, false>(plan.cfg, a, nblocks, va, vb, stream);
-    case MODE_STREAM:
-      return launch_cfg<MODE_STREAM, false>(plan.cfg, a, nblocks, va, vb, stream);
-    default:
-      return launch_cfg<MODE_TILE, false>(plan.cfg, a, nblocks, va, vb, stream);
+  if constexpr (AK == A_ROWS) {
+    switch (plan.mode) {
+      case MODE_SLICES:
+        return launch_cfg<MODE_SLICES, false>(plan.cfg, a, nblocks, va, vb, stream);
+      case MODE_STREAM:
+        return launch_cfg<MODE_STREAM, false>(plan.cfg, a, nblocks, va, vb, stream);
+      default:
+        return launch_cfg<MODE_TILE, false>(plan.cfg, a, nblocks, va, vb, stream);
+    }
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
+  // 16-byte vector loads need the contiguous dim (K for mat1 and for a
+  // [N,K] weight, N for mat2 [K,N]) divisible by 4 and aligned bases.
+  const bool va = p.K % 4 == 0 && ((uintptr_t)p.mat1 & 15) == 0;
+  const bool vb = (p.weight_nk ? p.K : p.N) % 4 == 0 && ((uintptr_t)p.mat2 & 15) == 0;
+  AddmmArgs a{};
+  return launch_gemm<A_ROWS>(p, a, va, vb, stream);
+}
+
+hipError_t launch_conv2d_nhwc(const ConvProblem& q, hipStream_t stream) {
+  // out[B*OH*OW, OC] = im2col_nhwc(x)[B*OH*OW, KH*KW*IC] @ w[OC, KH*KW*IC]^T + bias
+  AddmmProblem p;
+  p.out = q.out;
+  p.self = q.bias;
+  p.mat1 = q.x;
+  p.mat2 = q.w;
+  p.weight_nk = true;
+  p.M = q.B * q.OH * q.OW;
+  p.N = q.OC;
+  p.K = q.KH * q.KW * q.IC;
+  p.self_mode = q.bias ? 1 : 0;
+  p.beta = 1.0f;
+  p.alpha = 1.0f;
+  AddmmArgs a{};
+  a.g.H = q.H;
+  a.g.W = q.W;
+  a.g.IC = q.IC;
+  a.g.KW = q.KW;
+  a.g.OH = q.OH;
+  a.g.OW = q.OW;
+  a.g.sH = q.sH;
+  a.g.sW = q.sW;
+  a.g.pH = q.pH;
+  a.g.pW = q.pW;
+  a.g.dH = q.dH;
+  a.g.dW = q.dW;
+  a.g.x_elems = q.B * q.H * q.W * q.IC;
+  a.g.div_ow = make_fastdiv((uint32_t)q.OW);
+  a.g.div_oh = make_fastdiv((uint32_t)q.OH);
+  a.g.div_ic = make_fastdiv((uint32_t)q.IC);
+  a.g.div_kw = make_fastdiv((uint32_t)q.KW);
+  // 16-byte gathers need whole taps of four channels and an aligned input;
+  // the weight rows are K = KH*KW*IC long.
+  const bool va = q.IC % 4 == 0 && ((uintptr_t)q.x & 15) == 0;
+  const bool vb = p.K % 4 == 0 && ((uintptr_t)q.w & 15) == 0;
+  return launch_gemm<A_NHWC>(p, a, va, vb, stream);
 }
 
 }  // namespace baim

@@ -48,5 +48,8 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);
+// Channels-last conv (groups == 1): x [B,H,W,IC], w [OC,KH,KW,IC],
+// out [B,OH,OW,OC]; the addmm kernels with an im2col A operand.
+hipError_t launch_conv2d_nhwc(const ConvProblem& p, hipStream_t stream);
 
 }  // namespace baim

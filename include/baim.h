@@ -130,6 +130,36 @@ baim_status conv2d_gemm_f32(float* out, const float* input,
                             int64_t groups, void* stream);
 
 /*
+ * conv2d_nhwc_f32: the conv of conv2d_gemm_f32 (groups == 1) on
+ * channels-last tensors.
+ *
+ * From "et_vk conv2d: route standard (groups==1) conv through an im2col
+ * tiled GEMM", Solution and Constraints paragraphs: the conv is the GEMM of
+ * the weight with the implicit im2col of the input, and with NCHW the K
+ * dimension is strided, so it cannot be read four at a time.  Here the
+ * tensors are channels-last and K is ordered (kh, kw, ic), so each tap's
+ * input channels are contiguous: out[m, oc] = sum_kk A[m, kk] * w[oc, kk]
+ * + bias[oc], m = (b*OH + oh)*OW + ow, A the implicit im2col rows.  Same
+ * padding, stride, dilation and output-size rules as conv2d_gemm_f32.
+ *
+ *  out     [B,OH,OW,OC] fp32 (NHWC), written in full.
+ *  input   [B,H,W,IC] fp32 (NHWC).
+ *  weight  [OC,KH,KW,IC] fp32 (OHWI: a K-contiguous [OC, KH*KW*IC] matrix).
+ *  bias    [OC] fp32, or NULL for no bias.
+ *  B, IC, OC >= 1; KH, KW >= 1; sH, sW, dH, dW >= 1; pH, pW >= 0
+ *          (BAIM_ERR_SHAPE otherwise, or if the output would be empty).
+ *  stream  hipStream_t or NULL.
+ * Limits: every tensor below 2^31 elements, the input below 2^29,
+ * KH*KW*IC below 2^21, OC below 2^23 (BAIM_ERR_TOO_LARGE).
+ */
+baim_status conv2d_nhwc_f32(float* out, const float* input,
+                            const float* weight, const float* bias, int64_t B,
+                            int64_t IC, int64_t H, int64_t W, int64_t OC,
+                            int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                            int64_t pH, int64_t pW, int64_t dH, int64_t dW,
+                            void* stream);
+
+/*
  * sdpa_f32: out = softmax(q @ k^T * scale + attn_mask) @ v, non-causal.
  *
  * Defined by "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),

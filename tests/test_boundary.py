@@ -179,6 +179,32 @@ def test_gemm_plan(lib, monkeypatch):
     assert (p["bm"], p["bn"], p["splits"], p["stream_blocks"]) == (128, 64, 1, 256)
 
 
+def conv_nhwc(out=O, x=A, w=Bp, bias=S, B=1, IC=3, H=8, W=8, OC=4, KH=3, KW=3, sH=1, sW=1,
+              pH=1, pW=1, dH=1, dW=1):
+    return _capi.conv2d_nhwc_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH,
+                                 dW, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), _capi.BAIM_ERR_SHAPE),
+    (dict(IC=0), _capi.BAIM_ERR_SHAPE),
+    (dict(sH=0), _capi.BAIM_ERR_SHAPE),
+    (dict(pW=-1), _capi.BAIM_ERR_SHAPE),
+    (dict(KH=20), _capi.BAIM_ERR_SHAPE),                   # empty output
+    (dict(out=None), _capi.BAIM_ERR_NULL),
+    (dict(w=None), _capi.BAIM_ERR_NULL),
+    (dict(B=1, H=1 << 14, W=1 << 13, IC=4), _capi.BAIM_ERR_TOO_LARGE),   # input 2^29
+    (dict(IC=1 << 18, KH=3, KW=3), _capi.BAIM_ERR_TOO_LARGE),            # K >= 2^21
+    (dict(OC=1 << 23, H=1, W=1, KH=1, KW=1, pH=0, pW=0), _capi.BAIM_ERR_TOO_LARGE),
+    (dict(out=A + 8), _capi.BAIM_ERR_ALIAS),
+    (dict(out=S - 4), _capi.BAIM_ERR_ALIAS),
+])
+def test_conv_nhwc_rejects(lib, kw, status):
+    st = conv_nhwc(**kw)
+    assert st == status, (st, _capi.last_error())
+    assert _capi.last_error()
+
+
 M5 = 5 * P  # fake mask address
 
 
