@@ -97,6 +97,43 @@ class LinearCase:
 
 
 @dataclass(frozen=True)
+class ConvTCase:
+    """Transposed conv: x [B,IC,H,W], weight [IC,OC,KH,KW], bias [OC]."""
+    name: str
+    B: int
+    IC: int
+    H: int
+    W: int
+    OC: int
+    KH: int
+    KW: int
+    stride: tuple
+    padding: tuple
+    dilation: tuple
+    output_padding: tuple
+    x: tuple
+    w: tuple
+    bias: tuple | None
+    seed: int = 0
+    kind: str = field(default="convt", init=False)
+
+    def out_hw(self):
+        """(H-1)*s - 2p + d(k-1) + output_padding + 1 per axis."""
+        def one(n, k, s, p, d, op):
+            return (n - 1) * s - 2 * p + d * (k - 1) + op + 1
+        return (one(self.H, self.KH, self.stride[0], self.padding[0], self.dilation[0],
+                    self.output_padding[0]),
+                one(self.W, self.KW, self.stride[1], self.padding[1], self.dilation[1],
+                    self.output_padding[1]))
+
+    @property
+    def flops(self) -> int:
+        """Every input element meets every (oc, kh, kw): 2*B*IC*H*W*OC*KH*KW
+        (taps that fall outside the output are few and not subtracted)."""
+        return 2 * self.B * self.IC * self.H * self.W * self.OC * self.KH * self.KW
+
+
+@dataclass(frozen=True)
 class SdpaCase:
     """Non-causal attention: q [B,H,Sq,D], k and v [B,H,Skv,D], optional
     additive mask [B,H,Sq,Skv].  ``key_pad`` gives each batch entry b a
@@ -174,6 +211,16 @@ NHWC_CASES = {c.name: c for c in [
              N(1), N(0.02), N(0.02), channels_last=True),
     ConvCase("stem_conv7x7_s4_768_nhwc", 1, 3, 768, 768, 128, 7, 7, (4, 4), (3, 3), (1, 1),
              U01, N(0.05), N(0.02), channels_last=True),
+]}
+
+# Transposed convs of decoders: a 4x4 / stride-2 2x upsampling (256 -> 128
+# channels, 28 -> 56) and the 2x2 / stride-2 upscaling of a mask decoder
+# (256 -> 64 channels, 64 -> 128).
+CONVT_CASES = {c.name: c for c in [
+    ConvTCase("convt4x4_s2_28_to_56", 4, 256, 28, 28, 128, 4, 4, (2, 2), (1, 1), (1, 1), (0, 0),
+              N(1), N(0.02), N(0.02)),
+    ConvTCase("convt2x2_s2_64_to_128", 4, 256, 64, 64, 64, 2, 2, (2, 2), (0, 0), (1, 1), (0, 0),
+              N(1), N(0.05), N(0.02)),
 ]}
 
 # Non-causal attention in vision encoders and cross-attention: ViT-B/16 at
@@ -266,7 +313,18 @@ def sdpa_inputs(case: SdpaCase):
     return q, k, v, mask
 
 
+def convt_inputs(case: ConvTCase):
+    """(input [B,IC,H,W], weight [IC,OC,KH,KW], bias [OC] or None)."""
+    g = torch.Generator("cpu").manual_seed(case.seed)
+    x = draw((case.B, case.IC, case.H, case.W), case.x, g)
+    w = draw((case.IC, case.OC, case.KH, case.KW), case.w, g)
+    b = None if case.bias is None else draw((case.OC,), case.bias, g)
+    return x, w, b
+
+
 def inputs(case):
+    if case.kind == "convt":
+        return convt_inputs(case)
     if case.kind == "sdpa":
         return sdpa_inputs(case)
     if case.kind == "addmm":

@@ -22,6 +22,10 @@ marshals numpy arrays.  Definitions followed:
   stride is not contiguous, so K cannot be read four at a time): the conv
   with channels-last tensors, input [B,H,W,IC], weight [OC,KH,KW,IC],
   output [B,OH,OW,OC], taps summed in (kh, kw, ic) order.
+* conv_transpose2d -- the conv page routes transposed convs to their own
+  gather kernels and defines nothing more, so the standard definition (the
+  adjoint of conv2d, weight [IC,OC,KH,KW]): each input element scatters
+  x*w into out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW].
 * sdpa -- "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),
   Problem/Solution: non-causal ``softmax(q @ k^T * scale + mask) @ v`` over
   [B,H,S,D] tensors, optional additive mask [B,H,Sq,Skv], Sq may differ from
@@ -99,6 +103,12 @@ def _load():
     lib.oracle_conv2d_nhwc.restype = ctypes.c_int
     lib.oracle_conv2d_nhwc_at.argtypes = [_i64] * 13 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
     lib.oracle_conv2d_nhwc_at.restype = ctypes.c_int
+    lib.oracle_convt_out_size.argtypes = [_i64] * 6
+    lib.oracle_convt_out_size.restype = _i64
+    lib.oracle_conv_transpose2d.argtypes = [_i64] * 15 + [_fp, _fp, _fp, _dp, _dp]
+    lib.oracle_conv_transpose2d.restype = ctypes.c_int
+    lib.oracle_conv_transpose2d_at.argtypes = [_i64] * 15 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
+    lib.oracle_conv_transpose2d_at.restype = ctypes.c_int
     lib.oracle_sdpa.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _dp, _dp]
     lib.oracle_sdpa.restype = ctypes.c_int
     lib.oracle_sdpa_rows.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _i64, _lp, _dp, _dp]
@@ -343,6 +353,58 @@ def conv2d_nhwc_at(x, w, bias, stride, padding, dilation, idx) -> Result:
                                        _ptr(idx, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
     assert rc == 0
     bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[idx % OC])
+    return Result(ref, sabs, bb)
+
+
+def convt_out_size(size, k, stride, pad, dil, out_pad) -> int:
+    return int(_load().oracle_convt_out_size(size, k, stride, pad, dil, out_pad))
+
+
+def _convt_args(x, w, stride, padding, dilation, output_padding):
+    B, IC, H, W = x.shape
+    IC2, OC, KH, KW = w.shape
+    assert IC == IC2, "weight must be [IC, OC, KH, KW]"
+    (sH, sW), (pH, pW), (dH, dW) = _pair(stride), _pair(padding), _pair(dilation)
+    opH, opW = _pair(output_padding)
+    return (B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW)
+
+
+def conv_transpose2d(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0) -> Result:
+    """Full [B,OC,OH,OW] reference of the transposed conv (scatter form):
+    x [B,IC,H,W], w [IC,OC,KH,KW], bias [OC]."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _convt_args(x, w, stride, padding, dilation, output_padding)
+    B, OC = a[0], a[4]
+    OH = convt_out_size(a[2], a[5], a[7], a[9], a[11], a[13])
+    OW = convt_out_size(a[3], a[6], a[8], a[10], a[12], a[14])
+    if OH <= 0 or OW <= 0:
+        raise ValueError("empty transposed-conv output")
+    ref = np.empty((B, OC, OH, OW), np.float64)
+    sabs = np.empty((B, OC, OH, OW), np.float64)
+    rc = _load().oracle_conv_transpose2d(*a, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp),
+                                         _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    bb = np.zeros(OC) if bias is None else np.abs(bias.astype(np.float64))
+    return Result(ref, sabs, np.broadcast_to(bb[None, :, None, None], ref.shape))
+
+
+def conv_transpose2d_at(x, w, bias, stride, padding, dilation, output_padding, idx) -> Result:
+    """Transposed-conv reference (gather form) at sampled flat NCHW indices."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    a = _convt_args(x, w, stride, padding, dilation, output_padding)
+    B, OC = a[0], a[4]
+    OH = convt_out_size(a[2], a[5], a[7], a[9], a[11], a[13])
+    OW = convt_out_size(a[3], a[6], a[8], a[10], a[12], a[14])
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    assert (idx >= 0).all() and (idx < B * OC * OH * OW).all()
+    n = idx.size
+    ref = np.empty(n, np.float64)
+    sabs = np.empty(n, np.float64)
+    rc = _load().oracle_conv_transpose2d_at(*a, _ptr(x, _fp), _ptr(w, _fp), _ptr(bias, _fp), n,
+                                            _ptr(idx, _lp), _ptr(ref, _dp), _ptr(sabs, _dp))
+    assert rc == 0
+    oc = (idx // (OH * OW)) % OC
+    bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])
     return Result(ref, sabs, bb)
 
 

@@ -488,3 +488,99 @@ int oracle_conv2d_nhwc_at(int64_t B, int64_t IC, int64_t H, int64_t W,
   }
   return 0;
 }
+
+/* ---- Transposed conv2d (NCHW) -------------------------------------------
+ * The conv page routes transposed convs to their own gather kernels
+ * ("et_vk conv2d: route standard (groups==1) conv through an im2col tiled
+ * GEMM", Solution paragraph) and defines no arithmetic for them, so the
+ * oracle takes the standard definition (the adjoint of conv2d, as aten's
+ * conv_transpose2d): input x [B,IC,H,W], weight w [IC,OC,KH,KW] (groups ==
+ * 1), and every input element scatters into
+ *   out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW] += x[b,ic,ih,iw] * w[ic,oc,kh,kw]
+ * (positions outside the output are dropped), plus bias[oc].  Output size
+ * OH = (H-1)*sH - 2*pH + dH*(KH-1) + opH + 1 (opH, the output padding,
+ * only adds rows at the far edge) and likewise OW. */
+int64_t oracle_convt_out_size(int64_t in, int64_t k, int64_t s, int64_t p,
+                              int64_t d, int64_t op) {
+  return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;
+}
+
+/* Full reference in the scatter form above; ref/sabs are [B,OC,OH,OW]. */
+int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W,
+                            int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                            int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                            int64_t dW, int64_t opH, int64_t opW,
+                            const float* x, const float* w, const float* bias,
+                            double* ref, double* sabs) {
+  int64_t OH = oracle_convt_out_size(H, KH, sH, pH, dH, opH);
+  int64_t OW = oracle_convt_out_size(W, KW, sW, pW, dW, opW);
+  if (OH <= 0 || OW <= 0) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t oc = 0; oc < OC; ++oc) {
+      double* r = ref + (b * OC + oc) * OH * OW;
+      double* a = sabs + (b * OC + oc) * OH * OW;
+      for (int64_t o = 0; o < OH * OW; ++o) {
+        r[o] = 0.0;
+        a[o] = 0.0;
+      }
+      for (int64_t ic = 0; ic < IC; ++ic)
+        for (int64_t ih = 0; ih < H; ++ih)
+          for (int64_t iw = 0; iw < W; ++iw) {
+            double xv = (double)x[((b * IC + ic) * H + ih) * W + iw];
+            for (int64_t kh = 0; kh < KH; ++kh) {
+              int64_t oh = ih * sH - pH + kh * dH;
+              if (oh < 0 || oh >= OH) continue;
+              for (int64_t kw = 0; kw < KW; ++kw) {
+                int64_t ow = iw * sW - pW + kw * dW;
+                if (ow < 0 || ow >= OW) continue;
+                double p = xv * (double)w[((ic * OC + oc) * KH + kh) * KW + kw];
+                r[oh * OW + ow] += p;
+                a[oh * OW + ow] += fabs(p);
+              }
+            }
+          }
+      if (bias)
+        for (int64_t o = 0; o < OH * OW; ++o) r[o] += (double)bias[oc];
+    }
+  return 0;
+}
+
+/* Sampled reference at flat NCHW output indices, in the gather form: the
+ * taps of output (oh, ow) are the (ic, kh, kw) with oh + pH - kh*dH a
+ * multiple of sH whose quotient ih lies in the input (and likewise along
+ * W). */
+int oracle_conv_transpose2d_at(int64_t B, int64_t IC, int64_t H, int64_t W,
+                               int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                               int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                               int64_t dW, int64_t opH, int64_t opW,
+                               const float* x, const float* w,
+                               const float* bias, int64_t n,
+                               const int64_t* idx, double* ref, double* sabs) {
+  int64_t OH = oracle_convt_out_size(H, KH, sH, pH, dH, opH);
+  int64_t OW = oracle_convt_out_size(W, KW, sW, pW, dW, opW);
+  if (OH <= 0 || OW <= 0 || B <= 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < n; ++s) {
+    int64_t o = idx[s];
+    int64_t ow = o % OW, oh = (o / OW) % OH, oc = (o / (OW * OH)) % OC;
+    int64_t b = o / (OW * OH * OC);
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t ic = 0; ic < IC; ++ic)
+      for (int64_t kh = 0; kh < KH; ++kh) {
+        int64_t th = oh + pH - kh * dH;
+        if (th < 0 || th % sH != 0 || th / sH >= H) continue;
+        for (int64_t kw = 0; kw < KW; ++kw) {
+          int64_t tw = ow + pW - kw * dW;
+          if (tw < 0 || tw % sW != 0 || tw / sW >= W) continue;
+          double p = (double)x[((b * IC + ic) * H + th / sH) * W + tw / sW] *
+                     (double)w[((ic * OC + oc) * KH + kh) * KW + kw];
+          acc += p;
+          aabs += fabs(p);
+        }
+      }
+    ref[s] = (bias ? (double)bias[oc] : 0.0) + acc;
+    sabs[s] = aabs;
+  }
+  return 0;
+}

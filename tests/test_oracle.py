@@ -710,3 +710,87 @@ def test_sampled_nhwc_conv_equals_full():
     idx = np.array([0, 3, 17, full.ref.size - 1, full.ref.size // 2])
     s = oracle.conv2d_nhwc_at(x, w, b, 2, 1, 1, idx)
     assert (s.ref == full.ref.reshape(-1)[idx]).all() and (s.sabs == full.sabs.reshape(-1)[idx]).all()
+
+
+# ----------------------------------------------------------- transposed conv
+# The conv page keeps transposed convs on their own gather kernels; the
+# definition taken is the adjoint of conv2d (aten's conv_transpose2d):
+# weight [IC,OC,KH,KW], x[b,ic,ih,iw]*w[ic,oc,kh,kw] lands on
+# out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW].
+
+CONVT_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, dil, out_pad
+    (2, 3, 5, 4, 4, 3, 3, 1, 0, 1, 0), (1, 4, 6, 5, 3, 4, 4, 2, 1, 1, 0),
+    (2, 2, 4, 7, 5, 3, 2, (2, 3), (1, 0), (1, 2), (1, 2)), (1, 3, 3, 3, 2, 2, 2, 2, 0, 1, 1),
+    (1, 5, 7, 6, 4, 5, 3, 3, 2, 2, (2, 0))]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,opad", CONVT_SHAPES)
+def test_conv_transpose_vs_torch_float64(B, IC, H, W, OC, KH, KW, stride, pad, dil, opad):
+    x, w, b = rand32((B, IC, H, W), 150), rand32((IC, OC, KH, KW), 151), rand32((OC,), 152)
+    r = oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad)
+    t = F.conv_transpose2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                           torch.from_numpy(b).double(), stride, pad, opad, 1, dil).numpy()
+    assert r.ref.shape == t.shape
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,opad", CONVT_SHAPES)
+def test_conv_transpose_is_the_adjoint_of_conv(B, IC, H, W, OC, KH, KW, stride, pad, dil, opad):
+    # <convT(x), y> = <x, conv(y)> for the same weight read as a conv weight
+    # [OC', IC'] = [IC, OC] (no bias): the defining property, checked with
+    # the oracle's own direct conv.
+    x, w = rand32((B, IC, H, W), 153), rand32((IC, OC, KH, KW), 154)
+    r = oracle.conv_transpose2d(x, w, None, stride, pad, dil, opad)
+    y = rand32(r.ref.shape, 155)
+    c = oracle.conv2d(y, w, None, stride, pad, dil)   # y [B,OC,OH,OW] -> [B,IC,H',W']
+    h, wd = min(H, c.ref.shape[2]), min(W, c.ref.shape[3])
+    # with output padding the conv of y may see fewer rows than x has; the
+    # missing rows of x only reach output rows past OH, which do not exist
+    lhs = float((r.ref * y.astype(np.float64)).sum())
+    rhs = float((x[:, :, :h, :wd].astype(np.float64) * c.ref[:, :, :h, :wd]).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_conv_transpose_stride1_is_a_flipped_conv():
+    # stride 1: convT(x, w) = conv(x, flip(w)^T, pad = d*(K-1) - p)
+    x, w, b = rand32((2, 3, 6, 7), 156), rand32((3, 4, 3, 2), 157), rand32((4,), 158)
+    r = oracle.conv_transpose2d(x, w, b, 1, (1, 0), (2, 1), 0)
+    wf = np.ascontiguousarray(np.flip(w, (2, 3)).transpose(1, 0, 2, 3))
+    c = oracle.conv2d(x, wf, b, 1, (2 * 2 - 1, 1 * 1 - 0), (2, 1))
+    np.testing.assert_allclose(r.ref, c.ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_transpose_single_pixel_places_the_kernel():
+    # one nonzero input pixel at (ih, iw) stamps x * w[ic, oc] at
+    # (ih*s - p + kh*d, iw*s - p + kw*d)
+    x = np.zeros((1, 1, 4, 5), np.float32)
+    x[0, 0, 2, 3] = 2.0
+    w = rand32((1, 2, 3, 3), 159)
+    r = oracle.conv_transpose2d(x, w, None, 2, 1, 2, 0)
+    want = np.zeros_like(r.ref)
+    for oc in range(2):
+        for kh in range(3):
+            for kw in range(3):
+                want[0, oc, 2 * 2 - 1 + 2 * kh, 3 * 2 - 1 + 2 * kw] += 2.0 * w[0, oc, kh, kw]
+    assert (r.ref == want).all()
+
+
+def test_conv_transpose_output_size():
+    assert oracle.convt_out_size(5, 3, 1, 0, 1, 0) == 7
+    assert oracle.convt_out_size(6, 4, 2, 1, 1, 0) == 12     # the usual 2x upsampling
+    assert oracle.convt_out_size(4, 3, 2, 1, 2, 1) == 10     # (4-1)*2 - 2 + 4 + 1 + 1
+    assert oracle.convt_out_size(3, 2, 2, 0, 1, 1) == 7
+
+
+def test_sampled_conv_transpose_equals_full():
+    # the sampled form gathers (divisibility test) where the full form
+    # scatters: the two formulations must agree
+    for shape in CONVT_SHAPES:
+        B, IC, H, W, OC, KH, KW, stride, pad, dil, opad = shape
+        x, w, b = rand32((B, IC, H, W), 160), rand32((IC, OC, KH, KW), 161), rand32((OC,), 162)
+        full = oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad)
+        idx = np.arange(full.ref.size)
+        s = oracle.conv_transpose2d_at(x, w, b, stride, pad, dil, opad, idx)
+        np.testing.assert_allclose(s.ref, full.ref.reshape(-1), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(s.sabs, full.sabs.reshape(-1), rtol=1e-13, atol=0)

@@ -50,6 +50,11 @@ MUTANTS = {
                                  "w[((oc * c->IC + ic) * c->KH + kh) * c->KW + kw]"),
     "nhwc_output_written_as_nchw": ("int64_t o = ((b * c.OH + oh) * c.OW + ow) * OC + oc;",
                                     "int64_t o = ((b * OC + oc) * c.OH + oh) * c.OW + ow;"),
+    "convt_pad_sign": ("int64_t oh = ih * sH - pH + kh * dH;", "int64_t oh = ih * sH + pH + kh * dH;"),
+    "convt_weight_ic_oc_swapped": ("w[((ic * OC + oc) * KH + kh) * KW + kw]",
+                                   "w[((oc * IC + ic) * KH + kh) * KW + kw]"),
+    "convt_output_padding_ignored": ("d * (k - 1) + op + 1;", "d * (k - 1) + 1;"),
+    "convt_gather_dilation_dropped": ("int64_t th = oh + pH - kh * dH;", "int64_t th = oh + pH - kh;"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
 }
