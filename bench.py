@@ -93,10 +93,22 @@ class Case:
     def __init__(self, name, torch, baim, I):
         self.name = name
         c = (I.CASES.get(name) or I.LINEAR_CASES.get(name) or I.GROUPED_CASES.get(name)
-             or I.NHWC_CASES.get(name) or I.SDPA_CASES[name])
+             or I.NHWC_CASES.get(name) or I.CONVT_CASES.get(name) or I.SDPA_CASES[name])
         self.c = c
         self.op = c.kind
         self.flops = c.flops
+        if c.kind == "convt":
+            x, w, bias = I.convt_inputs(c)
+            self.host = (x, w, bias)
+            self.x, self.w, self.bias = x.cuda(), w.cuda(), bias.cuda()
+            OH, OW = c.out_hw()
+            self.out = torch.empty((c.B, c.OC, OH, OW), dtype=torch.float32, device="cuda")
+            self.kernel = "baim::conv_transpose_kernel"
+            self.run = lambda: baim.conv_transpose2d_f32(self.out, self.x, self.w, self.bias,
+                                                         c.stride, c.padding, c.output_padding,
+                                                         1, c.dilation)
+            self.bytes = 4 * (x.numel() + w.numel() + bias.numel() + self.out.numel())
+            return
         if c.kind == "sdpa":
             q, k, v, m = I.sdpa_inputs(c)
             self.host = (q, k, v, m)
@@ -155,13 +167,13 @@ class Case:
 
 def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
     """Ops beyond the step's workload (linear with weight [N,K], grouped and
-    depthwise conv, channels-last conv, attention), timed the same way but reported separately:
+    depthwise conv, channels-last conv, transposed conv, attention), timed the same way but reported separately:
     they are not part of `value`.  Each case
     first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
     switch to new buffers)."""
     rows = []
     for name in (list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.NHWC_CASES)
-                 + list(I.SDPA_CASES)):
+                 + list(I.CONVT_CASES) + list(I.SDPA_CASES)):
         cs = Case(name, torch, baim, I)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < warmup_s:

@@ -19,13 +19,17 @@ arguments and allocates outputs with torch:
   -- the same conv (groups == 1) on channels-last tensors: input [B,H,W,IC],
   weight [OC,KH,KW,IC], output [B,OH,OW,OC]; the implicit im2col then reads
   K (a tap's input channels) contiguously.
+* ``conv_transpose2d(input, weight, bias=None, stride=1, padding=0,
+  output_padding=0, groups=1, dilation=1)`` -- the transposed conv (weight
+  [IC, OC/groups, KH, KW], aten's argument order), as one dense implicit
+  GEMM per output phase.
 * ``sdpa(q, k, v, attn_mask=None, scale=None)`` -- non-causal attention
   ``softmax(q @ k^T * scale + attn_mask) @ v`` over [..., S, D] tensors
   ("[ExecuTorch][WebGPU] Add optimized SDPA op", Problem/Solution), in one
   fused pass.
 
-``addmm_f32``, ``linear_f32``, ``conv2d_gemm_f32``, ``conv2d_nhwc_f32`` and
-``sdpa_f32`` are the
+``addmm_f32``, ``linear_f32``, ``conv2d_gemm_f32``, ``conv2d_nhwc_f32``,
+``conv_transpose2d_f32`` and ``sdpa_f32`` are the
 same-named entry points of the C ABI taking caller-allocated tensors.  Tensors must be fp32, contiguous and
 on the same ROCm device; work is enqueued on the current torch stream.
 """
@@ -33,8 +37,9 @@ from __future__ import annotations
 
 from . import _capi
 
-__all__ = ["addmm", "linear", "conv2d", "conv2d_nhwc", "sdpa", "addmm_f32", "linear_f32",
-           "conv2d_gemm_f32", "conv2d_nhwc_f32", "sdpa_f32", "conv2d_out_hw", "gemm_plan",
+__all__ = ["addmm", "linear", "conv2d", "conv2d_nhwc", "conv_transpose2d", "sdpa", "addmm_f32",
+           "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32", "conv_transpose2d_f32", "sdpa_f32",
+           "conv_transpose2d_out_hw", "conv2d_out_hw", "gemm_plan",
            "BaimError", "library_path"]
 
 
@@ -354,3 +359,65 @@ def conv2d_nhwc(input, weight, bias=None, stride=1, padding=0, dilation=1):
                            dilation)
     out = torch.empty((x.shape[0], OH, OW, w.shape[0]), dtype=torch.float32, device=x.device)
     return conv2d_nhwc_f32(out, x, w, bias, stride, padding, dilation)
+
+
+def conv_transpose2d_out_hw(H, W, KH, KW, stride=1, padding=0, dilation=1, output_padding=0):
+    (sH, sW), (pH, pW), (dH, dW), (oH, oW) = (
+        _pair(stride, "stride"), _pair(padding, "padding"), _pair(dilation, "dilation"),
+        _pair(output_padding, "output_padding"))
+    st, oh, ow = _capi.conv_transpose2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, oH, oW)
+    _check(st)
+    return oh, ow
+
+
+def conv_transpose2d_f32(out, input, weight, bias=None, stride=1, padding=0, output_padding=0,
+                         groups=1, dilation=1):
+    """Transposed conv2d written into ``out`` [B, OC, OH, OW]: input
+    [B, IC, H, W], weight [IC, OC/groups, KH, KW], bias [OC] or None."""
+    import torch
+    out, x, w = _dev_f32(out, "out"), _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4 or out.dim() != 4:
+        raise ValueError("input, weight and out must be 4-D")
+    B, IC, H, W = x.shape
+    IC2, OCg, KH, KW = w.shape
+    if IC2 != IC or int(groups) < 1:
+        raise ValueError(f"weight must be [IC={IC}, OC/groups, KH, KW], got {list(w.shape)}")
+    OC = OCg * int(groups)
+    (sH, sW), (pH, pW), (dH, dW), (oH, oW) = (
+        _pair(stride, "stride"), _pair(padding, "padding"), _pair(dilation, "dilation"),
+        _pair(output_padding, "output_padding"))
+    bias_ptr = None
+    devs = {out.device, x.device, w.device}
+    if bias is not None:
+        bias = _dev_f32(bias, "bias")
+        if tuple(bias.shape) != (OC,):
+            raise ValueError(f"bias must be [{OC}]")
+        bias_ptr = bias.data_ptr()
+        devs.add(bias.device)
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on the same device")
+    st, OH, OW = _capi.conv_transpose2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, oH, oW)
+    _check(st)
+    if tuple(out.shape) != (B, OC, OH, OW):
+        raise ValueError(f"out must be [{B}, {OC}, {OH}, {OW}], got {list(out.shape)}")
+    dev = out.device
+    with torch.cuda.device(dev):
+        st = _capi.conv_transpose2d_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
+                                        B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, oH, oW,
+                                        int(groups), _stream(dev))
+    _check(st)
+    return out
+
+
+def conv_transpose2d(input, weight, bias=None, stride=1, padding=0, output_padding=0, groups=1,
+                     dilation=1):
+    """Transposed conv2d (weight [IC, OC/groups, KH, KW]) as a new tensor."""
+    import torch
+    x, w = _dev_f32(input, "input"), _dev_f32(weight, "weight")
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("input and weight must be 4-D")
+    OH, OW = conv_transpose2d_out_hw(x.shape[2], x.shape[3], w.shape[2], w.shape[3], stride,
+                                     padding, dilation, output_padding)
+    out = torch.empty((x.shape[0], w.shape[1] * int(groups), OH, OW), dtype=torch.float32,
+                      device=x.device)
+    return conv_transpose2d_f32(out, x, w, bias, stride, padding, output_padding, groups, dilation)

@@ -25,8 +25,8 @@ STATUS_NAMES = {
 }
 
 # Every symbol include/baim.h declares.
-EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32", "sdpa_f32",
-           "baim_conv2d_out_hw",
+EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32",
+           "conv_transpose2d_f32", "sdpa_f32", "baim_conv2d_out_hw", "baim_conv_transpose2d_out_hw",
            "baim_gemm_plan", "baim_last_error", "baim_version")
 
 _lib = None
@@ -53,6 +53,10 @@ def lib():
     L.conv2d_gemm_f32.restype = ctypes.c_int
     L.conv2d_nhwc_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 13 + [_vp]
     L.conv2d_nhwc_f32.restype = ctypes.c_int
+    L.conv_transpose2d_f32.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 16 + [_vp]
+    L.conv_transpose2d_f32.restype = ctypes.c_int
+    L.baim_conv_transpose2d_out_hw.argtypes = [_i64] * 12 + [ctypes.POINTER(_i64)] * 2
+    L.baim_conv_transpose2d_out_hw.restype = ctypes.c_int
     L.sdpa_f32.argtypes = [_vp] * 5 + [_i64] * 4 + [ctypes.POINTER(ctypes.c_float), _vp]
     L.sdpa_f32.restype = ctypes.c_int
     L.baim_conv2d_out_hw.argtypes = [_i64] * 10 + [ctypes.POINTER(_i64)] * 2
@@ -83,6 +87,19 @@ def conv2d_nhwc_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH
                     stream) -> int:
     return lib().conv2d_nhwc_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH,
                                  dW, stream)
+
+
+def conv_transpose2d_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
+                         opH, opW, groups, stream) -> int:
+    return lib().conv_transpose2d_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW,
+                                      dH, dW, opH, opW, groups, stream)
+
+
+def conv_transpose2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW):
+    oh, ow = _i64(0), _i64(0)
+    st = lib().baim_conv_transpose2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW,
+                                            ctypes.byref(oh), ctypes.byref(ow))
+    return st, oh.value, ow.value
 
 
 def sdpa_f32(out, q, k, v, mask, BH, Sq, Skv, D, scale, stream) -> int:

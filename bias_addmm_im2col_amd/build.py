@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbaim.so")
 SOURCES = ["api.cpp", "tile_select.cpp", "sdpa_plan.cpp", "addmm.hip", "conv2d_gemm.hip", "conv_direct.hip",
-           "sdpa.hip"]
+           "sdpa.hip", "conv_transpose.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -345,3 +345,92 @@ extern "C" baim_status conv2d_nhwc_f32(float* out, const float* input, const flo
   q.groups = 1;
   return launched(baim::launch_conv2d_nhwc(q, (hipStream_t)stream), "conv2d_nhwc_f32");
 }
+
+extern "C" baim_status baim_conv_transpose2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW,
+                                                    int64_t sH, int64_t sW, int64_t pH,
+                                                    int64_t pW, int64_t dH, int64_t dW,
+                                                    int64_t opH, int64_t opW, int64_t* OH,
+                                                    int64_t* OW) {
+  g_err.clear();
+  if (!OH || !OW)
+    return fail(BAIM_ERR_NULL, "baim_conv_transpose2d_out_hw: OH/OW must not be NULL");
+  *OH = *OW = 0;
+  if (H < 1 || W < 1 || KH < 1 || KW < 1)
+    return fail(BAIM_ERR_SHAPE, "conv_transpose2d: input and kernel sizes must be >= 1");
+  if (sH < 1 || sW < 1) return fail(BAIM_ERR_SHAPE, "conv_transpose2d: stride must be >= 1");
+  if (dH < 1 || dW < 1) return fail(BAIM_ERR_SHAPE, "conv_transpose2d: dilation must be >= 1");
+  if (pH < 0 || pW < 0) return fail(BAIM_ERR_SHAPE, "conv_transpose2d: padding must be >= 0");
+  if (H > kMaxElems || W > kMaxElems || KH > kMaxElems || KW > kMaxElems || sH > kMaxElems ||
+      sW > kMaxElems || pH > kMaxElems || pW > kMaxElems || dH > kMaxElems || dW > kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "conv_transpose2d: size argument too large");
+  if (opH < 0 || opW < 0 || opH >= (sH > dH ? sH : dH) || opW >= (sW > dW ? sW : dW))
+    return fail(BAIM_ERR_SHAPE,
+                "conv_transpose2d: output padding must be >= 0 and below max(stride, dilation)");
+  const int64_t oh = (H - 1) * sH - 2 * pH + dH * (KH - 1) + opH + 1;
+  const int64_t ow = (W - 1) * sW - 2 * pW + dW * (KW - 1) + opW + 1;
+  if (oh < 1 || ow < 1)
+    return fail(BAIM_ERR_SHAPE, "conv_transpose2d: empty output (%lld x %lld)", (long long)oh,
+                (long long)ow);
+  *OH = oh;
+  *OW = ow;
+  return BAIM_OK;
+}
+
+extern "C" baim_status conv_transpose2d_f32(float* out, const float* input, const float* weight,
+                                            const float* bias, int64_t B, int64_t IC, int64_t H,
+                                            int64_t W, int64_t OC, int64_t KH, int64_t KW,
+                                            int64_t sH, int64_t sW, int64_t pH, int64_t pW,
+                                            int64_t dH, int64_t dW, int64_t opH, int64_t opW,
+                                            int64_t groups, void* stream) {
+  g_err.clear();
+  if (B < 1 || IC < 1 || OC < 1)
+    return fail(BAIM_ERR_SHAPE, "conv_transpose2d: B, IC and OC must be >= 1");
+  if (groups < 1 || IC % groups != 0 || OC % groups != 0)
+    return fail(BAIM_ERR_SHAPE, "conv_transpose2d: groups=%lld must be >= 1 and divide IC=%lld "
+                "and OC=%lld", (long long)groups, (long long)IC, (long long)OC);
+  int64_t OH = 0, OW = 0;
+  const baim_status hs =
+      baim_conv_transpose2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW, &OH, &OW);
+  if (hs != BAIM_OK) return hs;  // message already set
+  const int64_t ocg = OC / groups;
+  const int64_t n_x = elems({B, IC, H, W}), n_w = elems({IC, ocg, KH, KW});
+  const int64_t n_out = elems({B, OC, OH, OW}), K = elems({IC / groups, KH, KW});
+  if (n_x < 0 || n_w < 0 || n_out < 0 || n_x >= kMaxElems || n_w >= kMaxElems ||
+      n_out >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE,
+                "conv_transpose2d: every tensor must have fewer than 2^31 elements");
+  if (n_x >= kMaxConvInput || n_w >= kMaxConvInput)
+    return fail(BAIM_ERR_TOO_LARGE,
+                "conv_transpose2d: input and weight must have fewer than 2^29 elements");
+  if (K >= kMaxK)
+    return fail(BAIM_ERR_TOO_LARGE, "conv_transpose2d: (IC/groups)*KH*KW must be below 2^21");
+  if (groups > 65535) return fail(BAIM_ERR_TOO_LARGE, "conv_transpose2d: groups must be <= 65535");
+  if (!out || !input || !weight)
+    return fail(BAIM_ERR_NULL, "conv_transpose2d: out/input/weight is NULL");
+  if (overlap(out, n_out, input, n_x) || overlap(out, n_out, weight, n_w) ||
+      overlap(out, n_out, bias, OC))
+    return fail(BAIM_ERR_ALIAS, "conv_transpose2d: out overlaps an input");
+
+  baim::ConvTProblem q;
+  q.out = out;
+  q.x = input;
+  q.w = weight;
+  q.bias = bias;
+  q.B = (int)B;
+  q.IC = (int)IC;
+  q.H = (int)H;
+  q.W = (int)W;
+  q.OC = (int)OC;
+  q.KH = (int)KH;
+  q.KW = (int)KW;
+  q.sH = (int)sH;
+  q.sW = (int)sW;
+  q.pH = (int)pH;
+  q.pW = (int)pW;
+  q.dH = (int)dH;
+  q.dW = (int)dW;
+  q.OH = (int)OH;
+  q.OW = (int)OW;
+  q.groups = (int)groups;
+  return launched(baim::launch_conv_transpose2d(q, (hipStream_t)stream), "conv_transpose2d_f32");
+}

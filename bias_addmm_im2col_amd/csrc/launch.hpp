@@ -37,6 +37,15 @@ struct SdpaProblem {
   float scale;
 };
 
+struct ConvTProblem {
+  float* out;         // [B, OC, OH, OW]
+  const float* x;     // [B, IC, H, W]
+  const float* w;     // [IC, OC/groups, KH, KW]
+  const float* bias;  // may be NULL
+  int B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW;
+  int groups;
+};
+
 // Whether a grouped conv runs as one implicit-im2col GEMM per group (true)
 // or on the direct kernel (per-group GEMMs too small for the matrix cores).
 inline bool conv_uses_gemm(const ConvProblem& q) {
@@ -48,6 +57,7 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);
+hipError_t launch_conv_transpose2d(const ConvTProblem& p, hipStream_t stream);
 // Channels-last conv (groups == 1): x [B,H,W,IC], w [OC,KH,KW,IC],
 // out [B,OH,OW,OC]; the addmm kernels with an im2col A operand.
 hipError_t launch_conv2d_nhwc(const ConvProblem& p, hipStream_t stream);

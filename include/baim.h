@@ -160,6 +160,53 @@ baim_status conv2d_nhwc_f32(float* out, const float* input,
                             void* stream);
 
 /*
+ * conv_transpose2d_f32: out = conv_transpose2d(input, weight, bias), NCHW.
+ *
+ * The conv page ("et_vk conv2d: route standard (groups==1) conv through an
+ * im2col tiled GEMM", Solution paragraph) keeps transposed convs on their
+ * own gather kernels and defines no arithmetic for them; this is the
+ * standard operation (aten's conv_transpose2d, the adjoint of conv2d):
+ * input element x[b, ic, ih, iw] times weight w[ic, oc, kh, kw] lands on
+ * out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW] (dropped outside the
+ * output), plus bias[oc]; with groups, input channels and output channels
+ * split into `groups` equal blocks that only meet each other.  Computed as
+ * one dense implicit GEMM per output phase (oh % sH, ow % sW), whose taps
+ * are exactly the ones that land on it.
+ *
+ *  out     [B,OC,OH,OW] fp32, written in full; OH, OW from
+ *          baim_conv_transpose2d_out_hw().
+ *  input   [B,IC,H,W] fp32.
+ *  weight  [IC,OC/groups,KH,KW] fp32.
+ *  bias    [OC] fp32, or NULL for no bias.
+ *  opH, opW  output padding: 0 <= op < max(stride, dilation) per axis.
+ *  groups  >= 1, dividing IC and OC.
+ *  stream  hipStream_t or NULL.
+ * Limits: every tensor below 2^31 elements, input and weight below 2^29,
+ * (IC/groups)*KH*KW below 2^21, groups at most 65535 (BAIM_ERR_TOO_LARGE).
+ */
+baim_status conv_transpose2d_f32(float* out, const float* input,
+                                 const float* weight, const float* bias,
+                                 int64_t B, int64_t IC, int64_t H, int64_t W,
+                                 int64_t OC, int64_t KH, int64_t KW,
+                                 int64_t sH, int64_t sW, int64_t pH,
+                                 int64_t pW, int64_t dH, int64_t dW,
+                                 int64_t opH, int64_t opW, int64_t groups,
+                                 void* stream);
+
+/*
+ * baim_conv_transpose2d_out_hw: the output size of the transposed conv,
+ * OH = (H-1)*sH - 2*pH + dH*(KH-1) + opH + 1 and likewise OW (aten's
+ * rule; the output padding only adds rows and columns at the far edge).
+ * BAIM_ERR_SHAPE for an empty output or an output padding outside
+ * [0, max(stride, dilation)).
+ */
+baim_status baim_conv_transpose2d_out_hw(int64_t H, int64_t W, int64_t KH,
+                                         int64_t KW, int64_t sH, int64_t sW,
+                                         int64_t pH, int64_t pW, int64_t dH,
+                                         int64_t dW, int64_t opH, int64_t opW,
+                                         int64_t* OH, int64_t* OW);
+
+/*
  * sdpa_f32: out = softmax(q @ k^T * scale + attn_mask) @ v, non-causal.
  *
  * Defined by "[ExecuTorch][WebGPU] Add optimized SDPA op" (PR #20851),

@@ -205,6 +205,41 @@ def test_conv_nhwc_rejects(lib, kw, status):
     assert _capi.last_error()
 
 
+def convt(out=O, x=A, w=Bp, bias=S, B=1, IC=4, H=8, W=8, OC=4, KH=3, KW=3, sH=2, sW=2, pH=1,
+          pW=1, dH=1, dW=1, opH=0, opW=0, groups=1):
+    return _capi.conv_transpose2d_f32(out, x, w, bias, B, IC, H, W, OC, KH, KW, sH, sW, pH, pW,
+                                      dH, dW, opH, opW, groups, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), _capi.BAIM_ERR_SHAPE),
+    (dict(groups=3), _capi.BAIM_ERR_SHAPE),             # does not divide IC
+    (dict(groups=0), _capi.BAIM_ERR_SHAPE),
+    (dict(sW=0), _capi.BAIM_ERR_SHAPE),
+    (dict(opH=2), _capi.BAIM_ERR_SHAPE),                # output padding >= max(stride, dilation)
+    (dict(opW=-1), _capi.BAIM_ERR_SHAPE),
+    (dict(H=1, KH=1, pH=1, sH=1), _capi.BAIM_ERR_SHAPE),  # empty output
+    (dict(out=None), _capi.BAIM_ERR_NULL),
+    (dict(x=None), _capi.BAIM_ERR_NULL),
+    (dict(IC=1 << 20, H=32, W=32), _capi.BAIM_ERR_TOO_LARGE),   # input 2^30
+    (dict(IC=1 << 18, OC=2, KH=3, KW=3, H=1, W=1), _capi.BAIM_ERR_TOO_LARGE),  # K >= 2^21
+    (dict(out=A + 8), _capi.BAIM_ERR_ALIAS),
+    (dict(out=S - 4), _capi.BAIM_ERR_ALIAS),
+])
+def test_conv_transpose_rejects(lib, kw, status):
+    st = convt(**kw)
+    assert st == status, (st, _capi.last_error())
+    assert _capi.last_error()
+
+
+def test_conv_transpose_out_hw(lib):
+    assert _capi.conv_transpose2d_out_hw(28, 28, 4, 4, 2, 2, 1, 1, 1, 1, 0, 0) == (0, 56, 56)
+    assert _capi.conv_transpose2d_out_hw(64, 64, 2, 2, 2, 2, 0, 0, 1, 1, 0, 0) == (0, 128, 128)
+    assert _capi.conv_transpose2d_out_hw(4, 5, 3, 3, 2, 2, 1, 1, 2, 2, 1, 0) == (0, 10, 11)
+    st, oh, ow = _capi.conv_transpose2d_out_hw(4, 4, 3, 3, 2, 2, 1, 1, 1, 1, 2, 0)
+    assert st == _capi.BAIM_ERR_SHAPE and (oh, ow) == (0, 0)
+
+
 M5 = 5 * P  # fake mask address
 
 

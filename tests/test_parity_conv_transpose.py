@@ -1,0 +1,131 @@
+"""GPU parity of the transposed conv (conv_transpose2d_f32) against the fp64
+oracle.
+
+The conv page keeps transposed convs on their own gather kernels; the
+operation is the adjoint of conv2d (aten's conv_transpose2d, weight
+[IC, OC/groups, KH, KW]).  Acceptance: |out - ref| <=
+4e-6*sqrt(K)*(sum|x*w| + |bias|) elementwise with K = (IC/groups)*KH*KW
+(an upper bound on the taps of any output); integer-valued inputs must
+match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bias_addmm_im2col_amd import inputs as I
+from tests._parity import check_bitwise, check_close, conv_sample, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    from bias_addmm_im2col_amd import _capi
+    _capi.lib()
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def gen(shape, seed, kind="U"):
+    g = torch.Generator("cpu").manual_seed(seed)
+    if kind == "U":
+        return torch.rand(shape, generator=g) * 2 - 1
+    return torch.randint(-4, 5, shape, generator=g).float()
+
+
+def run(x, w, b, stride=1, pad=0, opad=0, groups=1, dil=1):
+    import bias_addmm_im2col_amd as baim
+    out = baim.conv_transpose2d(dev(x), dev(w), dev(b), stride, pad, opad, groups, dil)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_grouped(x, w, b, stride, pad, opad, groups, dil):
+    """Grouped transposed conv from the ungrouped oracle, one group at a time."""
+    IC = x.shape[1]
+    icg, ocg = IC // groups, w.shape[1]
+    parts = []
+    for g in range(groups):
+        xs = x[:, g * icg:(g + 1) * icg].contiguous()
+        ws = w[g * icg:(g + 1) * icg].contiguous()
+        bs = None if b is None else b[g * ocg:(g + 1) * ocg].contiguous()
+        parts.append(oracle.conv_transpose2d(xs, ws, bs, stride, pad, dil, opad))
+    return oracle.Result(np.concatenate([p.ref for p in parts], 1),
+                         np.concatenate([p.sabs for p in parts], 1),
+                         np.concatenate([p.selfabs for p in parts], 1))
+
+
+SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, out_pad, dil, bias
+    (1, 4, 5, 5, 8, 3, 3, 1, 0, 0, 1, True),
+    (2, 16, 9, 7, 12, 4, 4, 2, 1, 0, 1, True),          # 2x upsampling
+    (2, 8, 6, 6, 5, 2, 2, 2, 0, 0, 1, False),           # 2x2 / stride 2: one tap per phase
+    (1, 6, 7, 5, 9, 3, 3, 2, 1, 1, 1, True),            # output padding
+    (1, 5, 6, 8, 7, 3, 2, (3, 2), (1, 0), (2, 1), (1, 2), True),
+    (2, 3, 5, 4, 4, 5, 3, 3, 2, (2, 0), 2, True),       # dilation 2 with stride 3
+    (1, 32, 10, 11, 70, 3, 3, 2, 1, 1, 1, True),
+    (1, 4, 4, 4, 3, 1, 1, 3, 0, 2, 1, True),            # 1x1 / stride 3: phases with no taps
+    (1, 64, 12, 12, 130, 4, 4, 2, 1, 0, 1, True),       # several k-tiles and m-tiles
+    (1, 2, 3, 3, 2, 3, 3, 5, 0, 0, 1, True),            # stride 5: 25 phases (two launches)
+]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,opad,dil,has_bias", SHAPES)
+def test_convt_small_full(B, IC, H, W, OC, KH, KW, stride, pad, opad, dil, has_bias):
+    say(f"conv_transpose2d_f32 x=[{B},{IC},{H},{W}] w=[{IC},{OC},{KH},{KW}] s={stride} "
+        f"p={pad} op={opad} d={dil}")
+    x, w = gen((B, IC, H, W), 1), gen((IC, OC, KH, KW), 2)
+    b = gen((OC,), 3) if has_bias else None
+    check_close(run(x, w, b, stride, pad, opad, 1, dil),
+                oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad), IC * KH * KW, 1.0,
+                f"convT {IC}x{KH}x{KW}")
+
+
+@pytest.mark.parametrize("groups,IC,OC", [(2, 8, 6), (4, 16, 16), (8, 8, 8)])
+def test_convt_grouped(groups, IC, OC):
+    say(f"conv_transpose2d_f32 groups={groups} IC={IC} OC={OC}")
+    x, w, b = gen((2, IC, 7, 6), 4), gen((IC, OC // groups, 3, 3), 5), gen((OC,), 6)
+    check_close(run(x, w, b, 2, 1, 1, groups), oracle_grouped(x, w, b, 2, 1, 1, groups, 1),
+                IC // groups * 9, 1.0, f"convT groups {groups}")
+
+
+@pytest.mark.parametrize("stride,k", [(1, 3), (2, 4), (2, 2), (3, 3)])
+def test_convt_integer_bitwise(stride, k):
+    say(f"conv_transpose2d_f32 integer s={stride} k={k}")
+    x, w, b = gen((2, 24, 9, 10), 7, "I"), gen((24, 40, k, k), 8, "I"), gen((40,), 9, "I")
+    check_bitwise(run(x, w, b, stride, 1 if k > 2 else 0),
+                  oracle.conv_transpose2d(x, w, b, stride, 1 if k > 2 else 0, 1, 0),
+                  f"convT integer s={stride}")
+
+
+@pytest.mark.parametrize("spec", ["0", "1", "2", "3", "4", "5", "6", "7"])
+def test_convt_forced_tile_configs(spec, monkeypatch):
+    monkeypatch.setenv("BAIM_TILE", spec)
+    say(f"BAIM_TILE={spec} conv_transpose2d_f32")
+    x, w, b = gen((2, 20, 9, 8), 10), gen((20, 70, 4, 4), 11), gen((70,), 12)
+    check_close(run(x, w, b, 2, 1, 1), oracle.conv_transpose2d(x, w, b, 2, 1, 1, 1), 20 * 16, 1.0,
+                f"convT {spec}")
+    x, w, b = gen((1, 16, 6, 7), 13, "I"), gen((16, 33, 3, 3), 14, "I"), gen((33,), 15, "I")
+    check_bitwise(run(x, w, b, 2, 1, 1), oracle.conv_transpose2d(x, w, b, 2, 1, 1, 1),
+                  f"convT int {spec}")
+
+
+@pytest.mark.parametrize("name", list(I.CONVT_CASES))
+def test_workload_convt(name):
+    import bias_addmm_im2col_amd as baim
+    c = I.CONVT_CASES[name]
+    say(f"workload {name}: conv_transpose2d_f32")
+    x, w, b = I.convt_inputs(c)
+    out = baim.conv_transpose2d(dev(x), dev(w), dev(b), c.stride, c.padding, c.output_padding, 1,
+                                c.dilation)
+    torch.cuda.synchronize()
+    OH, OW = c.out_hw()
+    idx = conv_sample(c.B, c.OC, OH, OW)
+    got = out.reshape(-1)[torch.from_numpy(idx).cuda()].cpu().numpy()
+    res = oracle.conv_transpose2d_at(x, w, b, c.stride, c.padding, c.dilation, c.output_padding, idx)
+    check_close(got, res, c.IC * c.KH * c.KW, 1.0, name)
