@@ -162,7 +162,7 @@ class Case:
                                                         c.stride, c.padding, c.dilation)
             self.bytes = 4 * (x.numel() + w.numel() + bias.numel() + self.out.numel())
             if c.groups > 1 and not (c.OC // c.groups >= 32 and c.IC // c.groups * c.KH * c.KW >= 32):
-                self.kernel = "baim::conv_direct_kernel"
+                self.kernel = "baim::conv_direct_tiled_kernel"
 
 
 def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
@@ -190,7 +190,7 @@ def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
         tf = cs.flops / us / 1e6
         row = {"case": name, "op": cs.op, "kernel": cs.kernel, "us": round(us, 2),
                "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)}
-        if cs.kernel == "baim::conv_direct_kernel":
+        if cs.kernel == "baim::conv_direct_tiled_kernel":
             # memory-bound: achieved bandwidth on the algorithmic bytes
             gbs = cs.bytes / us / 1e3
             row.update({"bound": "hbm", "gbytes_per_s": round(gbs, 1),
