@@ -444,6 +444,8 @@ GCONV_SHAPES = [
     (2, 12, 9, 9, 12, 1, 1, 1, 0, 1, 3, True),        # grouped 1x1: direct
     (1, 8, 70, 70, 8, 3, 3, 8, 1, 1, 8, True),        # stride 8: window > LDS, plain direct
     (2, 16, 70, 130, 16, 3, 3, 1, 1, 1, 16, False),   # depthwise, several tiles per plane
+    (1, 8, 130, 130, 8, 3, 3, 1, 1, 1, 4, True),      # 2 channels per group, LDS tiles
+    (1, 4, 140, 140, 4, 3, 3, 8, 1, 1, 4, True),      # stride 8 on a large plane: plain direct
 ]
 
 
