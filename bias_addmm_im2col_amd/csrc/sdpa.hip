@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "index_math.hpp"
 #include "launch.hpp"
@@ -59,7 +61,7 @@ struct SdpaArgs {
   float* out;
   int Sq, Skv, D;
   int qblocks, nblocks;
-  float scale;
+  float scale2;  // scale * log2(e): the logits are kept in base 2
 };
 
 template <int DP, int QW, int KW, int NB>
@@ -220,35 +222,54 @@ __global__ __launch_bounds__(256, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a)
       }
     }
 
-    // Logits, running maximum and sum.
+    // Logits in base 2 (scale2 = scale * log2(e), the mask times log2(e)),
+    // running maximum and sum.  Keys past Skv only occur in the last tile;
+    // only there does each logit need the -inf test.
     float mt = -INFINITY;
+    auto logits = [&](auto tail_tag) __attribute__((always_inline)) {
+      constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kv = kv0 + kb0 + 32 * kb + 8 * (j / 4) + 4 * h + (j % 4);
-        float x = s[kb][j] * a.scale;
-        if constexpr (MASK) x += mk[kb][j / 4][j % 4];
-        x = (blk[kb] && kv < Skv) ? x : -INFINITY;
-        s[kb][j] = x;
-        mt = fmaxf(mt, x);
-      }
+        for (int j = 0; j < 16; ++j) {
+          float x;
+          if constexpr (MASK)
+            x = fmaf(mk[kb][j / 4][j % 4], kLog2e, s[kb][j] * a.scale2);
+          else
+            x = s[kb][j] * a.scale2;
+          if constexpr (TAIL) {
+            const int kv = kv0 + kb0 + 32 * kb + 8 * (j / 4) + 4 * h + (j % 4);
+            x = (blk[kb] && kv < Skv) ? x : -INFINITY;
+          }
+          s[kb][j] = x;
+          mt = fmaxf(mt, x);
+        }
+    };
+    if (kv0 + S::BKV > Skv)
+      logits(std::true_type{});
+    else
+      logits(std::false_type{});
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * kLog2e);
     float ps = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f((s[kb][j] - m_use) * kLog2e);
+        const float p = __builtin_amdgcn_exp2f(s[kb][j] - m_use);
         s[kb][j] = p;
         ps += p;
       }
-    l_lane = l_lane * alpha + ps;
+    // Rescale only when some row's maximum moved (rare after the first
+    // tiles); otherwise the factor is exactly 1.
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_lane *= alpha;
+      scale_rows(o, alpha, slot, c, h);
+    }
+    l_lane += ps;
     m_run = m_new;
-    scale_rows(o, alpha, slot, c, h);
 
     // O += P V: step st of key block kb takes key kb0 + 32*kb + 8*(st/4) + 4*h + st%4.
 #pragma unroll
@@ -290,8 +311,8 @@ __global__ __launch_bounds__(256, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a)
 #pragma unroll
     for (int g = 0; g < KW; ++g)
       L += stat_l[g * S::BQ + 32 * qg + c] *
-           __builtin_amdgcn_exp2f((stat_m[g * S::BQ + 32 * qg + c] - m_use) * kLog2e);
-    scale_rows(o, __builtin_amdgcn_exp2f((m_run - m_use) * kLog2e), slot, c, h);
+           __builtin_amdgcn_exp2f(stat_m[g * S::BQ + 32 * qg + c] - m_use);
+    scale_rows(o, __builtin_amdgcn_exp2f(m_run - m_use), slot, c, h);
     if (kg > 0) {
       float* mine = red + ((kg - 1) * QW + qg) * 32 * DP;
 #pragma unroll
@@ -363,7 +384,7 @@ hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream) {
   a.Sq = p.Sq;
   a.Skv = p.Skv;
   a.D = p.D;
-  a.scale = p.scale;
+  a.scale2 = p.scale * kLog2e;
   a.qblocks = 0;
   a.nblocks = p.BH;
   const int cfg = plan_sdpa(p.BH, p.Sq, p.Skv, getenv("BAIM_SDPA"));
