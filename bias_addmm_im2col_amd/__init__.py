@@ -110,6 +110,15 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _on(dev):
+    """Make `dev` the current device for the call, unless it already is."""
+    import contextlib
+    import torch
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
 def addmm_f32(out, self, mat1, mat2, beta=1.0, alpha=1.0):
     """out[M,N] = beta*self + alpha*(mat1 @ mat2), written into ``out``.
 
@@ -143,7 +152,7 @@ def addmm_f32(out, self, mat1, mat2, beta=1.0, alpha=1.0):
     if len(devs) != 1:
         raise ValueError("all tensors must be on the same device")
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.addmm_f32(out.data_ptr(), self_ptr, self_2d, mat1.data_ptr(),
                              mat2.data_ptr(), M, N, K, beta, alpha, _stream(dev))
     _check(st)
@@ -182,7 +191,7 @@ def linear_f32(out, x, weight, bias=None):
     if len(devs) != 1:
         raise ValueError("all tensors must be on the same device")
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.linear_f32(out.data_ptr(), x.data_ptr(), weight.data_ptr(), bias_ptr, M, N, K,
                               _stream(dev))
     _check(st)
@@ -246,7 +255,7 @@ def conv2d_gemm_f32(out, input, weight, bias=None, stride=1, padding=0, dilation
     if tuple(out.shape) != (B, OC, OH, OW):
         raise ValueError(f"out must be [{B}, {OC}, {OH}, {OW}], got {list(out.shape)}")
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.conv2d_gemm_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
                                    B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
                                    int(groups), _stream(dev))
@@ -298,7 +307,7 @@ def sdpa_f32(out, q, k, v, attn_mask=None, scale=None):
         raise ValueError("all tensors must be on the same device")
     sc = None if scale is None else float(scale)
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.sdpa_f32(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), mask_ptr,
                             BH, Sq, Skv, D, sc, _stream(dev))
     _check(st)
@@ -341,7 +350,7 @@ def conv2d_nhwc_f32(out, input, weight, bias=None, stride=1, padding=0, dilation
     if tuple(out.shape) != (B, OH, OW, OC):
         raise ValueError(f"out must be [{B}, {OH}, {OW}, {OC}], got {list(out.shape)}")
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.conv2d_nhwc_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
                                    B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, _stream(dev))
     _check(st)
@@ -401,7 +410,7 @@ def conv_transpose2d_f32(out, input, weight, bias=None, stride=1, padding=0, out
     if tuple(out.shape) != (B, OC, OH, OW):
         raise ValueError(f"out must be [{B}, {OC}, {OH}, {OW}], got {list(out.shape)}")
     dev = out.device
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = _capi.conv_transpose2d_f32(out.data_ptr(), x.data_ptr(), w.data_ptr(), bias_ptr,
                                         B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, oH, oW,
                                         int(groups), _stream(dev))

@@ -16,7 +16,9 @@
 // that reads the input directly.  The fp32 sum runs in (ic, kh, kw) order
 // with fused multiply-adds in both.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
+#include "gemm_core.hpp"
 #include "index_math.hpp"
 #include "launch.hpp"
 
@@ -83,6 +85,80 @@ __global__ __launch_bounds__(256) void conv_direct_tiled_kernel(ConvDirectArgs p
   }
 }
 
+// Depthwise K x K, stride 1, "same" padding (K odd, pad (K-1)/2), width a
+// multiple of 4 and at most 256: no LDS and no barriers.  A thread computes
+// an OR x 4 output block.  The threads of an output row band sit in
+// consecutive lanes, one per 4-column chunk, in groups of TWP lanes (the
+// chunk count rounded up to a power of two, so a group never straddles a
+// wave).  Each thread loads its chunk of the K+OR-1 input rows with one
+// 16-byte load per row, and takes the (K-1)/2 columns on either side from
+// its neighbours' chunks by lane shuffles; the lanes at the row ends (and
+// the idle lanes past the last chunk) supply the zero padding.  So every
+// input element is loaded about (K+OR-1)/OR times and never across lanes.
+template <int K, int OR>
+__global__ __launch_bounds__(256) void conv_dw_rows_kernel(ConvDirectArgs p, uint32_t nthreads,
+                                                           int twp, FastDiv div_plane,
+                                                           FastDiv div_twp) {
+  constexpr int PADK = (K - 1) / 2;
+  static_assert(K % 2 == 1 && PADK <= 4, "odd K up to 9");
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  // Threads past the end still take part in the shuffles (their lanes
+  // carry zeros) and simply store nothing.
+  const uint32_t g = gid < nthreads ? gid : nthreads - 1;
+  const uint32_t plane = fdiv(g, div_plane);  // (b, oc)
+  const uint32_t t = g - plane * div_plane.d;
+  const uint32_t ty = fdiv(t, div_twp);
+  const int tx = (int)(t - ty * div_twp.d);
+  const int oh0 = OR * (int)ty, ow0 = 4 * tx;
+  const bool live = gid < nthreads && ow0 < p.OW;
+  const int oc = (int)(plane % (uint32_t)p.OC);
+  const int b = (int)(plane / (uint32_t)p.OC);
+  const int c = oc / p.OCg;  // the one input channel of this output channel
+  const int H = p.H, W = p.W;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.x + ((size_t)b * p.IC + c) * H * W, (int64_t)H * W);
+  float wk[K * K];
+#pragma unroll
+  for (int i = 0; i < K * K; ++i) wk[i] = p.w[(size_t)oc * K * K + i];
+  float acc[OR][4] = {};
+#pragma unroll
+  for (int r = 0; r < K + OR - 1; ++r) {
+    const int iy = oh0 - PADK + r;
+    const bool ok = live && (unsigned)iy < (unsigned)H;
+    const f32x4 q = Vec<4>::load(rs, ok ? (uint32_t)(iy * W + ow0) * 4u : kOOB);
+    // row[i] is input column ow0 - PADK + i
+    float row[4 + 2 * PADK];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) row[PADK + e] = q[e];
+#pragma unroll
+    for (int e = 0; e < PADK; ++e) {
+      const float left = __shfl_up(q[4 - PADK + e], 1, twp);
+      const float right = __shfl_down(q[e], 1, twp);
+      row[e] = tx > 0 ? left : 0.0f;
+      row[4 + PADK + e] = tx < twp - 1 ? right : 0.0f;
+    }
+    // input row r feeds output rows oy = r - kh for kh = 0..K-1
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh) {
+      const int oy = r - kh;
+      if (oy < 0 || oy >= OR) continue;
+#pragma unroll
+      for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+        for (int ox = 0; ox < 4; ++ox)
+          acc[oy][ox] = fmaf(wk[kh * K + kw], row[ox + kw], acc[oy][ox]);
+    }
+  }
+  if (!live) return;
+  const float bv = p.bias ? p.bias[oc] : 0.0f;
+  float* o = p.out + (size_t)plane * p.OH * p.OW;
+#pragma unroll
+  for (int oy = 0; oy < OR; ++oy)
+    if (oh0 + oy < p.OH) {
+      const f32x4 v = {acc[oy][0] + bv, acc[oy][1] + bv, acc[oy][2] + bv, acc[oy][3] + bv};
+      *reinterpret_cast<f32x4*>(o + (oh0 + oy) * p.OW + ow0) = v;
+    }
+}
+
 __global__ __launch_bounds__(256) void conv_direct_kernel(ConvDirectArgs p) {
   const int P = p.OH * p.OW;
   const int pix = blockIdx.x * 256 + threadIdx.x;
@@ -134,6 +210,27 @@ hipError_t launch_conv2d_direct(const ConvProblem& q, hipStream_t stream) {
   a.ICg = q.IC / q.groups;
   a.OCg = q.OC / q.groups;
   a.div_ow = make_fastdiv((uint32_t)q.OW);
+  // one input channel per output channel, K x K odd with "same" padding,
+  // stride and dilation 1, width a multiple of 4 up to 256, aligned tensors
+  const int K = q.KH;
+  if (a.ICg == 1 && q.KW == K && (K == 3 || K == 5 || K == 7) && q.pH == (K - 1) / 2 &&
+      q.pW == (K - 1) / 2 && q.sH == 1 && q.sW == 1 && q.dH == 1 && q.dW == 1 && q.W % 4 == 0 &&
+      q.W <= 256 && (((uintptr_t)q.x | (uintptr_t)q.out) & 15) == 0) {
+    constexpr int OR = 2;  // output rows per thread
+    int twp = 1;
+    while (twp < q.OW / 4) twp *= 2;
+    const uint32_t th = ((uint32_t)q.OH + OR - 1) / OR;
+    const uint32_t n = (uint32_t)q.B * (uint32_t)q.OC * th * (uint32_t)twp;
+    const dim3 grid((n + 255) / 256);
+    const FastDiv dp = make_fastdiv(th * (uint32_t)twp), dt = make_fastdiv((uint32_t)twp);
+    if (K == 3)
+      hipLaunchKernelGGL((conv_dw_rows_kernel<3, OR>), grid, dim3(256), 0, stream, a, n, twp, dp, dt);
+    else if (K == 5)
+      hipLaunchKernelGGL((conv_dw_rows_kernel<5, OR>), grid, dim3(256), 0, stream, a, n, twp, dp, dt);
+    else
+      hipLaunchKernelGGL((conv_dw_rows_kernel<7, OR>), grid, dim3(256), 0, stream, a, n, twp, dp, dt);
+    return hipGetLastError();
+  }
   // input window of one output tile: rows / columns its taps touch
   const int64_t win_h = (int64_t)(kTileH - 1) * q.sH + (int64_t)(q.KH - 1) * q.dH + 1;
   const int64_t win_w = (int64_t)(kTileW - 1) * q.sW + (int64_t)(q.KW - 1) * q.dW + 1;

@@ -443,9 +443,12 @@ GCONV_SHAPES = [
     (1, 16, 30, 31, 24, 5, 5, (2, 1), 2, (1, 2), 4, True),  # small groups: direct
     (2, 12, 9, 9, 12, 1, 1, 1, 0, 1, 3, True),        # grouped 1x1: direct
     (1, 8, 70, 70, 8, 3, 3, 8, 1, 1, 8, True),        # stride 8: window > LDS, plain direct
-    (2, 16, 70, 130, 16, 3, 3, 1, 1, 1, 16, False),   # depthwise, several tiles per plane
-    (1, 8, 130, 130, 8, 3, 3, 1, 1, 1, 4, True),      # 2 channels per group, LDS tiles
+    (2, 16, 70, 130, 16, 3, 3, 1, 1, 1, 16, False),   # depthwise, width 130: LDS tiles
+    (1, 8, 130, 130, 8, 3, 3, 1, 1, 1, 4, True),      # 2 channels per group: LDS tiles
     (1, 4, 140, 140, 4, 3, 3, 8, 1, 1, 4, True),      # stride 8 on a large plane: plain direct
+    (1, 2, 6, 1100, 2, 3, 3, 1, 1, 1, 2, True),       # depthwise 3x3 "same", width % 4 == 0:
+    (2, 24, 13, 16, 24, 5, 5, 1, 2, 1, 24, True),     #   4x4 output blocks in registers
+    (1, 8, 21, 28, 16, 7, 7, 1, 3, 1, 8, False),      #   (5x5, 7x7 with channel multiplier 2)
 ]
 
 
@@ -459,11 +462,12 @@ def test_grouped_conv_full(B, IC, H, W, OC, KH, KW, stride, pad, dil, groups, ha
                 IC // groups * KH * KW, 1.0, f"grouped conv g={groups}")
 
 
-@pytest.mark.parametrize("groups,OC", [(2, 128), (8, 256), (64, 64), (16, 32)])
-def test_grouped_conv_integer_bitwise(groups, OC):
-    say(f"conv2d_gemm_f32 integer groups={groups}")
+@pytest.mark.parametrize("groups,OC,W", [(2, 128, 14), (8, 256, 14), (64, 64, 14), (16, 32, 14),
+                                          (32, 32, 16)])
+def test_grouped_conv_integer_bitwise(groups, OC, W):
+    say(f"conv2d_gemm_f32 integer groups={groups} W={W}")
     IC = 64 if groups <= 8 else groups
-    x, w, bias = gen((2, IC, 15, 14), 98, "I"), gen((OC, IC // groups, 3, 3), 99, "I"), gen((OC,), 100, "I")
+    x, w, bias = gen((2, IC, 15, W), 98, "I"), gen((OC, IC // groups, 3, 3), 99, "I"), gen((OC,), 100, "I")
     out = run_gconv(x, w, bias, 1, 1, 1, groups)
     check_bitwise(out, oracle.conv2d_grouped(x, w, bias, 1, 1, 1, groups), f"grouped integer g={groups}")
 
