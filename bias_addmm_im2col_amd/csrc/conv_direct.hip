@@ -1,20 +1,24 @@
 // conv_direct.hip -- grouped / depthwise NCHW conv whose per-group GEMM is
 // too small for the matrix cores (fewer than 32 output channels or 32 taps
-// per group, e.g. depthwise), computed directly: one thread per output
-// element, summing the IC/G input channels of its group over the
-// (kh, kw) taps.  The conv page keeps grouped and depthwise convs on
-// direct kernels ("et_vk conv2d: route standard (groups==1) conv through
-// an im2col tiled GEMM", Solution paragraph); this is that path on gfx950.
-//
-// Memory-bound.  The main kernel gives a block a 32-row x 64-column tile of
-// one (image, output channel) plane: for each input channel of the group it
-// stages the input rows and columns the tile's taps touch (with the halo,
-// zero-filled outside the input) in LDS with coalesced loads all in flight
-// at once, then each thread sums its outputs' taps from LDS; the weights
-// are uniform across the block (scalar loads).  Tiles whose input window
-// would exceed 64 KB of LDS (large strides or dilations) use a plain kernel
-// that reads the input directly.  The fp32 sum runs in (ic, kh, kw) order
-// with fused multiply-adds in both.
+// per group, e.g. depthwise), computed directly, each output summing the
+// IC/G input channels of its group over the (kh, kw) taps.  The conv page
+// keeps grouped and depthwise convs on direct kernels ("et_vk conv2d: route
+// standard (groups==1) conv through an im2col tiled GEMM", Solution
+// paragraph); this is that path on gfx950.  Memory-bound; three kernels:
+//  * conv_dw_rows_kernel -- one input channel per output channel, odd
+//    K x K with same padding at stride 1, rows of 4k <= 256 floats: 2 x 4
+//    output blocks per thread from registers, halo columns by lane
+//    shuffles, no LDS (see the kernel);
+//  * conv_direct_tiled_kernel -- otherwise: a block owns a 32-row x
+//    64-column tile of one (image, output channel) plane; for each input
+//    channel of the group it stages the input rows and columns the tile's
+//    taps touch (with the halo, zero-filled outside the input) in LDS with
+//    coalesced loads all in flight at once, then each thread sums its
+//    outputs' taps from LDS; the weights are uniform across the block;
+//  * conv_direct_kernel -- one thread per output reading the input
+//    directly, for tiles whose input window would exceed 64 KB of LDS
+//    (large strides or dilations).
+// The fp32 sum runs in (ic, kh, kw) order with fused multiply-adds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
