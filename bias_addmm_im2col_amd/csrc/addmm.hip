@@ -176,6 +176,7 @@ typedef Tile<128, 128, 64, 2, 4, 2, 2> T128x128K2;
 typedef Tile<128, 64, 64, 4, 2, 2, 2> T128x64K2;
 typedef Tile<64, 64, 64, 2, 2, 2, 2> T64x64K2;
 typedef Tile<64, 64, 128, 2, 2, 4, 2> T64x64K4;
+typedef Tile<32, 128, 32, 1, 4, 1, 2> T32x128;
 
 // The host planner's table must describe exactly these tiles.
 template <class T>
@@ -186,7 +187,8 @@ constexpr bool same_tile(int cfg) {
 static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x64) &&
                   same_tile<T64x128>(TILE_64x128) && same_tile<T64x64>(TILE_64x64) &&
                   same_tile<T128x128K2>(TILE_128x128_K2) && same_tile<T128x64K2>(TILE_128x64_K2) &&
-                  same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
+                  same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4) &&
+                  same_tile<T32x128>(TILE_32x128),
               "tile table out of sync with the compiled tiles");
 
 template <class T, int VA, int VB, int MODE, bool WNK = false, int AK = A_ROWS>
@@ -239,6 +241,8 @@ static hipError_t launch_cfg(int cfg, const AddmmArgs& a, int nblocks, bool va, 
       return launch_vec<T64x64K2, TILE_64x64_K2, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_64x64_K4:
       return launch_vec<T64x64K4, TILE_64x64_K4, MODE, WNK, AK>(a, nblocks, va, vb, s);
+    case TILE_32x128:
+      return launch_vec<T32x128, TILE_32x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
     default:
       return launch_vec<T128x128, TILE_128x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
   }

@@ -266,6 +266,7 @@ typedef Tile<128, 128, 64, 2, 4, 2, 1> T128x128K2;
 typedef Tile<128, 64, 64, 4, 2, 2, 2> T128x64K2;
 typedef Tile<64, 64, 64, 2, 2, 2, 2> T64x64K2;
 typedef Tile<64, 64, 128, 2, 2, 4, 2> T64x64K4;
+typedef Tile<32, 128, 32, 1, 4, 1, 2> T32x128;
 
 template <class T>
 constexpr bool same_tile(int cfg) {
@@ -275,7 +276,8 @@ constexpr bool same_tile(int cfg) {
 static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x64) &&
                   same_tile<T64x128>(TILE_64x128) && same_tile<T64x64>(TILE_64x64) &&
                   same_tile<T128x128K2>(TILE_128x128_K2) && same_tile<T128x64K2>(TILE_128x64_K2) &&
-                  same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4),
+                  same_tile<T64x64K2>(TILE_64x64_K2) && same_tile<T64x64K4>(TILE_64x64_K4) &&
+                  same_tile<T32x128>(TILE_32x128),
               "tile table out of sync with the compiled tiles");
 
 // Valid taps of one axis on output phase r: k in [0, KK) with
@@ -321,6 +323,7 @@ hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int mt, int groups, 
     case TILE_128x64_K2: return launch_phases<T128x64K2>(a, nph, mt, groups, s);
     case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, mt, groups, s);
     case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, mt, groups, s);
+    case TILE_32x128: return launch_phases<T32x128>(a, nph, mt, groups, s);
     default: return launch_phases<T128x128>(a, nph, mt, groups, s);
   }
 }

@@ -96,6 +96,16 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
     return workers > 0 ? make_stream(cfg, M, N, K, workers) : make(cfg, M, N, K, splits);
 
   const int nkt = cdiv(K, 32);  // k-tiles of depth 32
+  if (M <= 32) {
+    // A 64-row tile would leave at least half its rows idle: 32 x 128
+    // tiles, with K split across blocks only when they cannot give half
+    // the CUs a block and K is deep (at least 8 k-tiles per slice).
+    const int64_t t = tiles_of(TILE_32x128, M, N);
+    if (t >= kNumCUs / 2 || nkt <= 8) return make(TILE_32x128, M, N, K, 1);
+    int s = (int)((kNumCUs + t - 1) / t);
+    if (s > nkt / 8) s = nkt / 8;
+    return make(TILE_32x128, M, N, K, s < 1 ? 1 : s);
+  }
   const int64_t t128 = tiles_of(TILE_128x128, M, N);
   if (t128 >= 2 * kNumCUs) return make(TILE_128x128, M, N, K, 1);
   if (t128 >= (3 * kNumCUs) / 4 && nkt >= 48) {

@@ -18,18 +18,19 @@ enum TileCfg {
   TILE_128x64_K2 = 5,   // BK 64, 16 waves
   TILE_64x64_K2 = 6,    // BK 64, 8 waves
   TILE_64x64_K4 = 7,    // BK 128, 16 waves
-  TILE_NCFG = 8
+  TILE_32x128 = 8,      // BK 32, 4 waves, 32x32 per wave: GEMMs with M <= 32
+  TILE_NCFG = 9
 };
 
-constexpr int kTileBM[TILE_NCFG] = {128, 128, 64, 64, 128, 128, 64, 64};
-constexpr int kTileBN[TILE_NCFG] = {128, 64, 128, 64, 128, 64, 64, 64};
-constexpr int kTileBK[TILE_NCFG] = {32, 32, 32, 32, 64, 64, 64, 128};
-constexpr int kTileWaves[TILE_NCFG] = {8, 8, 8, 4, 16, 16, 8, 16};
-constexpr int kTileKGroups[TILE_NCFG] = {1, 1, 1, 1, 2, 2, 2, 4};
+constexpr int kTileBM[TILE_NCFG] = {128, 128, 64, 64, 128, 128, 64, 64, 32};
+constexpr int kTileBN[TILE_NCFG] = {128, 64, 128, 64, 128, 64, 64, 64, 128};
+constexpr int kTileBK[TILE_NCFG] = {32, 32, 32, 32, 64, 64, 64, 128, 32};
+constexpr int kTileWaves[TILE_NCFG] = {8, 8, 8, 4, 16, 16, 8, 16, 4};
+constexpr int kTileKGroups[TILE_NCFG] = {1, 1, 1, 1, 2, 2, 2, 4, 1};
 // Configurations compiled with the K-slice and stream schedules (the
 // others would exceed their register budget with the extra state).
-constexpr bool kTileSlices[TILE_NCFG] = {true, true, true, true, false, true, true, true};
-constexpr bool kTileStream[TILE_NCFG] = {true, true, true, true, false, true, true, false};
+constexpr bool kTileSlices[TILE_NCFG] = {true, true, true, true, false, true, true, true, true};
+constexpr bool kTileStream[TILE_NCFG] = {true, true, true, true, false, true, true, false, true};
 constexpr int kNumCUs = 256;  // MI355X
 
 // How blocks map to work (the kernels' scheduling modes).

@@ -70,6 +70,8 @@ ADDMM_SHAPES = [
     (300, 517, 100, True, 0.25, 1.0),
     (256, 256, 512, False, 1.0, 1.0),
     (37, 1000, 41, True, 1.0, 1.0),
+    (32, 600, 1000, True, 1.0, 1.0),     # M <= 32: 32-row tiles
+    (7, 4096, 300, False, 1.0, 2.0),     # M <= 32, deep K: 32-row tiles in K slices
 ]
 
 
@@ -267,8 +269,9 @@ def test_repeated_launches_are_deterministic():
 # split over 2 wave groups (BK 64); 7 = 64x64 over 4 groups (BK 128).
 # "cfg,S": S K slices on separate blocks (S == 2: two-piece exchange,
 # S > 2: atomic adds); "cfg,sP": stream over P blocks (two-piece exchange).
-TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "0,3", "1,2", "2,4", "3,5", "0,64",
-              "4,2", "6,3", "7,2", "3,s7", "0,s2", "4,s3", "6,s5", "2,s9", "1,s4", "7,s1"]
+TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "0,3", "1,2", "2,4", "3,5", "0,64",
+              "4,2", "6,3", "7,2", "8,2", "8,3", "3,s7", "0,s2", "4,s3", "6,s5", "2,s9", "1,s4",
+              "7,s1", "8,s5"]
 
 
 @pytest.mark.parametrize("spec", TILE_SPECS)
@@ -472,7 +475,7 @@ def test_grouped_conv_integer_bitwise(groups, OC, W):
     check_bitwise(out, oracle.conv2d_grouped(x, w, bias, 1, 1, 1, groups), f"grouped integer g={groups}")
 
 
-@pytest.mark.parametrize("spec", ["1", "3", "6,2", "3,s7", "7,3"])
+@pytest.mark.parametrize("spec", ["1", "3", "6,2", "3,s7", "7,3", "8", "8,2"])
 def test_grouped_gemm_forced_tile_configs(spec, monkeypatch):
     monkeypatch.setenv("BAIM_TILE", spec)
     say(f"BAIM_TILE={spec} grouped conv")

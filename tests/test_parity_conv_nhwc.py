@@ -77,8 +77,8 @@ def test_nhwc_conv_integer_bitwise(IC, OC, k, stride):
                   "nhwc integer")
 
 
-TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "0,3", "2,4", "4,2", "7,2", "3,s7", "1,s4",
-              "6,s5"]
+TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "0,3", "2,4", "4,2", "7,2", "3,s7",
+              "1,s4", "6,s5", "8,s3"]
 
 
 @pytest.mark.parametrize("spec", TILE_SPECS)

@@ -103,7 +103,7 @@ def test_convt_integer_bitwise(stride, k):
                   f"convT integer s={stride}")
 
 
-@pytest.mark.parametrize("spec", ["0", "1", "2", "3", "4", "5", "6", "7"])
+@pytest.mark.parametrize("spec", ["0", "1", "2", "3", "4", "5", "6", "7", "8"])
 def test_convt_forced_tile_configs(spec, monkeypatch):
     monkeypatch.setenv("BAIM_TILE", spec)
     say(f"BAIM_TILE={spec} conv_transpose2d_f32")

@@ -50,6 +50,10 @@ int main() {
   const GemmPlan st = plan_gemm(256, 12544, 2304, "1,s256");
   if (st.mode != MODE_STREAM || st.workers != 256) bad += printf("stream override\n") > 0;
   if (plan_gemm(64, 64, 2304, "1,s256").mode != MODE_TILE) bad += printf("stream fallback\n") > 0;
+  // M <= 32 takes the 32-row tile
+  if (plan_gemm(32, 12544, 288, nullptr).cfg != TILE_32x128) bad += printf("32-row tile\n") > 0;
+  if (plan_gemm(7, 4096, 4096, nullptr).cfg != TILE_32x128) bad += printf("32-row tile 2\n") > 0;
+  if (plan_gemm(33, 4096, 4096, nullptr).cfg == TILE_32x128) bad += printf("33 rows\n") > 0;
   // K == 0 never splits
   if (plan_gemm(8, 8, 0, "0,4").splits != 1) bad += printf("K=0 split\n") > 0;
   if (bad) return 1;
