@@ -75,18 +75,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, only
-    while the kernel sources are the ones the counters were taken on."""
+def load_counters(kernel: str):
+    """(HBM bytes per launch, MFMA-busy fraction) from the committed
+    rocprofv3 counter runs, only while the kernel sources are the ones the
+    counters were taken on; (None, None) otherwise."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     if t.get("kernel_source_sha") != kernel_source_hash():
-        return None
+        return None, None
     entry = t.get("kernels", {}).get(kernel)
-    return None if entry is None else entry.get("bytes_per_launch")
+    if entry is None:
+        return None, None
+    return entry.get("bytes_per_launch"), entry.get("mfma_busy")
 
 
 def raw_call(torch, fname, *args):
@@ -353,7 +356,7 @@ def main():
     dom = max(k_time, key=k_time.get)
     achieved = k_flops[dom] / (k_time[dom] * 1e-3) / 1e12
     n_launch = k_launch[dom]
-    traffic = load_traffic(dom)
+    traffic, mfma_busy = load_counters(dom)
 
     widened = time_widened(torch, baim, I)
 
@@ -391,6 +394,10 @@ def main():
             "launches_per_step": n_launch,
             "flops_per_launch_avg": k_flops[dom] // n_launch,
             "avg_launch_us": round(k_time[dom] / n_launch * 1e3, 2),
+            # from the same committed counter runs as `traffic` (null likewise)
+            "mfma_busy": mfma_busy,
+            "hbm_gbytes_per_s": (None if traffic is None
+                                 else round(traffic / (k_time[dom] / n_launch * 1e-3) / 1e9, 1)),
         },
         "cpu_baseline": cpu,
         "widened": widened,
