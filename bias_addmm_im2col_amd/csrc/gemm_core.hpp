@@ -303,6 +303,15 @@ __device__ __forceinline__ bool reduce_k_groups(Accum<T>& acc, float* smem, cons
 // loads issued an iteration earlier.  The loop is unrolled by two so that
 // register slots are compile-time indices.
 //
+// That wait is only exact when no branch skips the loads: the compiler
+// counts outstanding loads per path and, where a path may have issued fewer,
+// waits for all of them, i.e. also for tile t+2.  Row and column loaders
+// therefore always fetch; the last two iterations of a range fetch tile
+// t_end - 1 again into a slot that is never written to LDS.  The im2col
+// gathers keep the skipping form: their ranges are short pieces of a
+// tile (stream scheduling), where the extra loads cost more than the
+// exact wait gains (measured on the 3x3 convs).
+//
 // A loader may also keep per-k-tile metadata in LDS: meta(t) writes the
 // metadata of tile t into slot t % 4 and is called PF + 1 tiles ahead of
 // load(t).  The slot it overwrites was last read by load(t - 4), several
@@ -336,10 +345,16 @@ struct MainLoop {
     // within the same iteration.
     constexpr int NEXT = T::PF == 2 ? 1 - S : 0;
     if (T::PF == 2) {
-      if (t + 2 < t_end) fetch<S>(t + 2);
+      if (!BL::kHasMeta)
+        fetch<S>(t + 2 < t_end ? t + 2 : t_end - 1);
+      else if (t + 2 < t_end)
+        fetch<S>(t + 2);
       if (BL::kHasMeta && t + 3 < t_end) bl.meta(t + 3);
     } else {
-      if (t + 1 < t_end) fetch<0>(t + 1);
+      if (!BL::kHasMeta)
+        fetch<0>(t + 1 < t_end ? t + 1 : t_end - 1);
+      else if (t + 1 < t_end)
+        fetch<0>(t + 1);
       if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
     }
     mma_tile<T, BL::kBTransposed>(acc, cur, cur + T::A_FLOATS, ws, lane);
@@ -361,7 +376,8 @@ __device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_be
     __syncthreads();
   }
   ml.template fetch<0>(t_begin);
-  if (T::PF == 2 && t_begin + 1 < t_end) ml.template fetch<1>(t_begin + 1);
+  if (T::PF == 2 && (!BL::kHasMeta || t_begin + 1 < t_end))
+    ml.template fetch<1>(t_begin + 1 < t_end ? t_begin + 1 : t_begin);
   ml.template put<0>(t_begin, smem);
   __syncthreads();
   if (T::PF == 2) {
