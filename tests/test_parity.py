@@ -185,6 +185,35 @@ def test_conv_integer_bitwise(stride, pad, dil):
     check_bitwise(out, oracle.conv2d(x, w, bias, stride, pad, dil), "conv integer")
 
 
+# Output rows a multiple of 4 wide (whole 16-byte groups of output columns),
+# pads up to 6 on 4-wide rows, one-row inputs and a 64-float input, where
+# every tap row is the first or last row of the tensor.
+ROW4_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, dil, bias
+    (1, 4, 4, 4, 3, 3, 3, 1, 1, 1, True),
+    (2, 8, 12, 16, 40, 3, 3, 1, 1, 1, True),
+    (1, 4, 6, 8, 9, 3, 3, 1, 2, 2, False),
+    (2, 12, 9, 20, 70, 5, 5, 1, 2, 1, True),
+    (1, 16, 7, 4, 33, 1, 7, 1, (0, 3), 1, True),
+    (3, 20, 5, 12, 136, 3, 5, 1, (1, 2), 1, True),
+    (1, 4, 1, 8, 5, 1, 3, 1, (0, 1), 1, True),
+    (2, 8, 15, 12, 24, 3, 3, (2, 1), 1, 1, True),
+    (1, 4, 3, 4, 8, 1, 9, 1, (0, 6), 1, True),
+]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,has_bias", ROW4_SHAPES)
+def test_conv_rows_of_four(B, IC, H, W, OC, KH, KW, stride, pad, dil, has_bias):
+    say(f"conv2d_gemm_f32 x=[{B},{IC},{H},{W}] w=[{OC},{IC},{KH},{KW}] s={stride} p={pad} d={dil}")
+    x, w = gen((B, IC, H, W), 60), gen((OC, IC, KH, KW), 61)
+    bias = gen((OC,), 62) if has_bias else None
+    out = run_conv(x, w, bias, stride, pad, dil)
+    check_close(out, oracle.conv2d(x, w, bias, stride, pad, dil), IC * KH * KW, 1.0, "conv rows of 4")
+    xi, wi, bi = gen((B, IC, H, W), 63, "I"), gen((OC, IC, KH, KW), 64, "I"), gen((OC,), 65, "I")
+    check_bitwise(run_conv(xi, wi, bi, stride, pad, dil), oracle.conv2d(xi, wi, bi, stride, pad, dil),
+                  "conv rows of 4 integer")
+
+
 def test_conv_1x1_equals_addmm():
     """P-4 on the GPU: a 1x1 conv and addmm(W, x[b]) agree bit for bit on
     integer inputs."""
@@ -310,6 +339,13 @@ def test_conv_forced_tile_configs(spec, monkeypatch):
     x, w, bias = gen((2, 40, 19, 17), 49, "I"), gen((72, 40, 3, 3), 50, "I"), gen((72,), 51, "I")
     out = run_conv(x, w, bias, 1, 1, 1)
     check_bitwise(out, oracle.conv2d(x, w, bias, 1, 1, 1), f"conv integer {spec}")
+    say(f"BAIM_TILE={spec} conv2d_gemm_f32 rows of 4")
+    x, w, bias = gen((2, 24, 13, 20), 52), gen((136, 24, 3, 3), 53), gen((136,), 54)
+    check_close(run_conv(x, w, bias, 1, 1, 1), oracle.conv2d(x, w, bias, 1, 1, 1), 24 * 9, 1.0,
+                f"conv rows of 4 {spec}")
+    x, w, bias = gen((2, 24, 13, 20), 55, "I"), gen((136, 24, 3, 3), 56, "I"), gen((136,), 57, "I")
+    check_bitwise(run_conv(x, w, bias, 1, 2, 2), oracle.conv2d(x, w, bias, 1, 2, 2),
+                  f"conv rows of 4 integer {spec}")
 
 
 @pytest.mark.parametrize("spec", ["3,s7", "0,2", "6,s5", "1,s4"])
@@ -441,6 +477,7 @@ GCONV_SHAPES = [
     (2, 64, 17, 19, 128, 3, 3, 1, 1, 1, 2, True),     # GEMM, 64 out ch / group
     (2, 128, 15, 13, 128, 3, 3, 2, 1, 1, 4, True),    # GEMM, 32 / group, stride 2
     (1, 96, 14, 14, 96, 3, 3, 1, 2, 2, 3, False),     # GEMM, dilation 2
+    (2, 64, 12, 16, 128, 3, 3, 1, 1, 1, 4, True),     # GEMM, rows of 16
     (2, 32, 17, 19, 32, 3, 3, 1, 1, 1, 32, True),     # depthwise: direct
     (2, 8, 21, 20, 16, 3, 3, 1, 1, 1, 8, True),       # channel multiplier 2: direct
     (1, 16, 30, 31, 24, 5, 5, (2, 1), 2, (1, 2), 4, True),  # small groups: direct
