@@ -13,7 +13,7 @@ through the C ABI on torch's current stream, inputs already resident in HBM:
   ragged_577      addmm 577x1024 @ 1024x4096, self [M,N]
 
 flops = 2*M*N*K per launch (the conv's bias adds are not counted).  Prints
-ONE JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+ONE JSON line.  ``--gpus`` above 1 is refused: the measurement is of one GPU.
 """
 from __future__ import annotations
 
@@ -297,8 +297,9 @@ def cpu_baseline(cases, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build measures one MI355X "
-              "(the path needs no collective; see the sharding note in the design doc).",
+        print(f"bench.py: --gpus {args.gpus} is not supported: bench.py measures one MI355X. "
+              "The path needs no collective: addmm shards by rows of mat1 and conv by batch or "
+              "output channels, each GPU running this same kernel on its share.",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -394,8 +395,14 @@ def main():
             "launches_per_step": n_launch,
             "flops_per_launch_avg": k_flops[dom] // n_launch,
             "avg_launch_us": round(k_time[dom] / n_launch * 1e3, 2),
-            # from the same committed counter runs as `traffic` (null likewise)
+            # from the same committed counter runs as `traffic` (null likewise).
+            # MFMA-busy cycles over elapsed cycles is the fraction of the
+            # clock-adjusted peak 256*256*f_clk at whatever clock the chip
+            # held; the clock it implies is achieved / (256*256*busy).
             "mfma_busy": mfma_busy,
+            "frac_of_clock_adjusted_peak": mfma_busy,
+            "implied_clock_ghz": (None if not mfma_busy
+                                  else round(achieved * 1e12 / (256 * 256 * mfma_busy) / 1e9, 3)),
             "hbm_gbytes_per_s": (None if traffic is None
                                  else round(traffic / (k_time[dom] / n_launch * 1e-3) / 1e9, 1)),
         },
