@@ -338,8 +338,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_case_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-                   for i in range(len(cases))]
+    launch_ms = [sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+                 for i in range(len(cases))]
+    per_case_ms = [sum(t) / len(t) for t in launch_ms]
     flops_step = sum(cs.flops for cs in cases)
     value = flops_step * args.steps / wall / 1e12
 
@@ -347,9 +348,11 @@ def main():
     k_time = {}
     k_flops = {}
     k_launch = {}
-    for cs, ms in zip(cases, per_case_ms):
+    for cs, ms, ts in zip(cases, per_case_ms, launch_ms):
         tf = cs.flops / (ms * 1e-3) / 1e12
+        # "us" is the mean over the timed steps; median and minimum beside it
         case_rows.append({"case": cs.name, "op": cs.op, "kernel": cs.kernel, "us": round(ms * 1e3, 2),
+                          "us_median": round(ts[len(ts) // 2] * 1e3, 2), "us_min": round(ts[0] * 1e3, 2),
                           "tflops": round(tf, 2), "frac_of_peak": round(tf / PEAK_TFLOPS, 4)})
         k_time[cs.kernel] = k_time.get(cs.kernel, 0.0) + ms
         k_flops[cs.kernel] = k_flops.get(cs.kernel, 0) + cs.flops
