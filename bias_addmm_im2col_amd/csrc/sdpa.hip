@@ -104,7 +104,7 @@ __device__ __forceinline__ void scale_rows(f32x16 (&o)[ND], float f, float* slot
 }
 
 template <int DP, int QW, int KW, int NB, bool MASK, int MV>
-__global__ __launch_bounds__(256, DP <= 64 ? 2 : 1) void sdpa_kernel(SdpaArgs a) {
+__global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) void sdpa_kernel(SdpaArgs a) {
   using S = SdpaShape<DP, QW, KW, NB>;
   __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
   float* Ks = smem;
@@ -362,13 +362,14 @@ hipError_t launch_cfg(SdpaArgs a, bool mask_vec, hipStream_t s) {
 
 template <int DP>
 hipError_t launch_dp(const SdpaArgs& a, int cfg, bool mask_vec, hipStream_t s) {
-  static_assert(kSdpaQW[SDPA_Q4] == 4 && kSdpaKW[SDPA_Q4] == 1 && kSdpaNB[SDPA_Q4] == 2, "");
-  static_assert(kSdpaQW[SDPA_Q2K2] == 2 && kSdpaKW[SDPA_Q2K2] == 2 && kSdpaNB[SDPA_Q2K2] == 1, "");
-  static_assert(kSdpaQW[SDPA_K4] == 1 && kSdpaKW[SDPA_K4] == 4 && kSdpaNB[SDPA_K4] == 1, "");
+  constexpr int NBQ4 = sdpa_nb(SDPA_Q4, DP);
+  static_assert(kSdpaQW[SDPA_Q4] == 4 && kSdpaKW[SDPA_Q4] == 1, "");
+  static_assert(kSdpaQW[SDPA_Q2K2] == 2 && kSdpaKW[SDPA_Q2K2] == 2 && sdpa_nb(SDPA_Q2K2, DP) == 1, "");
+  static_assert(kSdpaQW[SDPA_K4] == 1 && kSdpaKW[SDPA_K4] == 4 && sdpa_nb(SDPA_K4, DP) == 1, "");
   switch (cfg) {
     case SDPA_Q2K2: return launch_cfg<DP, 2, 2, 1>(a, mask_vec, s);
     case SDPA_K4: return launch_cfg<DP, 1, 4, 1>(a, mask_vec, s);
-    default: return launch_cfg<DP, 4, 1, 2>(a, mask_vec, s);
+    default: return launch_cfg<DP, 4, 1, NBQ4>(a, mask_vec, s);
   }
 }
 
@@ -387,7 +388,7 @@ hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream) {
   a.scale2 = p.scale * kLog2e;
   a.qblocks = 0;
   a.nblocks = p.BH;
-  const int cfg = plan_sdpa(p.BH, p.Sq, p.Skv, getenv("BAIM_SDPA"));
+  const int cfg = plan_sdpa(p.BH, p.Sq, p.Skv, p.D, getenv("BAIM_SDPA"));
   // 16-byte mask loads need rows that start on 16-byte boundaries.
   const bool mask_vec = p.mask && p.Skv % 4 == 0 && ((uintptr_t)p.mask & 15) == 0;
   if (p.D <= 32) return launch_dp<32>(a, cfg, mask_vec, stream);
