@@ -24,7 +24,10 @@
 // weight offset}.  The weight is small and cache-resident, so its A tile
 // uses 4-byte loads; the input gather writes the transposed B tile with
 // 16-byte LDS stores.  The epilogue adds bias[oc] and stores to
-// out[b, oc, rh + sH*t, rw + sW*u].
+// out[b, oc, rh + sH*t, rw + sW*u].  When the tiles of all phases would
+// leave most CUs idle and K is deep, K is split over blocks instead: an
+// initialisation kernel writes bias[oc] into the output and each slice adds
+// its partial sums atomically (the summation order then varies run to run).
 #include <stdlib.h>
 
 #include <vector>
@@ -44,6 +47,7 @@ struct ConvTPhase {
   int Th, Tw;                      // outputs of the phase per image: rows, columns
   int N, K;                        // B*Th*Tw, ICg*nh*nw
   int tiles_n, nkt;
+  int kps;                         // k-tiles per K slice
   int nw;                          // valid taps along W
   int kh0, kw0, step_h, step_w;    // valid taps kh = kh0 + i*step_h, kw = kw0 + j*step_w
   int c0h, c0w, dlh, dlw;          // input row of tap i: t + c0h - i*dlh (same along W)
@@ -59,6 +63,8 @@ struct ConvTArgs {
   int ICg, OCg;
   int x_elems, w_elems;
   int tiles_m;
+  int splits;     // K slices per tile; above 1 they add into an output holding the bias
+  int slice_row;  // blocks per slice in a grid row: tiles_m * (largest phase's tiles_n)
   ConvTPhase ph[kMaxPhases];
 };
 
@@ -211,9 +217,13 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
   const int g = blockIdx.z;
   const int ntiles = a.tiles_m * P.tiles_n;
   const int lid = xcd_linear(blockIdx.x, gridDim.x);
-  if (lid >= ntiles) return;  // this phase has fewer tiles than the grid row
+  const int z = lid / a.slice_row, tile = lid - z * a.slice_row;
+  if (tile >= ntiles) return;  // this phase has fewer tiles than the grid row
+  const int tb = z * P.kps;
+  const int te = P.nkt < tb + P.kps ? P.nkt : tb + P.kps;
+  if (a.splits > 1 && tb >= te) return;  // empty slice: the output already holds the bias
   int tm, tn;
-  grouped_tile(lid, a.tiles_m, P.tiles_n, 8, tm, tn);
+  grouped_tile(tile, a.tiles_m, P.tiles_n, 8, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
   TImColLoader<T> bl;
   bl.init(a, P, n0, table, g);
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, 0, P.nkt, smem, ws, lane);
+  mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // + bias[oc]; column n = (b, t, u) goes to out[b, oc, rh + sH*t, rw + sW*u].
@@ -253,9 +263,21 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
         const int oc = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
         if (oc >= a.OCg) continue;
         const int ocx = g * a.OCg + oc;
-        a.out[obase[j] + (size_t)ocx * plane] = acc.c[i][j][r] + (a.bias ? a.bias[ocx] : 0.0f);
+        float* o = &a.out[obase[j] + (size_t)ocx * plane];
+        if (a.splits > 1)
+          unsafeAtomicAdd(o, acc.c[i][j][r]);
+        else
+          *o = acc.c[i][j][r] + (a.bias ? a.bias[ocx] : 0.0f);
       }
   }
+}
+
+// bias[oc] (or 0) into every output before K slices add their partial sums.
+__global__ __launch_bounds__(256) void convt_init_kernel(float* out, const float* bias, uint32_t total,
+                                                         FastDiv div_plane, uint32_t OC) {
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < total; i += stride)
+    out[i] = bias ? bias[fdiv(i, div_plane) % OC] : 0.0f;
 }
 
 typedef Tile<128, 128, 32, 2, 4, 1, 2> T128x128;
@@ -308,23 +330,23 @@ AxisTaps axis_taps(int r, int s, int p, int d, int KK) {
 }
 
 template <class T>
-hipError_t launch_phases(const ConvTArgs& a, int nph, int max_tiles_n, int groups, hipStream_t s) {
-  const dim3 grid(a.tiles_m * max_tiles_n, nph, groups);
+hipError_t launch_phases(const ConvTArgs& a, int nph, int groups, hipStream_t s) {
+  const dim3 grid(a.slice_row * a.splits, nph, groups);
   hipLaunchKernelGGL((conv_transpose_kernel<T>), grid, dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int mt, int groups, hipStream_t s) {
+hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int groups, hipStream_t s) {
   switch (cfg) {
-    case TILE_128x64: return launch_phases<T128x64>(a, nph, mt, groups, s);
-    case TILE_64x128: return launch_phases<T64x128>(a, nph, mt, groups, s);
-    case TILE_64x64: return launch_phases<T64x64>(a, nph, mt, groups, s);
-    case TILE_128x128_K2: return launch_phases<T128x128K2>(a, nph, mt, groups, s);
-    case TILE_128x64_K2: return launch_phases<T128x64K2>(a, nph, mt, groups, s);
-    case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, mt, groups, s);
-    case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, mt, groups, s);
-    case TILE_32x128: return launch_phases<T32x128>(a, nph, mt, groups, s);
-    default: return launch_phases<T128x128>(a, nph, mt, groups, s);
+    case TILE_128x64: return launch_phases<T128x64>(a, nph, groups, s);
+    case TILE_64x128: return launch_phases<T64x128>(a, nph, groups, s);
+    case TILE_64x64: return launch_phases<T64x64>(a, nph, groups, s);
+    case TILE_128x128_K2: return launch_phases<T128x128K2>(a, nph, groups, s);
+    case TILE_128x64_K2: return launch_phases<T128x64K2>(a, nph, groups, s);
+    case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, groups, s);
+    case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, groups, s);
+    case TILE_32x128: return launch_phases<T32x128>(a, nph, groups, s);
+    default: return launch_phases<T128x128>(a, nph, groups, s);
   }
 }
 
@@ -394,12 +416,53 @@ hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
   // planner's choice by 1.3-1.5x.  Smaller problems keep the GEMM plan.
   const int n_all = (int)(n_sum < 0x7FFFFFFF ? n_sum : 0x7FFFFFFF);
   const char* spec = getenv("BAIM_TILE");
+  const bool forced = spec && *spec;
   GemmPlan plan = plan_gemm(a.OCg, n_all, k_max, spec);
+  // K slices only from a "cfg,S" override here; the automatic choice follows.
+  int splits = forced && plan.mode == MODE_SLICES ? plan.splits : 1;
   const int64_t t64x128 = (int64_t)((a.OCg + 63) / 64) * ((n_all + 127) / 128);
-  if (!(spec && *spec) && t64x128 >= kNumCUs / 2) plan = plan_gemm(a.OCg, n_all, k_max, "2");
+  if (!forced && t64x128 >= kNumCUs / 2) plan = plan_gemm(a.OCg, n_all, k_max, "2");
   plan = plan_tiles_only(plan, a.OCg, n_all, k_max);
+  // Tiles of all phases and groups, and the deepest phase's k-tiles.
+  auto count = [&](int cfg, int64_t* tiles, int* nkt_max) {
+    const int bm = kTileBM[cfg], bn = kTileBN[cfg], bk = kTileBK[cfg];
+    *tiles = 0;
+    *nkt_max = 0;
+    for (const ConvTPhase& P : all) {
+      *tiles += (int64_t)((a.OCg + bm - 1) / bm) * ((P.N + bn - 1) / bn);
+      const int nkt = (P.K + bk - 1) / bk;
+      if (nkt > *nkt_max) *nkt_max = nkt;
+    }
+    *tiles *= q.groups;
+  };
+  int64_t tiles;
+  int nkt_max;
+  count(plan.cfg, &tiles, &nkt_max);
+  // Too few tiles to give half the CUs a block, and deep K: split K over
+  // 2..8 slices towards two blocks per CU, on the 8-wave 64x128 tile when
+  // there are more than 32 output channels per group (measured 3-5x faster
+  // than whole tiles on 7x7 -> 14x14 and 4x4 -> 8x8 upsamplings with
+  // K = 2048-4096).  The 200-tile 4x4 upsampling of 28x28 stays whole:
+  // there two slices measured 6% slower.
+  if (!forced && tiles < kNumCUs / 2 && nkt_max >= 16) {
+    if (a.OCg > 32) {
+      plan = plan_tiles_only(plan_gemm(a.OCg, n_all, k_max, "2"), a.OCg, n_all, k_max);
+      count(plan.cfg, &tiles, &nkt_max);
+    }
+    const int64_t want = (2 * kNumCUs + tiles - 1) / tiles;
+    splits = want < 2 ? 2 : (want > 8 ? 8 : (int)want);
+  }
   const int BN = kTileBN[plan.cfg], BK = kTileBK[plan.cfg];
   a.tiles_m = (a.OCg + kTileBM[plan.cfg] - 1) / kTileBM[plan.cfg];
+  a.splits = splits;
+  if (splits > 1) {
+    const uint32_t total = (uint32_t)((int64_t)q.B * q.OC * q.OH * q.OW);
+    const uint32_t gb = (total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u;
+    hipLaunchKernelGGL(convt_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias, total,
+                       make_fastdiv((uint32_t)(q.OH * q.OW)), (uint32_t)q.OC);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipError_t err = hipSuccess;
   for (int first = 0; first < nall && err == hipSuccess; first += kMaxPhases) {
     const int nph = nall - first < kMaxPhases ? nall - first : kMaxPhases;
@@ -408,10 +471,12 @@ hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
       ConvTPhase P = all[first + i];
       P.tiles_n = (P.N + BN - 1) / BN;
       P.nkt = (P.K + BK - 1) / BK;
+      P.kps = (P.nkt + splits - 1) / splits;
       if (P.tiles_n > max_tiles_n) max_tiles_n = P.tiles_n;
       a.ph[i] = P;
     }
-    err = launch_cfg(plan.cfg, a, nph, max_tiles_n, q.groups, stream);
+    a.slice_row = a.tiles_m * max_tiles_n;
+    err = launch_cfg(plan.cfg, a, nph, q.groups, stream);
   }
   return err;
 }

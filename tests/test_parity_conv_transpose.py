@@ -115,6 +115,46 @@ def test_convt_forced_tile_configs(spec, monkeypatch):
                   f"convT int {spec}")
 
 
+@pytest.mark.parametrize("spec", ["2,2", "2,3", "0,2", "3,4", "7,2", "8,3"])
+def test_convt_k_slices(spec, monkeypatch):
+    """K split over blocks that add into an output pre-filled with the bias:
+    several phases, a phase with no taps (1x1 kernel, stride 3), groups, and
+    more slices than some phases have k-tiles."""
+    monkeypatch.setenv("BAIM_TILE", spec)
+    for (B, IC, H, W, OC, KH, KW, stride, pad, opad, groups, dil) in [
+            (2, 64, 9, 7, 40, 4, 4, 2, 1, 0, 1, 1),
+            (1, 48, 5, 6, 33, 3, 3, 2, 1, 1, 1, 1),
+            (1, 96, 4, 4, 20, 1, 1, 3, 0, 2, 1, 1),
+            (2, 64, 6, 5, 32, 3, 3, 2, 1, 1, 4, 1),
+            (1, 40, 7, 7, 24, 3, 3, (3, 2), 2, (2, 1), 1, (1, 2))]:
+        say(f"BAIM_TILE={spec} conv_transpose2d_f32 x=[{B},{IC},{H},{W}] OC={OC} k=({KH},{KW}) "
+            f"s={stride} p={pad} op={opad} g={groups} d={dil}")
+        x, w = gen((B, IC, H, W), 16), gen((IC, OC // groups, KH, KW), 17)
+        b = gen((OC,), 18)
+        ref = (oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad) if groups == 1
+               else oracle_grouped(x, w, b, stride, pad, opad, groups, dil))
+        check_close(run(x, w, b, stride, pad, opad, groups, dil), ref, IC // groups * KH * KW, 1.0,
+                    f"convT slices {spec}")
+        xi, wi = gen((B, IC, H, W), 19, "I"), gen((IC, OC // groups, KH, KW), 20, "I")
+        refi = (oracle.conv_transpose2d(xi, wi, None, stride, pad, dil, opad) if groups == 1
+                else oracle_grouped(xi, wi, None, stride, pad, opad, groups, dil))
+        check_bitwise(run(xi, wi, None, stride, pad, opad, groups, dil), refi,
+                      f"convT slices integer {spec}")
+
+
+@pytest.mark.parametrize("B,IC,H,OC,k,stride,pad", [(1, 512, 7, 256, 4, 2, 1), (1, 256, 14, 40, 3, 2, 1),
+                                                  (2, 1024, 4, 24, 4, 2, 1)])
+def test_convt_small_grid_deep_k(B, IC, H, OC, k, stride, pad):
+    """Shapes whose tiles leave most CUs idle: the planner splits K itself."""
+    say(f"conv_transpose2d_f32 small grid x=[{B},{IC},{H},{H}] OC={OC} k={k} s={stride} p={pad}")
+    x, w, b = gen((B, IC, H, H), 21), gen((IC, OC, k, k), 22), gen((OC,), 23)
+    check_close(run(x, w, b, stride, pad), oracle.conv_transpose2d(x, w, b, stride, pad, 1, 0),
+                IC * k * k, 1.0, "convT small grid")
+    xi, wi, bi = gen((B, IC, H, H), 24, "I"), gen((IC, OC, k, k), 25, "I"), gen((OC,), 26, "I")
+    check_bitwise(run(xi, wi, bi, stride, pad), oracle.conv_transpose2d(xi, wi, bi, stride, pad, 1, 0),
+                  "convT small grid integer")
+
+
 @pytest.mark.parametrize("name", list(I.CONVT_CASES))
 def test_workload_convt(name):
     import bias_addmm_im2col_amd as baim
