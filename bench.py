@@ -215,15 +215,24 @@ class Case:
                 self.kernel = "baim::conv_dw_rows_kernel" if dw else "baim::conv_direct_tiled_kernel"
 
 
-def time_widened(torch, baim, I, warmup_s=0.05, iters=50):
+# The other addmm and conv configurations of the same metric (the small
+# 64x96x80 addmm, the FFN linear with self [N] and with a full self, the
+# 7x7 stride-4 stem): reported beside the step, not part of `value`.
+OTHER_CONFIG_CASES = ["addmm_small_64x96x80", "ffn_2048x768x3072_bias",
+                      "ffn_2048x768x3072_full_self", "stem_conv7x7_s4_768"]
+
+
+def time_widened(torch, baim, I, names=None, warmup_s=0.05, iters=50):
     """Ops beyond the step's workload (linear with weight [N,K], grouped and
-    depthwise conv, channels-last conv, transposed conv, attention), timed the same way but reported separately:
-    they are not part of `value`.  Each case
-    first runs for `warmup_s` seconds (clocks settle over ~20 ms after a
-    switch to new buffers)."""
+    depthwise conv, channels-last conv, transposed conv, attention), or the
+    cases `names`, timed the same way but reported separately: they are not
+    part of `value`.  Each case first runs for `warmup_s` seconds (clocks
+    settle over ~20 ms after a switch to new buffers)."""
     rows = []
-    for name in (list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.NHWC_CASES)
-                 + list(I.CONVT_CASES) + list(I.SDPA_CASES)):
+    if names is None:
+        names = (list(I.LINEAR_CASES) + list(I.GROUPED_CASES) + list(I.NHWC_CASES)
+                 + list(I.CONVT_CASES) + list(I.SDPA_CASES))
+    for name in names:
         cs = Case(name, torch, baim, I)
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < warmup_s:
@@ -363,6 +372,7 @@ def main():
     traffic, mfma_busy = load_counters(dom)
 
     widened = time_widened(torch, baim, I)
+    other_configs = time_widened(torch, baim, I, OTHER_CONFIG_CASES)
 
     cpu = cpu_baseline(cases, args.cpu_seconds)
 
@@ -410,6 +420,7 @@ def main():
                                  else round(traffic / (k_time[dom] / n_launch * 1e-3) / 1e9, 1)),
         },
         "cpu_baseline": cpu,
+        "other_configs": other_configs,
         "widened": widened,
     }
     print(json.dumps(line), flush=True)
