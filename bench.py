@@ -33,8 +33,11 @@ METRIC = "fp32 TFLOP/s (addmm, im2col conv2d) and % of MI355X fp32 MFMA peak"
 STEP_CASES = ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2",
               "up_proj_4096x1024x4096", "down_proj_4096x4096x1024",
               "ragged_577x1024x4096_full_self"]
+# Every source the step's kernels are built from (the .hip files and all the
+# headers they include) plus the compiler flags: the committed counter runs
+# are only valid for exactly these.
 KERNEL_SOURCES = ["gemm_core.hpp", "index_math.hpp", "tile_select.hpp", "tile_select.cpp",
-                  "addmm.hip", "conv2d_gemm.hip"]
+                  "launch.hpp", "im2col_nhwc.hpp", "addmm.hip", "conv2d_gemm.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -43,6 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps, so the timed steps "
+                         "run at the GPU's steady clock")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -68,10 +74,12 @@ def calibrate_copy():
 
 
 def kernel_source_hash() -> str:
+    from bias_addmm_im2col_amd import build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(build.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -334,6 +342,13 @@ def main():
             if events is not None:
                 events[i][1].record()
 
+    # The clock ramps for tens of milliseconds after the GPU turns busy: run
+    # untimed steps for --settle-s seconds, then the warmup steps.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -370,6 +385,13 @@ def main():
     achieved = k_flops[dom] / (k_time[dom] * 1e-3) / 1e12
     n_launch = k_launch[dom]
     traffic, mfma_busy = load_counters(dom)
+    counters_from = None
+    if traffic is not None or mfma_busy is not None:
+        counters_from = {"file": os.path.relpath(TRAFFIC_FILE, ROOT),
+                         "kernel_source_sha": kernel_source_hash(),
+                         "what": "traffic, mfma_busy and hbm_gbytes_per_s come from committed "
+                                 "rocprofv3 counter runs on these exact kernel sources, not "
+                                 "from this run"}
 
     widened = time_widened(torch, baim, I)
     other_configs = time_widened(torch, baim, I, OTHER_CONFIG_CASES)
@@ -383,6 +405,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_s,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -418,6 +441,7 @@ def main():
                                   else round(achieved * 1e12 / (256 * 256 * mfma_busy) / 1e9, 3)),
             "hbm_gbytes_per_s": (None if traffic is None
                                  else round(traffic / (k_time[dom] / n_launch * 1e-3) / 1e9, 1)),
+            "counters_from": counters_from,
         },
         "cpu_baseline": cpu,
         "other_configs": other_configs,

@@ -253,6 +253,8 @@ template <int AK>
 static hipError_t launch_gemm(const AddmmProblem& p, AddmmArgs& a, bool va, bool vb,
                               hipStream_t stream) {
   GemmPlan plan = plan_gemm(p.M, p.N, p.K, getenv("BAIM_TILE"));
+  // mat2 [K, N] is read BK rows at a time with 32-bit offsets
+  if (AK == A_ROWS && !p.weight_nk) plan = plan_fit_col_operand(plan, p.M, p.N, p.K);
   if (plan.mode == MODE_STREAM && !(va && vb)) plan = plan_tiles_only(plan, p.M, p.N, p.K);
   if (AK == A_NHWC && !(va && vb) && plan.cfg == TILE_128x128_K2)
     plan = plan_gemm(p.M, p.N, p.K, "0");  // same block tile, 8 waves

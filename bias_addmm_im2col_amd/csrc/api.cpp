@@ -23,8 +23,10 @@ thread_local std::string g_err;
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive
 // Byte offsets inside one tile of the operands are 32-bit: a block's A tile
-// spans at most 256 rows of K floats, a B tile 64 rows of N floats, and the
-// conv gather addresses the whole input.
+// spans at most 128 rows of K floats, and the conv gather addresses the
+// whole input.  A B tile of mat2 [K, N] spans BK rows of N floats: 64 rows
+// fit any N below 2^23, and the launcher moves a plan whose tile has 128
+// rows to a 64-row tile when (127 * N + BN) floats would pass 2^31 bytes.
 constexpr int64_t kMaxK = (int64_t)1 << 21;
 constexpr int64_t kMaxAddmmN = (int64_t)1 << 23;
 constexpr int64_t kMaxConvInput = (int64_t)1 << 29;

@@ -139,4 +139,14 @@ GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K) {
   return make(p.cfg, M, N, K, 1);
 }
 
+bool plan_col_tile_fits(int cfg, int N) {
+  return ((int64_t)(kTileBK[cfg] - 1) * N + kTileBN[cfg]) * 4 < ((int64_t)1 << 31);
+}
+
+GemmPlan plan_fit_col_operand(const GemmPlan& p, int M, int N, int K) {
+  if (plan_col_tile_fits(p.cfg, N)) return p;
+  if (p.mode == MODE_STREAM) return make_stream(TILE_64x64_K2, M, N, K, p.workers);
+  return make(TILE_64x64_K2, M, N, K, p.mode == MODE_SLICES ? p.splits : 1);
+}
+
 }  // namespace baim

@@ -59,6 +59,16 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec);
 // The same tile configuration with one tile per block.
 GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K);
 
+// Whether a B tile read from a row-major [K, N] matrix (mat2) keeps every
+// in-tile byte offset below 2^31: the tile spans BK rows of N floats, so
+// (BK - 1) * N + BN floats must stay addressable by a 32-bit offset.
+bool plan_col_tile_fits(int cfg, int N);
+
+// `p` with its configuration replaced, if its B tile over a row-major
+// [K, N] matrix would not fit 32-bit offsets, by the 64x64x64 tile (BK 64),
+// in the same mode (slices or stream) where that tile allows it.
+GemmPlan plan_fit_col_operand(const GemmPlan& p, int M, int N, int K);
+
 inline int64_t plan_tiles(const GemmPlan& p) { return (int64_t)p.tiles_m * p.tiles_n; }
 
 // The block count of a plan.

@@ -105,9 +105,9 @@ def _load():
     lib.oracle_conv2d_nhwc_at.restype = ctypes.c_int
     lib.oracle_convt_out_size.argtypes = [_i64] * 6
     lib.oracle_convt_out_size.restype = _i64
-    lib.oracle_conv_transpose2d.argtypes = [_i64] * 15 + [_fp, _fp, _fp, _dp, _dp]
+    lib.oracle_conv_transpose2d.argtypes = [_i64] * 16 + [_fp, _fp, _fp, _dp, _dp]
     lib.oracle_conv_transpose2d.restype = ctypes.c_int
-    lib.oracle_conv_transpose2d_at.argtypes = [_i64] * 15 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
+    lib.oracle_conv_transpose2d_at.argtypes = [_i64] * 16 + [_fp, _fp, _fp, _i64, _lp, _dp, _dp]
     lib.oracle_conv_transpose2d_at.restype = ctypes.c_int
     lib.oracle_sdpa.argtypes = [_i64] * 4 + [_fp] * 4 + [ctypes.c_float, _dp, _dp]
     lib.oracle_sdpa.restype = ctypes.c_int
@@ -360,20 +360,23 @@ def convt_out_size(size, k, stride, pad, dil, out_pad) -> int:
     return int(_load().oracle_convt_out_size(size, k, stride, pad, dil, out_pad))
 
 
-def _convt_args(x, w, stride, padding, dilation, output_padding):
+def _convt_args(x, w, stride, padding, dilation, output_padding, groups):
     B, IC, H, W = x.shape
-    IC2, OC, KH, KW = w.shape
-    assert IC == IC2, "weight must be [IC, OC, KH, KW]"
+    IC2, OCg, KH, KW = w.shape
+    assert IC == IC2, "weight must be [IC, OC/groups, KH, KW]"
+    assert groups >= 1 and IC % groups == 0
     (sH, sW), (pH, pW), (dH, dW) = _pair(stride), _pair(padding), _pair(dilation)
     opH, opW = _pair(output_padding)
-    return (B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW)
+    return (B, IC, H, W, OCg * groups, KH, KW, sH, sW, pH, pW, dH, dW, opH, opW, groups)
 
 
-def conv_transpose2d(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0) -> Result:
+def conv_transpose2d(x, w, bias=None, stride=1, padding=0, dilation=1, output_padding=0,
+                     groups=1) -> Result:
     """Full [B,OC,OH,OW] reference of the transposed conv (scatter form):
-    x [B,IC,H,W], w [IC,OC,KH,KW], bias [OC]."""
+    x [B,IC,H,W], w [IC,OC/groups,KH,KW], bias [OC].  Input channel ic only
+    feeds the output channels of its group ic // (IC/groups)."""
     x, w, bias = _f32(x), _f32(w), _f32(bias)
-    a = _convt_args(x, w, stride, padding, dilation, output_padding)
+    a = _convt_args(x, w, stride, padding, dilation, output_padding, groups)
     B, OC = a[0], a[4]
     OH = convt_out_size(a[2], a[5], a[7], a[9], a[11], a[13])
     OW = convt_out_size(a[3], a[6], a[8], a[10], a[12], a[14])
@@ -388,10 +391,11 @@ def conv_transpose2d(x, w, bias=None, stride=1, padding=0, dilation=1, output_pa
     return Result(ref, sabs, np.broadcast_to(bb[None, :, None, None], ref.shape))
 
 
-def conv_transpose2d_at(x, w, bias, stride, padding, dilation, output_padding, idx) -> Result:
+def conv_transpose2d_at(x, w, bias, stride, padding, dilation, output_padding, idx,
+                        groups=1) -> Result:
     """Transposed-conv reference (gather form) at sampled flat NCHW indices."""
     x, w, bias = _f32(x), _f32(w), _f32(bias)
-    a = _convt_args(x, w, stride, padding, dilation, output_padding)
+    a = _convt_args(x, w, stride, padding, dilation, output_padding, groups)
     B, OC = a[0], a[4]
     OH = convt_out_size(a[2], a[5], a[7], a[9], a[11], a[13])
     OW = convt_out_size(a[3], a[6], a[8], a[10], a[12], a[14])

@@ -494,10 +494,12 @@ int oracle_conv2d_nhwc_at(int64_t B, int64_t IC, int64_t H, int64_t W,
  * ("et_vk conv2d: route standard (groups==1) conv through an im2col tiled
  * GEMM", Solution paragraph) and defines no arithmetic for them, so the
  * oracle takes the standard definition (the adjoint of conv2d, as aten's
- * conv_transpose2d): input x [B,IC,H,W], weight w [IC,OC,KH,KW] (groups ==
- * 1), and every input element scatters into
- *   out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW] += x[b,ic,ih,iw] * w[ic,oc,kh,kw]
- * (positions outside the output are dropped), plus bias[oc].  Output size
+ * conv_transpose2d): input x [B,IC,H,W], weight w [IC,OC/G,KH,KW] for G
+ * groups, and every input element scatters into
+ *   out[b, oc, ih*sH - pH + kh*dH, iw*sW - pW + kw*dW] += x[b,ic,ih,iw] * w[ic,ocl,kh,kw]
+ * (positions outside the output are dropped), plus bias[oc].  With groups,
+ * input channel ic only reaches the output channels of its own group
+ * g = ic / (IC/G): oc = g*(OC/G) + ocl.  Output size
  * OH = (H-1)*sH - 2*pH + dH*(KH-1) + opH + 1 (opH, the output padding,
  * only adds rows at the far edge) and likewise OW. */
 int64_t oracle_convt_out_size(int64_t in, int64_t k, int64_t s, int64_t p,
@@ -509,12 +511,13 @@ int64_t oracle_convt_out_size(int64_t in, int64_t k, int64_t s, int64_t p,
 int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W,
                             int64_t OC, int64_t KH, int64_t KW, int64_t sH,
                             int64_t sW, int64_t pH, int64_t pW, int64_t dH,
-                            int64_t dW, int64_t opH, int64_t opW,
+                            int64_t dW, int64_t opH, int64_t opW, int64_t G,
                             const float* x, const float* w, const float* bias,
                             double* ref, double* sabs) {
   int64_t OH = oracle_convt_out_size(H, KH, sH, pH, dH, opH);
   int64_t OW = oracle_convt_out_size(W, KW, sW, pW, dW, opW);
-  if (OH <= 0 || OW <= 0) return -1;
+  if (OH <= 0 || OW <= 0 || G < 1 || IC % G || OC % G) return -1;
+  int64_t icg = IC / G, ocg = OC / G;
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t b = 0; b < B; ++b)
     for (int64_t oc = 0; oc < OC; ++oc) {
@@ -524,7 +527,8 @@ int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W,
         r[o] = 0.0;
         a[o] = 0.0;
       }
-      for (int64_t ic = 0; ic < IC; ++ic)
+      int64_t g = oc / ocg, ocl = oc % ocg;
+      for (int64_t ic = g * icg; ic < (g + 1) * icg; ++ic)
         for (int64_t ih = 0; ih < H; ++ih)
           for (int64_t iw = 0; iw < W; ++iw) {
             double xv = (double)x[((b * IC + ic) * H + ih) * W + iw];
@@ -534,7 +538,7 @@ int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W,
               for (int64_t kw = 0; kw < KW; ++kw) {
                 int64_t ow = iw * sW - pW + kw * dW;
                 if (ow < 0 || ow >= OW) continue;
-                double p = xv * (double)w[((ic * OC + oc) * KH + kh) * KW + kw];
+                double p = xv * (double)w[((ic * ocg + ocl) * KH + kh) * KW + kw];
                 r[oh * OW + ow] += p;
                 a[oh * OW + ow] += fabs(p);
               }
@@ -553,20 +557,22 @@ int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W,
 int oracle_conv_transpose2d_at(int64_t B, int64_t IC, int64_t H, int64_t W,
                                int64_t OC, int64_t KH, int64_t KW, int64_t sH,
                                int64_t sW, int64_t pH, int64_t pW, int64_t dH,
-                               int64_t dW, int64_t opH, int64_t opW,
+                               int64_t dW, int64_t opH, int64_t opW, int64_t G,
                                const float* x, const float* w,
                                const float* bias, int64_t n,
                                const int64_t* idx, double* ref, double* sabs) {
   int64_t OH = oracle_convt_out_size(H, KH, sH, pH, dH, opH);
   int64_t OW = oracle_convt_out_size(W, KW, sW, pW, dW, opW);
-  if (OH <= 0 || OW <= 0 || B <= 0) return -1;
+  if (OH <= 0 || OW <= 0 || B <= 0 || G < 1 || IC % G || OC % G) return -1;
+  int64_t icg = IC / G, ocg = OC / G;
 #pragma omp parallel for schedule(static)
   for (int64_t s = 0; s < n; ++s) {
     int64_t o = idx[s];
     int64_t ow = o % OW, oh = (o / OW) % OH, oc = (o / (OW * OH)) % OC;
     int64_t b = o / (OW * OH * OC);
+    int64_t g = oc / ocg, ocl = oc % ocg;
     double acc = 0.0, aabs = 0.0;
-    for (int64_t ic = 0; ic < IC; ++ic)
+    for (int64_t ic = g * icg; ic < (g + 1) * icg; ++ic)
       for (int64_t kh = 0; kh < KH; ++kh) {
         int64_t th = oh + pH - kh * dH;
         if (th < 0 || th % sH != 0 || th / sH >= H) continue;
@@ -574,7 +580,7 @@ int oracle_conv_transpose2d_at(int64_t B, int64_t IC, int64_t H, int64_t W,
           int64_t tw = ow + pW - kw * dW;
           if (tw < 0 || tw % sW != 0 || tw / sW >= W) continue;
           double p = (double)x[((b * IC + ic) * H + th / sH) * W + tw / sW] *
-                     (double)w[((ic * OC + oc) * KH + kh) * KW + kw];
+                     (double)w[((ic * ocg + ocl) * KH + kh) * KW + kw];
           acc += p;
           aabs += fabs(p);
         }

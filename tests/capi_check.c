@@ -36,8 +36,8 @@ int oracle_conv2d_nhwc(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC, 
 int oracle_conv_transpose2d(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
                             int64_t KH, int64_t KW, int64_t sH, int64_t sW, int64_t pH,
                             int64_t pW, int64_t dH, int64_t dW, int64_t opH, int64_t opW,
-                            const float* x, const float* w, const float* bias, double* ref,
-                            double* sabs);
+                            int64_t groups, const float* x, const float* w, const float* bias,
+                            double* ref, double* sabs);
 int oracle_sdpa(int64_t BH, int64_t Sq, int64_t Skv, int64_t D, const float* q, const float* k,
                 const float* v, const float* mask, float scale, double* out, double* err);
 
@@ -189,7 +189,8 @@ static void test_convs(void) {
                conv_transpose2d_f32(dtout, dx, dw, dbias, B, IC, H, W, OC, KH, KW, 2, 2, 1, 1, 1,
                                     1, 1, 1, 1, NULL), BAIM_OK);
   out = from_device(dtout, nt);
-  oracle_conv_transpose2d(B, IC, H, W, OC, KH, KW, 2, 2, 1, 1, 1, 1, 1, 1, x, w, bias, tref, tsabs);
+  oracle_conv_transpose2d(B, IC, H, W, OC, KH, KW, 2, 2, 1, 1, 1, 1, 1, 1, 1, x, w, bias, tref,
+                          tsabs);
   for (int64_t i = 0; i < nt; ++i) tbabs[i] = fabs((double)bias[(i / (TH * TW)) % OC]);
   compare("conv_transpose2d_f32", out, tref, tsabs, tbabs, 4e-6 * sqrt((double)(IC * KH * KW)), nt);
   free(out);

@@ -36,6 +36,23 @@ def test_counter_figures_only_for_the_hashed_kernel_sources(tmp_path, monkeypatc
 
 
 def test_source_hash_covers_the_gemm_and_conv_sources():
-    for f in ("gemm_core.hpp", "addmm.hip", "conv2d_gemm.hip", "tile_select.cpp"):
-        assert f in bench.KERNEL_SOURCES
+    # the step's kernel sources and, transitively, every local header they
+    # include
+    import re
+    csrc = os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc")
+    todo, seen = ["addmm.hip", "conv2d_gemm.hip", "tile_select.cpp"], set()
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        todo += re.findall(r'^#include "([^"]+)"', open(os.path.join(csrc, f)).read(), flags=re.M)
+    assert seen <= set(bench.KERNEL_SOURCES), seen - set(bench.KERNEL_SOURCES)
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_source_hash_covers_the_compiler_flags(monkeypatch):
+    from bias_addmm_im2col_amd import build
+    h0 = bench.kernel_source_hash()
+    monkeypatch.setattr(build, "HIPCC_FLAGS", build.HIPCC_FLAGS + ["-DX"])
+    assert bench.kernel_source_hash() != h0

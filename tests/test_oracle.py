@@ -794,3 +794,61 @@ def test_sampled_conv_transpose_equals_full():
         s = oracle.conv_transpose2d_at(x, w, b, stride, pad, dil, opad, idx)
         np.testing.assert_allclose(s.ref, full.ref.reshape(-1), rtol=1e-13, atol=1e-13)
         np.testing.assert_allclose(s.sabs, full.sabs.reshape(-1), rtol=1e-13, atol=0)
+
+
+# Grouped transposed conv: weight [IC, OC/G, KH, KW]; input channel ic feeds
+# only the output channels of its group ic // (IC/G) (aten's groups).
+CONVT_GROUPED_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, stride, pad, dil, out_pad, groups
+    (2, 4, 5, 4, 6, 3, 3, 2, 1, 1, 1, 2), (1, 6, 4, 5, 3, 2, 3, (2, 1), (0, 1), 1, (1, 0), 3),
+    (1, 8, 3, 3, 8, 3, 3, 1, 1, 2, 0, 8), (2, 4, 3, 4, 8, 4, 4, 2, 1, 1, 0, 4)]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,opad,groups", CONVT_GROUPED_SHAPES)
+def test_grouped_conv_transpose_vs_torch_float64(B, IC, H, W, OC, KH, KW, stride, pad, dil, opad,
+                                                 groups):
+    x = rand32((B, IC, H, W), 163)
+    w, b = rand32((IC, OC // groups, KH, KW), 164), rand32((OC,), 165)
+    r = oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad, groups)
+    t = F.conv_transpose2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                           torch.from_numpy(b).double(), stride, pad, opad, groups, dil).numpy()
+    assert r.ref.shape == t.shape
+    np.testing.assert_allclose(r.ref, t, rtol=1e-12, atol=1e-12)
+    idx = np.arange(r.ref.size)
+    s = oracle.conv_transpose2d_at(x, w, b, stride, pad, dil, opad, idx, groups)
+    np.testing.assert_allclose(s.ref, r.ref.reshape(-1), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(s.sabs, r.sabs.reshape(-1), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,KH,KW,stride,pad,dil,opad,groups", CONVT_GROUPED_SHAPES)
+def test_grouped_conv_transpose_is_the_adjoint_of_grouped_conv(B, IC, H, W, OC, KH, KW, stride,
+                                                               pad, dil, opad, groups):
+    # <convT_G(x), y> = <x, conv_G(y)>: the weight [IC, OC/G, KH, KW] read as
+    # a grouped conv weight [OC' = IC, IC'/G = OC/G, KH, KW].
+    x, w = rand32((B, IC, H, W), 166), rand32((IC, OC // groups, KH, KW), 167)
+    r = oracle.conv_transpose2d(x, w, None, stride, pad, dil, opad, groups)
+    y = rand32(r.ref.shape, 168)
+    c = oracle.conv2d_grouped(y, w, None, stride, pad, dil, groups)
+    h, wd = min(H, c.ref.shape[2]), min(W, c.ref.shape[3])
+    lhs = float((r.ref * y.astype(np.float64)).sum())
+    rhs = float((x[:, :, :h, :wd].astype(np.float64) * c.ref[:, :, :h, :wd]).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_grouped_conv_transpose_block_structure():
+    # a group's output channels are untouched by the other groups' inputs:
+    # zeroing every input channel outside group 1 leaves groups 0 and 2 at
+    # their bias, and group 1 equals the ungrouped transposed conv of its
+    # own channels and weight slice
+    G, icg, ocg = 3, 2, 4
+    x, w, b = rand32((1, G * icg, 4, 5), 169), rand32((G * icg, ocg, 3, 3), 170), rand32((G * ocg,), 171)
+    x[:, :icg] = 0.0
+    x[:, 2 * icg:] = 0.0
+    r = oracle.conv_transpose2d(x, w, b, 2, 1, 1, 1, G)
+    for g in (0, 2):
+        assert (r.ref[:, g * ocg:(g + 1) * ocg] ==
+                b[g * ocg:(g + 1) * ocg].astype(np.float64)[None, :, None, None]).all()
+    one = oracle.conv_transpose2d(np.ascontiguousarray(x[:, icg:2 * icg]),
+                                  np.ascontiguousarray(w[icg:2 * icg]),
+                                  np.ascontiguousarray(b[ocg:2 * ocg]), 2, 1, 1, 1)
+    assert (r.ref[:, ocg:2 * ocg] == one.ref).all()

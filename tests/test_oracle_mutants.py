@@ -1,12 +1,16 @@
 """Planted mistakes in the oracle must fail its pins.
 
-Each case copies oracle.c to a temporary directory, plants one plausible
+Each case copies the oracle to a temporary directory, plants one plausible
 mistake (a dropped term, a wrong sign or index, a transposed operand, a
-missing bias, ...), builds it with gcc, and runs the pin suite
-(tests/test_oracle.py) against that build in a child process.  The child must
-fail; if it passes, the pins have a blind spot.  All of this runs on the CPU.
+missing bias, a loosened acceptance bound, ...), and runs the pin suites
+(tests/test_oracle.py and tests/test_oracle_tolerance.py) against it in a
+child process.  The child must fail; if it passes, the pins have a blind
+spot.  Mistakes in oracle.c are built with gcc and loaded in place of the
+real library; mistakes in the Python wrapper (the acceptance-bound helpers)
+run from a copy of the package and its tests.  All of this runs on the CPU.
 """
 import os
+import shutil
 import subprocess
 import sys
 
@@ -14,6 +18,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PIN_FILES = ["test_oracle.py", "test_oracle_tolerance.py"]
 
 MUTANTS = {
     "drop_first_term": ("    acc += p;\n", "    if (k) acc += p;\n"),
@@ -51,13 +57,51 @@ MUTANTS = {
     "nhwc_output_written_as_nchw": ("int64_t o = ((b * c.OH + oh) * c.OW + ow) * OC + oc;",
                                     "int64_t o = ((b * OC + oc) * c.OH + oh) * c.OW + ow;"),
     "convt_pad_sign": ("int64_t oh = ih * sH - pH + kh * dH;", "int64_t oh = ih * sH + pH + kh * dH;"),
-    "convt_weight_ic_oc_swapped": ("w[((ic * OC + oc) * KH + kh) * KW + kw]",
-                                   "w[((oc * IC + ic) * KH + kh) * KW + kw]"),
+    "convt_weight_ic_oc_swapped": ("w[((ic * ocg + ocl) * KH + kh) * KW + kw]",
+                                   "w[((ocl * IC + ic) * KH + kh) * KW + kw]"),
+    "convt_group_input_channels_from_group_0": ("for (int64_t ic = g * icg; ic < (g + 1) * icg; ++ic)\n        for (int64_t ih",
+                                                "for (int64_t ic = 0; ic < icg; ++ic)\n        for (int64_t ih"),
+    "convt_grouped_weight_row": ("double p = xv * (double)w[((ic * ocg + ocl)",
+                                 "double p = xv * (double)w[(((ic % icg) * ocg + ocl)"),
     "convt_output_padding_ignored": ("d * (k - 1) + op + 1;", "d * (k - 1) + 1;"),
     "convt_gather_dilation_dropped": ("int64_t th = oh + pH - kh * dH;", "int64_t th = oh + pH - kh;"),
     "im2col_row_order": ("int64_t kk = (ic * KH + kh) * KW + kw;",
                          "int64_t kk = (ic * KW + kw) * KH + kh;"),
+    "conv_sabs_signed": ("aabs += fabs(wv * xv);", "aabs += wv * xv;"),
+    "linear_sabs_drops_first_tap": ("    acc += p;\n    aabs += fabs(p);\n  }\n  *ref = (bias",
+                                    "    acc += p;\n    if (k) aabs += fabs(p);\n  }\n  *ref = (bias"),
+    "convt_sabs_signed": ("a[oh * OW + ow] += fabs(p);", "a[oh * OW + ow] += p;"),
+    "sdpa_err_drops_sqrt_skv": ("(sd * a[j] + fabs(s[j] - m) + ss + 1.0)", "(sd * a[j] + fabs(s[j] - m) + 1.0)"),
+    "sdpa_err_drops_out_term": ("+ fabs(out[d])) *", ") *"),
+    "sdpa_err_drops_mask_term": ("a[j] = fabs((double)scale) * dabs + fabs(mk);",
+                                 "a[j] = fabs((double)scale) * dabs;"),
 }
+
+# Mistakes in the acceptance-bound helpers of oracle/__init__.py.
+PY_MUTANTS = {
+    "bound_drops_beta": ("return np.abs(np.float64(np.float32(beta)) * full)", "return np.abs(full)"),
+    "bound_k_for_sqrt_k": ("return 4e-6 * np.sqrt(K) * (", "return 4e-6 * K * ("),
+    "bound_10x_constant": ("return 4e-6 * np.sqrt(K) * (", "return 4e-5 * np.sqrt(K) * ("),
+    "bound_drops_alpha": ("(abs(float(np.float32(alpha))) * res.sabs + res.selfabs)",
+                          "(res.sabs + res.selfabs)"),
+    "bound_drops_self_term": ("(abs(float(np.float32(alpha))) * res.sabs + res.selfabs)",
+                              "(abs(float(np.float32(alpha))) * res.sabs)"),
+    "bound_self_2d_read_as_row": ("full = s.reshape(M, N) if self_2d else np.broadcast_to(s, (M, N))",
+                                  "full = np.broadcast_to(s.reshape(-1)[:N], (M, N))"),
+    "bound_sampled_self_column": ("full = s.reshape(M, N)[rows, cols] if self_2d else s[cols]",
+                                  "full = s.reshape(M, N)[rows, cols] if self_2d else s[rows % N]"),
+    "bound_bias_by_row": ("return np.broadcast_to(b, (M, N)) if rows is None else b[cols]",
+                          "return np.broadcast_to(b, (M, N)) if rows is None else b[rows % len(b)]"),
+    "bound_conv_sampled_bias_channel": ("    oc = (idx // (OH * OW)) % OC\n    bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])\n    return Result(ref, sabs, bb)\n\n\ndef conv2d_grouped(",
+                                        "    oc = idx % OC\n    bb = np.zeros(n) if bias is None else np.abs(bias.astype(np.float64)[oc])\n    return Result(ref, sabs, bb)\n\n\ndef conv2d_grouped("),
+    "bound_sdpa_10x_constant": ("return 4e-6 * res.err", "return 4e-5 * res.err"),
+}
+
+
+def _run_pins(cwd, env):
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                          [os.path.join(cwd, "tests", f) for f in PIN_FILES],
+                          cwd=cwd, env=env, capture_output=True, text=True, timeout=600)
 
 
 @pytest.mark.slow
@@ -73,7 +117,40 @@ def test_planted_mistake_is_caught(name, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
                            str(c_file), "-lm"])
     env = dict(os.environ, BAIM_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
-    proc = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle.py")],
-                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    proc = _run_pins(ROOT, env)
     assert proc.returncode != 0, f"pins missed planted mistake {name}:\n{proc.stdout[-2000:]}"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_planted_bound_mistake_is_caught(name, tmp_path):
+    """A copy of the oracle package (with the real liboracle.so) and of the
+    tests, with one mistake in the Python bound helpers."""
+    old, new = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    os.makedirs(tmp_path / "oracle")
+    (tmp_path / "oracle" / "__init__.py").write_text(src.replace(old, new, 1))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "_build"))
+    shutil.copytree(os.path.join(ROOT, "bias_addmm_im2col_amd"), tmp_path / "bias_addmm_im2col_amd",
+                    ignore=shutil.ignore_patterns("__pycache__", "_build", "*.so", "csrc"))
+    import oracle
+    env = dict(os.environ, BAIM_ORACLE_LIB=oracle.build(force=False), OMP_NUM_THREADS="2")
+    proc = _run_pins(str(tmp_path), env)
+    assert "oracle_mutant_marker" not in proc.stdout
+    assert proc.returncode != 0, f"pins missed planted mistake {name}:\n{proc.stdout[-2000:]}"
+
+
+def test_python_mutant_copy_is_the_one_imported(tmp_path):
+    """The copy-and-run scheme above really tests the copied package: a
+    wrapper that fails on import makes the copied pins fail."""
+    os.makedirs(tmp_path / "oracle")
+    (tmp_path / "oracle" / "__init__.py").write_text(open(PY_SRC).read() +
+                                                    "\nraise ImportError('copied oracle loaded')\n")
+    os.makedirs(tmp_path / "tests")
+    shutil.copy(os.path.join(ROOT, "tests", "conftest.py"), tmp_path / "tests" / "conftest.py")
+    (tmp_path / "tests" / "test_oracle.py").write_text("import oracle\n\ndef test_x():\n    pass\n")
+    (tmp_path / "tests" / "test_oracle_tolerance.py").write_text("def test_y():\n    pass\n")
+    proc = _run_pins(str(tmp_path), dict(os.environ))
+    assert proc.returncode != 0 and "copied oracle loaded" in proc.stdout + proc.stderr

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from bias_addmm_im2col_amd import inputs as I
+from tests import _specs
 from tests._parity import check_bitwise, check_close, dev
 
 pytestmark = pytest.mark.gpu
@@ -77,19 +78,20 @@ def test_nhwc_conv_integer_bitwise(IC, OC, k, stride):
                   "nhwc integer")
 
 
-TILE_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "8", "0,3", "2,4", "4,2", "7,2", "3,s7",
-              "1,s4", "6,s5", "8,s3"]
+TILE_SPECS = _specs.NHWC_SPECS
 
 
 @pytest.mark.parametrize("spec", TILE_SPECS)
 def test_nhwc_conv_forced_tile_configs(spec, monkeypatch):
     monkeypatch.setenv("BAIM_TILE", spec)
-    for (IC, k, stride) in [(16, 3, 1), (3, 5, 2)]:
+    for (IC, k, stride) in _specs.NHWC_SHAPES:
         say(f"BAIM_TILE={spec} conv2d_nhwc_f32 IC={IC} k={k}")
         x, w, b = gen((2, 21, 18, IC), 7), gen((70, k, k, IC), 8), gen((70,), 9)
         check_close(run(x, w, b, stride, 1, 1), oracle.conv2d_nhwc(x, w, b, stride, 1, 1),
                     k * k * IC, 1.0, f"nhwc {spec}")
-    x, w, b = gen((1, 15, 16, 32), 10, "I"), gen((66, 3, 3, 32), 11, "I"), gen((66,), 12, "I")
+    B, H, W, IC, OC = _specs.NHWC_INT_SHAPE
+    say(f"BAIM_TILE={spec} conv2d_nhwc_f32 integer x=[{B},{H},{W},{IC}] OC={OC}")
+    x, w, b = gen((B, H, W, IC), 10, "I"), gen((OC, 3, 3, IC), 11, "I"), gen((OC,), 12, "I")
     check_bitwise(run(x, w, b, 1, 1, 1), oracle.conv2d_nhwc(x, w, b, 1, 1, 1), f"nhwc int {spec}")
 
 

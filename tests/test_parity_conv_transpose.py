@@ -45,21 +45,6 @@ def run(x, w, b, stride=1, pad=0, opad=0, groups=1, dil=1):
     return out.cpu().numpy()
 
 
-def oracle_grouped(x, w, b, stride, pad, opad, groups, dil):
-    """Grouped transposed conv from the ungrouped oracle, one group at a time."""
-    IC = x.shape[1]
-    icg, ocg = IC // groups, w.shape[1]
-    parts = []
-    for g in range(groups):
-        xs = x[:, g * icg:(g + 1) * icg].contiguous()
-        ws = w[g * icg:(g + 1) * icg].contiguous()
-        bs = None if b is None else b[g * ocg:(g + 1) * ocg].contiguous()
-        parts.append(oracle.conv_transpose2d(xs, ws, bs, stride, pad, dil, opad))
-    return oracle.Result(np.concatenate([p.ref for p in parts], 1),
-                         np.concatenate([p.sabs for p in parts], 1),
-                         np.concatenate([p.selfabs for p in parts], 1))
-
-
 SHAPES = [
     # B, IC, H, W, OC, KH, KW, stride, pad, out_pad, dil, bias
     (1, 4, 5, 5, 8, 3, 3, 1, 0, 0, 1, True),
@@ -90,7 +75,7 @@ def test_convt_small_full(B, IC, H, W, OC, KH, KW, stride, pad, opad, dil, has_b
 def test_convt_grouped(groups, IC, OC):
     say(f"conv_transpose2d_f32 groups={groups} IC={IC} OC={OC}")
     x, w, b = gen((2, IC, 7, 6), 4), gen((IC, OC // groups, 3, 3), 5), gen((OC,), 6)
-    check_close(run(x, w, b, 2, 1, 1, groups), oracle_grouped(x, w, b, 2, 1, 1, groups, 1),
+    check_close(run(x, w, b, 2, 1, 1, groups), oracle.conv_transpose2d(x, w, b, 2, 1, 1, 1, groups),
                 IC // groups * 9, 1.0, f"convT groups {groups}")
 
 
@@ -131,13 +116,11 @@ def test_convt_k_slices(spec, monkeypatch):
             f"s={stride} p={pad} op={opad} g={groups} d={dil}")
         x, w = gen((B, IC, H, W), 16), gen((IC, OC // groups, KH, KW), 17)
         b = gen((OC,), 18)
-        ref = (oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad) if groups == 1
-               else oracle_grouped(x, w, b, stride, pad, opad, groups, dil))
+        ref = oracle.conv_transpose2d(x, w, b, stride, pad, dil, opad, groups)
         check_close(run(x, w, b, stride, pad, opad, groups, dil), ref, IC // groups * KH * KW, 1.0,
                     f"convT slices {spec}")
         xi, wi = gen((B, IC, H, W), 19, "I"), gen((IC, OC // groups, KH, KW), 20, "I")
-        refi = (oracle.conv_transpose2d(xi, wi, None, stride, pad, dil, opad) if groups == 1
-                else oracle_grouped(xi, wi, None, stride, pad, opad, groups, dil))
+        refi = oracle.conv_transpose2d(xi, wi, None, stride, pad, dil, opad, groups)
         check_bitwise(run(xi, wi, None, stride, pad, opad, groups, dil), refi,
                       f"convT slices integer {spec}")
 

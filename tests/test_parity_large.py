@@ -41,6 +41,26 @@ def test_addmm_deep_k_near_the_limit():
     check_close(out.cpu().numpy(), oracle.addmm(a, b, s, False, 1.0, 1.0), K, 1.0, "deep K")
 
 
+@pytest.mark.parametrize("spec", ["7", "7,s5", "7,3"])
+def test_addmm_wide_mat2_with_a_128_row_tile(spec, monkeypatch):
+    """N past 2^22: the 128-row B tile of mat2 [K, N] would need offsets of
+    127*N floats, beyond 32 bits; forced, the launcher moves the plan to a
+    64-row tile, and every sampled output (the last rows of each k-tile
+    included) matches the oracle."""
+    import bias_addmm_im2col_amd as baim
+    monkeypatch.setenv("BAIM_TILE", spec)
+    M, K, N = 3, 200, (1 << 22) + 200000
+    say(f"addmm M={M} N={N} K={K} BAIM_TILE={spec}")
+    a, b, s = gen((M, K), 7), gen((K, N), 8), gen((N,), 9)
+    out = baim.addmm(s.cuda(), a.cuda(), b.cuda(), beta=1.0, alpha=1.0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    cols = np.concatenate([[0, N - 1, N // 2, (1 << 22) + 7], rng.integers(0, N, 3000)])
+    rows = rng.integers(0, M, cols.size)
+    got = out.cpu().numpy()[rows, cols]
+    check_close(got, oracle.addmm_at(a, b, s, False, 1.0, 1.0, rows, cols), K, 1.0, "wide mat2")
+
+
 def test_linear_long_m():
     """M = 2^20 + 3 rows: a long grid of row tiles."""
     import bias_addmm_im2col_amd as baim

@@ -54,6 +54,21 @@ int main() {
   if (plan_gemm(32, 12544, 288, nullptr).cfg != TILE_32x128) bad += printf("32-row tile\n") > 0;
   if (plan_gemm(7, 4096, 4096, nullptr).cfg != TILE_32x128) bad += printf("32-row tile 2\n") > 0;
   if (plan_gemm(33, 4096, 4096, nullptr).cfg == TILE_32x128) bad += printf("33 rows\n") > 0;
+  // a B tile of mat2 [K, N] keeps 32-bit offsets: the 128-row tile moves to
+  // a 64-row tile at large N, in the same mode; plans that fit stay
+  for (int N : {1, 4096, 4227300, 4227400, 8388607})
+    for (const char* s : {"7", "7,3", "7,s9", "0", "6,s5", "4,2"}) {
+      const GemmPlan p0 = plan_gemm(64, N, 4096, s);
+      const GemmPlan p1 = plan_fit_col_operand(p0, 64, N, 4096);
+      if (!plan_col_tile_fits(p1.cfg, N)) bad += printf("col tile N=%d %s\n", N, s) > 0;
+      if (plan_col_tile_fits(p0.cfg, N) && (p1.cfg != p0.cfg || p1.mode != p0.mode))
+        bad += printf("fitting plan changed N=%d %s\n", N, s) > 0;
+      if (p1.mode != p0.mode && !(p0.mode == MODE_STREAM && p1.mode == MODE_TILE))
+        bad += printf("mode changed N=%d %s\n", N, s) > 0;
+      bad += check(64, N, 4096, s);
+    }
+  if (plan_col_tile_fits(TILE_64x64_K4, 4227400) || !plan_col_tile_fits(TILE_64x64_K4, 4227300))
+    bad += printf("128-row tile limit\n") > 0;
   // K == 0 never splits
   if (plan_gemm(8, 8, 0, "0,4").splits != 1) bad += printf("K=0 split\n") > 0;
   if (bad) return 1;
