@@ -37,7 +37,8 @@ STEP_CASES = ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2",
 # headers they include) plus the compiler flags: the committed counter runs
 # are only valid for exactly these.
 KERNEL_SOURCES = ["gemm_core.hpp", "index_math.hpp", "tile_select.hpp", "tile_select.cpp",
-                  "launch.hpp", "im2col_nhwc.hpp", "addmm.hip", "conv2d_gemm.hip"]
+                  "launch.hpp", "im2col_nhwc.hpp", "conv_window_plan.hpp", "conv_window_plan.cpp",
+                  "addmm.hip", "conv2d_gemm.hip", "conv_window.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -162,11 +163,18 @@ class Case:
         if c.kind == "conv" and c.channels_last:  # out[B*OH*OW, OC]: the linear-shaped GEMM
             M, N = N, M
         p = baim.gemm_plan(M, N, K)
-        self.plan = p
-        # one kernel instance per (op, block tile, waves, wave groups, K split)
         kname = "conv2d_gemm_kernel" if c.kind == "conv" and not c.channels_last else "addmm_kernel"
+        geom = ""
+        if c.kind == "conv" and not c.channels_last:
+            p = baim.conv2d_plan((c.B, c.IC, c.H, c.W), (c.OC, c.IC // c.groups, c.KH, c.KW),
+                                 c.stride, c.padding, c.dilation, c.groups)
+            if p["kernel"] == 1:
+                kname = "conv_window_kernel"
+                geom = (f"{c.KH}x{c.KW} s{c.stride[0]} d{c.dilation[0]}, ")
+        self.plan = p
+        # one kernel instance per (op, geometry, block tile, waves, wave groups, K split)
         self.kernel = (f"baim::{kname}"
-                       f"<Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
+                       f"<{geom}Tile {p['bm']}x{p['bn']}x{p['bk']}, {p['waves']} waves, "
                        f"{p['kgroups']} k-groups>" + (f" split {p['splits']}" if p['splits'] > 1 else "")
                        + (f" stream {p['stream_blocks']}" if p['stream_blocks'] > 0 else ""))
         if c.kind == "addmm":

@@ -196,12 +196,16 @@ baim_status linear_f32(float* out, const float* x, const float* weight, const fl
   return launched(baim::launch_addmm(p, (hipStream_t)stream), "linear_f32");
 }
 
-baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
-                            const float* bias, int64_t B, int64_t IC, int64_t H, int64_t W,
-                            int64_t OC, int64_t KH, int64_t KW, int64_t sH, int64_t sW,
-                            int64_t pH, int64_t pW, int64_t dH, int64_t dW, int64_t groups,
-                            void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// The size checks of conv2d_gemm_f32 (everything but pointers); fills the
+// sizes of `q` and the element counts of input, weight and output.
+baim_status conv_sizes(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC, int64_t KH,
+                       int64_t KW, int64_t sH, int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                       int64_t dW, int64_t groups, baim::ConvProblem* q, int64_t* n_x,
+                       int64_t* n_w, int64_t* n_out) {
   if (B < 1 || IC < 1 || OC < 1)
     return fail(BAIM_ERR_SHAPE, "conv2d: B, IC and OC must be >= 1");
   if (groups < 1) return fail(BAIM_ERR_SHAPE, "conv2d: groups must be >= 1");
@@ -212,12 +216,14 @@ baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
     return fail(BAIM_ERR_SHAPE, "conv2d: groups=%lld must divide IC=%lld and OC=%lld",
                 (long long)groups, (long long)IC, (long long)OC);
   const int64_t icg = IC / groups;
-  const int64_t n_x = elems({B, IC, H, W}), n_w = elems({OC, icg, KH, KW});
-  const int64_t n_out = elems({B, OC, OH, OW}), K = elems({icg, KH, KW});
-  if (n_x < 0 || n_w < 0 || n_out < 0 || n_x >= kMaxElems || n_w >= kMaxElems ||
-      n_out >= kMaxElems)
+  *n_x = elems({B, IC, H, W});
+  *n_w = elems({OC, icg, KH, KW});
+  *n_out = elems({B, OC, OH, OW});
+  const int64_t K = elems({icg, KH, KW});
+  if (*n_x < 0 || *n_w < 0 || *n_out < 0 || *n_x >= kMaxElems || *n_w >= kMaxElems ||
+      *n_out >= kMaxElems)
     return fail(BAIM_ERR_TOO_LARGE, "conv2d: every tensor must have fewer than 2^31 elements");
-  if (n_x >= kMaxConvInput) return fail(BAIM_ERR_TOO_LARGE, "conv2d: input must have fewer than 2^29 elements");
+  if (*n_x >= kMaxConvInput) return fail(BAIM_ERR_TOO_LARGE, "conv2d: input must have fewer than 2^29 elements");
   if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d: (IC/groups)*KH*KW must be below 2^21");
   if (groups > 65535 || OC > 65535 || B > 65535)
     return fail(BAIM_ERR_TOO_LARGE, "conv2d: groups, OC and B must be at most 65535");
@@ -225,35 +231,96 @@ baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
   const int64_t n_pad = elems({H + 2 * pH, W + 2 * pW});
   if (n_pad < 0 || n_pad >= kMaxElems)
     return fail(BAIM_ERR_TOO_LARGE, "conv2d: padded input plane must have fewer than 2^31 elements");
+  q->B = (int)B;
+  q->IC = (int)IC;
+  q->H = (int)H;
+  q->W = (int)W;
+  q->OC = (int)OC;
+  q->KH = (int)KH;
+  q->KW = (int)KW;
+  q->sH = (int)sH;
+  q->sW = (int)sW;
+  q->pH = (int)pH;
+  q->pW = (int)pW;
+  q->dH = (int)dH;
+  q->dW = (int)dW;
+  q->OH = (int)OH;
+  q->OW = (int)OW;
+  q->groups = (int)groups;
+  return BAIM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+baim_status conv2d_gemm_f32(float* out, const float* input, const float* weight,
+                            const float* bias, int64_t B, int64_t IC, int64_t H, int64_t W,
+                            int64_t OC, int64_t KH, int64_t KW, int64_t sH, int64_t sW,
+                            int64_t pH, int64_t pW, int64_t dH, int64_t dW, int64_t groups,
+                            void* stream) {
+  g_err.clear();
+  baim::ConvProblem q;
+  int64_t n_x = 0, n_w = 0, n_out = 0;
+  const baim_status st =
+      conv_sizes(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, groups, &q, &n_x, &n_w, &n_out);
+  if (st != BAIM_OK) return st;
   if (!out || !input || !weight) return fail(BAIM_ERR_NULL, "conv2d: out/input/weight is NULL");
   if (overlap(out, n_out, input, n_x) || overlap(out, n_out, weight, n_w) ||
       overlap(out, n_out, bias, OC))
     return fail(BAIM_ERR_ALIAS, "conv2d: out overlaps an input");
-
-  baim::ConvProblem q;
   q.out = out;
   q.x = input;
   q.w = weight;
   q.bias = bias;
-  q.B = (int)B;
-  q.IC = (int)IC;
-  q.H = (int)H;
-  q.W = (int)W;
-  q.OC = (int)OC;
-  q.KH = (int)KH;
-  q.KW = (int)KW;
-  q.sH = (int)sH;
-  q.sW = (int)sW;
-  q.pH = (int)pH;
-  q.pW = (int)pW;
-  q.dH = (int)dH;
-  q.dW = (int)dW;
-  q.OH = (int)OH;
-  q.OW = (int)OW;
-  q.groups = (int)groups;
   if (!baim::conv_uses_gemm(q))
     return launched(baim::launch_conv2d_direct(q, (hipStream_t)stream), "conv2d_gemm_f32");
   return launched(baim::launch_conv2d(q, (hipStream_t)stream), "conv2d_gemm_f32");
+}
+
+baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC,
+                             int64_t KH, int64_t KW, int64_t sH, int64_t sW, int64_t pH,
+                             int64_t pW, int64_t dH, int64_t dW, int64_t groups, int* kernel,
+                             int* bm, int* bn, int* bk, int* waves, int* kgroups, int* splits,
+                             int* stream_blocks) {
+  g_err.clear();
+  if (!kernel || !bm || !bn || !bk || !waves || !kgroups || !splits || !stream_blocks)
+    return fail(BAIM_ERR_NULL, "baim_conv2d_plan: output pointers must not be NULL");
+  baim::ConvProblem q;
+  int64_t n_x = 0, n_w = 0, n_out = 0;
+  const baim_status st =
+      conv_sizes(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, groups, &q, &n_x, &n_w, &n_out);
+  if (st != BAIM_OK) return st;
+  *bm = *bn = *bk = *waves = *kgroups = *stream_blocks = 0;
+  *splits = 1;
+  if (!baim::conv_uses_gemm(q)) {
+    *kernel = 2;
+    return BAIM_OK;
+  }
+  const baim::WinPlan wp = baim::plan_conv_window(baim::win_shape(q), true, getenv("BAIM_CONV_WIN"));
+  if (wp.geom >= 0) {
+    *kernel = 1;
+    *bm = baim::kWinBM;
+    *bn = baim::kWinBN;
+    *bk = baim::kWinCI * q.KH * q.KW;
+    *waves = baim::kWinWaves;
+    *kgroups = baim::kWinKGroups;
+    *splits = wp.mode == baim::MODE_SLICES ? wp.splits : 1;
+    *stream_blocks = wp.mode == baim::MODE_STREAM ? wp.workers : 0;
+    return BAIM_OK;
+  }
+  *kernel = 0;
+  const int M = q.OC / q.groups, N = q.B * q.OH * q.OW, K = q.IC / q.groups * q.KH * q.KW;
+  baim::GemmPlan p = baim::plan_gemm(M, N, K, getenv("BAIM_TILE"));
+  if (p.mode == baim::MODE_STREAM && K % 4 != 0) p = baim::plan_tiles_only(p, M, N, K);
+  *bm = baim::kTileBM[p.cfg];
+  *bn = baim::kTileBN[p.cfg];
+  *bk = baim::kTileBK[p.cfg];
+  *waves = baim::kTileWaves[p.cfg];
+  *kgroups = baim::kTileKGroups[p.cfg];
+  *splits = p.mode == baim::MODE_SLICES ? p.splits : 1;
+  *stream_blocks = p.mode == baim::MODE_STREAM ? p.workers : 0;
+  return BAIM_OK;
 }
 
 }  // extern "C"

@@ -310,7 +310,18 @@ static hipError_t launch_cfg(int cfg, const ConvArgs& a, int nblocks, bool va, h
   }
 }
 
+hipError_t launch_conv_out_init(float* out, const float* bias, bool sentinel, uint32_t total,
+                                uint32_t P, uint32_t OC, hipStream_t stream) {
+  const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
+  hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, out, bias, sentinel ? 1 : 0,
+                     total, make_fastdiv(P), OC);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
+  const bool aligned = ((uintptr_t)q.x & 15) == 0 && ((uintptr_t)q.w & 15) == 0;
+  const WinPlan wp = plan_conv_window(win_shape(q), aligned, getenv("BAIM_CONV_WIN"));
+  if (wp.geom >= 0) return launch_conv2d_window(q, wp, stream);
   ConvArgs a;
   a.out = q.out;
   a.x = q.x;
@@ -347,11 +358,9 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.sched = Sched{plan.tiles_m, plan.tiles_n, 8, plan.nkt, plan.splits, plan.kt_per_split};
   const int nblocks = (int)plan_blocks(plan);
   if (plan_needs_init(plan)) {
-    const uint32_t total = (uint32_t)q.OC * (uint32_t)a.N;
-    const int gb = (int)((total + 255u) / 256u < 4096u ? (total + 255u) / 256u : 4096u);
-    hipLaunchKernelGGL(conv_init_kernel, dim3(gb), dim3(256), 0, stream, q.out, q.bias,
-                       plan_uses_exchange(plan) ? 1 : 0, total, a.div_p, (uint32_t)q.OC);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_conv_out_init(q.out, q.bias, plan_uses_exchange(plan),
+                                              (uint32_t)q.OC * (uint32_t)a.N, a.div_p.d,
+                                              (uint32_t)q.OC, stream);
     if (e != hipSuccess) return e;
   }
   switch (plan.mode) {

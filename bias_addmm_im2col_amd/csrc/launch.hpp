@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "conv_window_plan.hpp"
+
 namespace baim {
 
 struct AddmmProblem {
@@ -54,6 +56,19 @@ inline bool conv_uses_gemm(const ConvProblem& q) {
 }
 
 hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream);
+// Output initialisation before split conv tiles land: the two-piece
+// sentinel, or bias[oc] (0 without a bias) for atomic K slices.  out is
+// [B, OC, P] with total = B*OC*P elements.
+hipError_t launch_conv_out_init(float* out, const float* bias, bool sentinel, uint32_t total,
+                                uint32_t P, uint32_t OC, hipStream_t stream);
+// groups == 1 convs with a compiled small-kernel geometry (3x3 at stride 1,
+// dilation 1 or 2) whose input rows fit the LDS window: the implicit GEMM
+// with the B operand read from an LDS copy of the input rows.
+inline WinShape win_shape(const ConvProblem& q) {
+  return WinShape{q.B, q.IC, q.H, q.W, q.OC, q.KH, q.KW, q.sH, q.sW, q.pH, q.pW, q.dH, q.dW,
+                  q.OH, q.OW, q.groups};
+}
+hipError_t launch_conv2d_window(const ConvProblem& p, const WinPlan& plan, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);

@@ -271,6 +271,34 @@ baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn,
                            int* bk, int* waves, int* kgroups, int* splits,
                            int* stream_blocks);
 
+/*
+ * baim_conv2d_plan: how conv2d_gemm_f32 computes a conv of these sizes on
+ * 16-byte aligned input and weight (the conv page routes groups == 1 convs
+ * through its im2col tiled GEMM and the others to their own kernels: "et_vk
+ * conv2d: route standard (groups==1) conv through an im2col tiled GEMM",
+ * Solution paragraph).  Arguments as conv2d_gemm_f32's sizes.  Writes
+ * *kernel:
+ *   0  the implicit-im2col GEMM; the tile fields are baim_gemm_plan's for
+ *      M = OC/groups, N = B*OH*OW, K = (IC/groups)*KH*KW;
+ *   1  the LDS-window kernel for compiled small kernels (3x3 at stride 1,
+ *      dilation 1 or 2, OW >= 32, W % 4 == 0, W + pW <= 60, pW <= 4,
+ *      IC % 4 == 0, groups == 1): block tile BM output channels x BN
+ *      output pixels of one image, BK = 8 input channels x KH*KW taps;
+ *   2  the direct kernels of grouped and depthwise convs (tile fields 0,
+ *      splits 1).
+ * splits and stream_blocks mean what they mean for baim_gemm_plan.  The
+ * overrides BAIM_TILE (kernel 0) and BAIM_CONV_WIN ("off", "tile", "2" or
+ * "sP"; kernel 1) apply here as in the op.  Returns the status
+ * conv2d_gemm_f32 would return for these sizes (SHAPE, TOO_LARGE), or
+ * BAIM_ERR_NULL if an output pointer is NULL.  Host-only; touches no GPU.
+ */
+baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W,
+                             int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                             int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                             int64_t dW, int64_t groups, int* kernel, int* bm,
+                             int* bn, int* bk, int* waves, int* kgroups,
+                             int* splits, int* stream_blocks);
+
 /* Text describing the last error returned on the calling thread ("" if the
  * last call succeeded).  The pointer stays valid until the next call on the
  * same thread. */

@@ -40,7 +40,8 @@ def test_source_hash_covers_the_gemm_and_conv_sources():
     # include
     import re
     csrc = os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc")
-    todo, seen = ["addmm.hip", "conv2d_gemm.hip", "tile_select.cpp"], set()
+    todo, seen = ["addmm.hip", "conv2d_gemm.hip", "conv_window.hip", "tile_select.cpp",
+                  "conv_window_plan.cpp"], set()
     while todo:
         f = todo.pop()
         if f in seen:

@@ -1,0 +1,125 @@
+"""GPU parity of the LDS-window conv kernel (3x3 at stride 1, dilation 1 or 2)
+against the fp64 oracle, through conv2d_gemm_f32.
+
+The kernel copies the input rows a block's output pixels touch into LDS
+and reads every im2col element from there; what it must get right is the
+window (rows above and below the image, columns left and right of it),
+output pixel runs that cross output rows and end past an image, k-tiles of
+eight input channels with a partial last one, ragged output channels, and
+the two-piece schedules.  Every case first checks through baim_conv2d_plan
+that the window kernel really is what runs.  Acceptance as in
+tests/test_parity.py; integer-valued inputs must match bit for bit.
+"""
+import pytest
+import torch
+
+import oracle
+from tests._parity import check_bitwise, check_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    from bias_addmm_im2col_amd import _capi
+    _capi.lib()
+
+
+def say(msg):
+    print(f"[window] {msg}", flush=True)
+
+
+def gen(shape, seed, kind="U"):
+    g = torch.Generator("cpu").manual_seed(seed)
+    if kind == "U":
+        return torch.rand(shape, generator=g) * 2 - 1
+    return torch.randint(-4, 5, shape, generator=g).float()
+
+
+def run(x, w, b, pad, dil):
+    import bias_addmm_im2col_amd as baim
+    out = baim.conv2d(dev(x), dev(w), dev(b), 1, pad, dil)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def plan(x, w, pad, dil):
+    import bias_addmm_im2col_amd as baim
+    return baim.conv2d_plan(tuple(x.shape), tuple(w.shape), 1, pad, dil)
+
+
+SHAPES = [
+    # B, IC, H, W, OC, pad, dil, bias
+    (1, 8, 40, 40, 128, 1, 1, True),        # one k-tile, whole 64-pixel runs? (1600 = 25 x 64)
+    (2, 12, 33, 36, 200, 1, 1, True),       # partial last k-tile, ragged OC, runs past each image
+    (1, 4, 7, 32, 64, (2, 1), 1, False),    # tall pad, short image: most window rows are padding
+    (3, 16, 34, 36, 136, 0, 1, True),       # no padding: OW = 34
+    (2, 20, 38, 40, 72, 2, 2, True),        # dilation 2, pad 2
+    (1, 8, 40, 44, 96, (1, 0), 2, False),   # dilation 2, pads smaller than the reach
+    (1, 12, 9, 60, 40, (1, 0), 1, True),    # widest row the window holds (W + pW + 4 = 64)
+    (2, 32, 56, 56, 256, 1, 1, True),       # the mid-stage shape at reduced batch and depth
+]
+
+
+@pytest.mark.parametrize("spec", ["", "tile", "2", "s7", "s3"])
+@pytest.mark.parametrize("B,IC,H,W,OC,pad,dil,has_bias", SHAPES)
+def test_window_conv(B, IC, H, W, OC, pad, dil, has_bias, spec, monkeypatch):
+    if spec:
+        monkeypatch.setenv("BAIM_CONV_WIN", spec)
+    x, w = gen((B, IC, H, W), 1), gen((OC, IC, 3, 3), 2)
+    b = gen((OC,), 3) if has_bias else None
+    p = plan(x, w, pad, dil)
+    say(f"BAIM_CONV_WIN={spec!r} x=[{B},{IC},{H},{W}] OC={OC} p={pad} d={dil} plan {p}")
+    assert p["kernel"] == 1
+    if spec == "2" and IC > 8:
+        assert p["splits"] == 2
+    if spec.startswith("s") and p["stream_blocks"] == 0:
+        # fewer workers than tiles is required for a stream; else one tile per block
+        assert p["splits"] == 1
+    check_close(run(x, w, b, pad, dil), oracle.conv2d(x, w, b, 1, pad, dil), IC * 9, 1.0,
+                f"window {spec}")
+    xi, wi, bi = gen((B, IC, H, W), 4, "I"), gen((OC, IC, 3, 3), 5, "I"), gen((OC,), 6, "I")
+    check_bitwise(run(xi, wi, bi, pad, dil), oracle.conv2d(xi, wi, bi, 1, pad, dil),
+                  f"window integer {spec}")
+
+
+def test_window_stream_pieces_are_reproducible(monkeypatch):
+    """A stream plan cuts tiles into two pieces; the exchange combines them
+    in an order-free way, so repeated launches give the same bits."""
+    import bias_addmm_im2col_amd as baim
+    monkeypatch.setenv("BAIM_CONV_WIN", "s13")
+    x, w, b = gen((2, 40, 36, 36), 7), gen((136, 40, 3, 3), 8), gen((136,), 9)
+    assert plan(x, w, 1, 1)["stream_blocks"] == 13
+    outs = [baim.conv2d(dev(x), dev(w), dev(b), 1, 1, 1).cpu() for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    check_close(outs[0].numpy(), oracle.conv2d(x, w, b, 1, 1, 1), 360, 1.0, "stream s13")
+
+
+def test_window_matches_the_gather_kernel_bitwise(monkeypatch):
+    """On integer inputs the window kernel and the general implicit-im2col
+    kernel (BAIM_CONV_WIN=off) both give the exact result."""
+    x, w, b = gen((2, 24, 32, 40), 10, "I"), gen((96, 24, 3, 3), 11, "I"), gen((96,), 12, "I")
+    win = run(x, w, b, 1, 1)
+    monkeypatch.setenv("BAIM_CONV_WIN", "off")
+    import bias_addmm_im2col_amd as baim
+    assert baim.conv2d_plan(tuple(x.shape), tuple(w.shape), 1, 1, 1)["kernel"] == 0
+    gat = run(x, w, b, 1, 1)
+    assert (win == gat).all()
+    check_bitwise(win, oracle.conv2d(x, w, b, 1, 1, 1), "window vs gather")
+
+
+def test_window_nonfinite_input_stays_local():
+    """An Inf in the input reaches exactly the outputs whose taps read it
+    (the padding columns and rows are zeros, not neighbouring data)."""
+    import numpy as np
+    x, w, b = gen((1, 8, 34, 36), 13), gen((64, 8, 3, 3), 14), gen((64,), 15)
+    x[0, 3, 0, 35] = float("inf")   # last column of the first row
+    x[0, 5, 33, 0] = float("-inf")  # first column of the last row
+    out = run(x, w, b, 1, 1)
+    ref = oracle.conv2d(x, w, b, 1, 1, 1)
+    bad = ~np.isfinite(ref.ref)
+    assert (~np.isfinite(out) == bad).all()
+    finite = np.isfinite(ref.ref)
+    assert (np.abs(out[finite] - ref.ref[finite]) <= oracle.tolerance(ref, 72)[finite]).all()
