@@ -8,28 +8,33 @@
 // The general conv kernel (conv2d_gemm.hip) gathers every im2col element
 // B[kk, n] with its own 4-byte load.  For a 3x3 kernel the nine taps of one
 // input channel read the same few input rows, shifted; here a block instead
-// copies, for each k-tile of CI = 8 input channels, the input rows its
-// output pixels touch (all W columns, zero rows above and below the image,
-// zero columns left and right) into LDS with 16-byte loads, and every MFMA
-// step reads its B value from that window at a compile-time offset from a
+// copies, for each k-tile of CI input channels, the input rows its output
+// pixels touch (all W columns, zero rows above and below the image, zero
+// columns left and right) into LDS with 16-byte loads, and every MFMA step
+// reads its B value from that window at a compile-time offset from a
 // per-lane base: one `ds_read_b32 v, base offset:imm`, no index arithmetic.
-// A 3x3 stride-1 k-tile of 8 channels and 64 pixels then costs 9 window
-// loads per block instead of 72 gathers.
+// A 3x3 stride-1 k-tile of 16 channels and 128 pixels then costs 21 window
+// loads per block instead of 288 gathers.
 //
-// Block tile: 128 output channels x 64 consecutive output pixels of one
-// image (a run of (oh, ow) in row-major order, so at OW >= 32 it touches at
-// most three output rows).  16 waves: 4 x 2 waves of 32 x 32 outputs, and
-// two wave groups that split each k-tile by input channel (group g takes
-// channels 4g..4g+3 of the k-tile); the groups' partial tiles are summed
-// through LDS in group order.
+// Block tile: BM output channels x BN consecutive output pixels of one
+// image (a run of (oh, ow) in row-major order; 128 pixels touch at most four
+// output rows when OW >= 43).  16 waves: WM x WN waves of 32 x 32 outputs,
+// and WK wave groups that split each k-tile by input channel (group g takes
+// channels [g*CI/WK, (g+1)*CI/WK) of the k-tile); the groups' partial tiles
+// are summed through LDS in group order.  The 64 x 128 block with 16
+// channels per k-tile measured faster than 128 x 64 with 8 (3x3 s1:
+// 139.5 -> 136.1 us; in steady state 72% -> 77% of the fp32 peak): half the
+// barriers per flop, fewer weight loads per flop, and lane-half weight runs
+// of 36 (a whole number of float4s, so 16-byte LDS writes).
 //
 // K order inside a wave group.  v_mfma_f32_32x32x2_f32 takes k = h from
-// lane-half h (lanes 32h..32h+31).  Step s (0 <= s < 2*TAPS) of half h uses
-// channel 4g + 2h + s/TAPS and tap s%TAPS.  The two halves' B addresses then
-// differ by the constant 2 channel planes, which folds into the per-lane
-// base, and each half's A values for consecutive steps are consecutive
-// weights of one row (weight k = ic*TAPS + tap), read 16 bytes at a time
-// from a segment of the A tile.  Any fp32 summation order is acceptable.
+// lane-half h (lanes 32h..32h+31).  Step s (0 <= s < CH*TAPS) of half h uses
+// channel g*CI/WK + h*CH + s/TAPS of the k-tile and tap s%TAPS, CH being the
+// channels per lane-half.  The two halves' B addresses then differ by the
+// constant CH channel planes, which folds into the per-lane base, and each
+// half's A values for consecutive steps are consecutive weights of one row
+// (weight k = ic*TAPS + tap), read 16 bytes at a time from a segment of the
+// A tile.  Any fp32 summation order is acceptable.
 #include <stdlib.h>
 
 #include "conv_window_plan.hpp"
@@ -39,25 +44,30 @@
 
 namespace baim {
 
-template <int KH_, int KW_, int SH_, int SW_, int DH_, int DW_, int WR_>
+template <int KH_, int KW_, int SH_, int SW_, int DH_, int DW_, int WR_, int BM_ = 128,
+          int BN_ = 64, int CI_ = 8, int WM_ = 4, int WN_ = 2, int WK_ = 2>
 struct WinCfg {
   static constexpr int KH = KH_, KW = KW_, SH = SH_, SW = SW_, DH = DH_, DW = DW_;
   static constexpr int TAPS = KH * KW;
-  static constexpr int BM = 128, BN = 64;
-  static constexpr int CI = 8;           // input channels per k-tile
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int CI = CI_;         // input channels per k-tile
   static constexpr int BK = CI * TAPS;   // k per k-tile
-  static constexpr int WM = 4, WN = 2, WK = 2;
+  static constexpr int WM = WM_, WN = WN_, WK = WK_;
   static constexpr int NT = 64 * WM * WN * WK;
   static constexpr int WTM = BM / WM, WTN = BN / WN, FM = 1, FN = 1;
+  static_assert(WTM == 32 && WTN == 32, "one 32 x 32 block per wave");
   static constexpr int BKW = BK / WK;
-  // A tile in LDS: per row four segments (wave group g, lane-half h at
-  // segment 2g + h) of HALF = 2*TAPS weights, each padded to a multiple of
+  // Channels of one lane-half: wave group g takes channels
+  // [g*CI/WK, (g+1)*CI/WK) of the k-tile, lane-half h the h-th half of them.
+  static constexpr int CH = CI / (2 * WK);
+  // A tile in LDS: per row 2*WK segments (wave group g, lane-half h at
+  // segment 2g + h) of HALF = CH*TAPS weights, each padded to a multiple of
   // four floats so that every segment starts 16-byte aligned.  The row
-  // stride is 4 (mod 16) floats: the 16-byte reads of 8 consecutive rows
-  // cover all 32 banks.
-  static constexpr int HALF = 2 * TAPS;
+  // stride is an odd multiple of 4 floats (mod 32): the 16-byte reads of 8
+  // consecutive rows cover all 32 banks.
+  static constexpr int HALF = CH * TAPS;
   static constexpr int SEG = (HALF + 3) / 4 * 4;
-  static constexpr int AS = 4 * SEG + 4;
+  static constexpr int AS = 2 * WK * SEG + 4;
   // Input window in LDS: per channel WR rows of RS floats; input column iw
   // sits at CL + iw, so columns [CL - pW, CL) and [CL + W, RS) hold zeros.
   static constexpr int RS = 64, CL = 4, WR = WR_;
@@ -70,8 +80,8 @@ struct WinCfg {
   static constexpr int A_NQ = (A_ITEMS + NT - 1) / NT;
   static constexpr int B_ITEMS = CI * WR * ((RS - CL) / 4);  // upper bound (W + CL <= RS)
   static constexpr int B_NQ = (B_ITEMS + NT - 1) / NT;
-  static_assert(HALF % 2 == 0 && BKW == 2 * HALF, "two channels per lane-half");
-  static_assert(AS % 16 == 4, "A rows must start 4 (mod 16) floats apart");
+  static_assert(CI % (2 * WK) == 0 && HALF % 2 == 0 && BKW == 2 * HALF, "lane-half channels");
+  static_assert(AS % 8 == 4, "A rows must start an odd multiple of 4 floats apart (mod 32)");
   static_assert((WK - 1) * BM * BN <= SMEM_FLOATS, "k-group reduction must fit in LDS");
   static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
@@ -121,12 +131,17 @@ struct WinALoader {
       const int i = threadIdx.x + C::NT * q;
       if (C::A_ITEMS % C::NT != 0 && i >= C::A_ITEMS) continue;
       const int r = i / (C::BK / 4), c = (i % (C::BK / 4)) * 4;
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-      const int k0 = c, k1 = c + 2;  // even, so each pair stays in one segment
-      *reinterpret_cast<f32x2*>(&As[r * C::AS + (k0 / C::HALF) * C::SEG + k0 % C::HALF]) =
-          f32x2{reg[S][q][0], reg[S][q][1]};
-      *reinterpret_cast<f32x2*>(&As[r * C::AS + (k1 / C::HALF) * C::SEG + k1 % C::HALF]) =
-          f32x2{reg[S][q][2], reg[S][q][3]};
+      if constexpr (C::HALF % 4 == 0) {
+        // segments hold whole float4s
+        *reinterpret_cast<f32x4*>(&As[r * C::AS + (c / C::HALF) * C::SEG + c % C::HALF]) = reg[S][q];
+      } else {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const int k0 = c, k1 = c + 2;  // even, so each pair stays in one segment
+        *reinterpret_cast<f32x2*>(&As[r * C::AS + (k0 / C::HALF) * C::SEG + k0 % C::HALF]) =
+            f32x2{reg[S][q][0], reg[S][q][1]};
+        *reinterpret_cast<f32x2*>(&As[r * C::AS + (k1 / C::HALF) * C::SEG + k1 % C::HALF]) =
+            f32x2{reg[S][q][2], reg[S][q][3]};
+      }
     }
   }
 };
@@ -289,7 +304,7 @@ __device__ __forceinline__ void win_piece(const WinArgs& p, float* smem, int m0,
 
   // The lane's output pixel, and where its taps start in the window.
   const int pix = p0 + ws.wn0 + c;
-  int boff = (4 * ws.kgroup + 2 * h) * C::PS + C::CL;
+  int boff = (2 * ws.kgroup + h) * C::CH * C::PS + C::CL;
   if (pix < p.P) {
     const int oh = pix / p.OW, ow = pix - oh * p.OW;
     boff += (oh - oh_first) * C::SH * C::RS + ow * C::SW - p.pW;
@@ -357,8 +372,8 @@ __global__ __launch_bounds__(C::NT) void conv_window_kernel(WinArgs p) {
 }
 
 // Compiled geometries (the host plan's table, conv_window_plan.hpp).
-typedef WinCfg<3, 3, 1, 1, 1, 1, 5> Win3x3S1D1;
-typedef WinCfg<3, 3, 1, 1, 2, 2, 7> Win3x3S1D2;
+typedef WinCfg<3, 3, 1, 1, 1, 1, 6, 64, 128, 16, 2, 4, 2> Win3x3S1D1;
+typedef WinCfg<3, 3, 1, 1, 2, 2, 8, 64, 128, 16, 2, 4, 2> Win3x3S1D2;
 
 template <class C>
 constexpr bool same_geom(int g) {

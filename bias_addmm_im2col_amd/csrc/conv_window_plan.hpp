@@ -9,8 +9,8 @@
 namespace baim {
 
 // Compiled window geometries: kernel KH x KW, stride, dilation, and WR, the
-// window rows held per input channel (enough for the output rows a run of
-// kWinBN pixels touches at OW >= 32).
+// window rows held per input channel (enough for the four output rows a
+// run of kWinBN pixels touches at OW >= 43).
 enum WinGeom { WIN_3x3_S1_D1 = 0, WIN_3x3_S1_D2 = 1, WIN_NGEOM = 2 };
 constexpr int kWinKH[WIN_NGEOM] = {3, 3};
 constexpr int kWinKW[WIN_NGEOM] = {3, 3};
@@ -18,10 +18,10 @@ constexpr int kWinSH[WIN_NGEOM] = {1, 1};
 constexpr int kWinSW[WIN_NGEOM] = {1, 1};
 constexpr int kWinDH[WIN_NGEOM] = {1, 2};
 constexpr int kWinDW[WIN_NGEOM] = {1, 2};
-constexpr int kWinWR[WIN_NGEOM] = {5, 7};
+constexpr int kWinWR[WIN_NGEOM] = {6, 8};
 // Block tile (output channels x output pixels of one image), input
 // channels per k-tile, LDS window row stride and the column of iw = 0.
-constexpr int kWinBM = 128, kWinBN = 64, kWinCI = 8, kWinRS = 64, kWinCL = 4;
+constexpr int kWinBM = 64, kWinBN = 128, kWinCI = 16, kWinRS = 64, kWinCL = 4;
 constexpr int kWinWaves = 16, kWinKGroups = 2;
 
 struct WinShape {

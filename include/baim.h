@@ -281,9 +281,9 @@ baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn,
  *   0  the implicit-im2col GEMM; the tile fields are baim_gemm_plan's for
  *      M = OC/groups, N = B*OH*OW, K = (IC/groups)*KH*KW;
  *   1  the LDS-window kernel for compiled small kernels (3x3 at stride 1,
- *      dilation 1 or 2, OW >= 32, W % 4 == 0, W + pW <= 60, pW <= 4,
+ *      dilation 1 or 2, OW >= 43, W % 4 == 0, W + pW <= 60, pW <= 4,
  *      IC % 4 == 0, groups == 1): block tile BM output channels x BN
- *      output pixels of one image, BK = 8 input channels x KH*KW taps;
+ *      output pixels of one image, BK = 16 input channels x KH*KW taps;
  *   2  the direct kernels of grouped and depthwise convs (tile fields 0,
  *      splits 1).
  * splits and stream_blocks mean what they mean for baim_gemm_plan.  The

@@ -2,9 +2,9 @@
 LDS-window kernel, how its tiles map to blocks, and that every window shape
 of the GPU parity tests really is planned onto it.
 
-The window kernel holds, per input channel, the input rows that a run of 64
-output pixels touches (5 rows for a 3x3 stride-1 kernel, 7 at dilation 2,
-when OW >= 32) with every column [-pW, W + pW) in a 64-float LDS row; it
+The window kernel holds, per input channel, the input rows that a run of 128
+output pixels touches (6 rows for a 3x3 stride-1 kernel, 8 at dilation 2,
+when OW >= 43) with every column [-pW, W + pW) in a 64-float LDS row; it
 loads whole rows with 16-byte loads (W % 4 == 0) and weight rows
 K = IC*9 with 16-byte loads (IC % 4 == 0).  Anything else takes the
 general implicit-im2col GEMM (kernel 0) or, for grouped convs, the direct
@@ -33,44 +33,45 @@ def plan(B, IC, H, W, OC, KH=3, KW=3, s=1, p=1, d=1, groups=1, pH=None):
 
 
 def test_mid_stage_convs_take_the_window_kernel():
-    # [4,256,56,56] x [256,256,3,3]: 2 x 196 tiles of 128 x 64, streamed
+    # [4,256,56,56] x [256,256,3,3]: 4 x 100 tiles of 64 x 128, streamed
     # over one block per CU
     for d in (1, 2):
         pl = plan(4, 256, 56, 56, 256, p=d, d=d)
         assert pl["kernel"] == 1 and pl["stream_blocks"] == 256 and pl["splits"] == 1
-        assert (pl["bm"], pl["bn"], pl["bk"], pl["waves"], pl["kgroups"]) == (128, 64, 72, 16, 2)
+        assert (pl["bm"], pl["bn"], pl["bk"], pl["waves"], pl["kgroups"]) == (64, 128, 144, 16, 2)
 
 
 def test_other_convs_keep_their_kernels():
     assert plan(4, 256, 57, 57, 256, s=2)["kernel"] == 0          # stride 2 (not compiled)
     assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 0     # the 7x7 stem
-    assert plan(2, 16, 40, 31, 64)["kernel"] == 0                   # OW = 31: runs touch 4 rows
-    assert plan(2, 16, 40, 30, 64)["kernel"] == 0                   # W % 4 != 0
-    assert plan(2, 18, 40, 40, 64)["kernel"] == 0                   # IC % 4 != 0
+    assert plan(2, 16, 40, 42, 64)["kernel"] == 0                   # OW = 42: runs touch 5 rows
+    assert plan(2, 16, 40, 44, 64)["kernel"] == 1                   # OW = 44: at most 4
+    assert plan(2, 16, 40, 46, 64)["kernel"] == 0                   # W % 4 != 0
+    assert plan(2, 18, 40, 48, 64)["kernel"] == 0                   # IC % 4 != 0
     assert plan(2, 16, 40, 64, 64, p=0)["kernel"] == 0              # W + 4 > 64 floats
     assert plan(2, 16, 40, 60, 64, p=0)["kernel"] == 1              # W + 4 = 64: fits
     assert plan(2, 16, 40, 60, 64, p=1)["kernel"] == 0              # W + pW + 4 > 64
-    assert plan(2, 16, 40, 40, 64, p=5)["kernel"] == 0              # pW above the 4 pad columns
-    assert plan(2, 16, 40, 40, 64, 1, 1, 1, 0)["kernel"] == 0       # 1x1 (not compiled)
-    assert plan(2, 16, 40, 40, 64, groups=2)["kernel"] == 0         # grouped: per-group GEMM
-    assert plan(2, 16, 40, 40, 16, groups=16)["kernel"] == 2        # depthwise: direct
-    assert plan(2, 16, 40, 40, 64, d=3, p=3)["kernel"] == 0         # dilation 3
+    assert plan(2, 16, 40, 48, 64, p=5)["kernel"] == 0              # pW above the 4 pad columns
+    assert plan(2, 16, 40, 48, 64, 1, 1, 1, 0)["kernel"] == 0       # 1x1 (not compiled)
+    assert plan(2, 16, 40, 48, 64, groups=2)["kernel"] == 0         # grouped: per-group GEMM
+    assert plan(2, 16, 40, 48, 16, groups=16)["kernel"] == 2        # depthwise: direct
+    assert plan(2, 16, 40, 48, 64, d=3, p=3)["kernel"] == 0         # dilation 3
 
 
 def test_window_schedules(monkeypatch):
     # few tiles: one per block; 257..511 tiles: stream over 256 blocks
-    assert plan(1, 64, 40, 40, 128)["stream_blocks"] == 0           # 25 tiles
-    assert plan(1, 64, 56, 56, 256)["stream_blocks"] == 0           # 98 tiles
-    assert plan(3, 64, 56, 56, 256)["stream_blocks"] == 256         # 294 tiles
-    assert plan(6, 64, 56, 56, 256)["stream_blocks"] == 0           # 588 tiles
-    assert plan(3, 8, 56, 56, 256)["stream_blocks"] == 0            # one k-tile: nothing to split
+    assert plan(1, 64, 48, 48, 128)["stream_blocks"] == 0           # 2 x 18 tiles
+    assert plan(1, 64, 56, 56, 256)["stream_blocks"] == 0           # 4 x 25 tiles
+    assert plan(3, 64, 56, 56, 256)["stream_blocks"] == 256         # 4 x 75 tiles
+    assert plan(6, 64, 56, 56, 256)["stream_blocks"] == 0           # 4 x 150 tiles
+    assert plan(3, 16, 56, 56, 256)["stream_blocks"] == 0           # one k-tile: nothing to split
     monkeypatch.setenv("BAIM_CONV_WIN", "2")
-    assert plan(1, 64, 40, 40, 128)["splits"] == 2
-    assert plan(1, 8, 40, 40, 128)["splits"] == 1                   # one k-tile
+    assert plan(1, 64, 48, 48, 128)["splits"] == 2
+    assert plan(1, 16, 48, 48, 128)["splits"] == 1                  # one k-tile
     monkeypatch.setenv("BAIM_CONV_WIN", "s7")
-    assert plan(1, 64, 40, 40, 128)["stream_blocks"] == 7
-    monkeypatch.setenv("BAIM_CONV_WIN", "s25")                      # not below the 25 tiles
-    assert plan(1, 64, 40, 40, 128)["stream_blocks"] == 0
+    assert plan(1, 64, 48, 48, 128)["stream_blocks"] == 7
+    monkeypatch.setenv("BAIM_CONV_WIN", "s36")                      # not below the 36 tiles
+    assert plan(1, 64, 48, 48, 128)["stream_blocks"] == 0
     monkeypatch.setenv("BAIM_CONV_WIN", "tile")
     pl = plan(4, 256, 56, 56, 256)
     assert pl["kernel"] == 1 and pl["stream_blocks"] == 0 and pl["splits"] == 1

@@ -5,7 +5,7 @@ The kernel copies the input rows a block's output pixels touch into LDS
 and reads every im2col element from there; what it must get right is the
 window (rows above and below the image, columns left and right of it),
 output pixel runs that cross output rows and end past an image, k-tiles of
-eight input channels with a partial last one, ragged output channels, and
+sixteen input channels with a partial last one, ragged output channels, and
 the two-piece schedules.  Every case first checks through baim_conv2d_plan
 that the window kernel really is what runs.  Acceptance as in
 tests/test_parity.py; integer-valued inputs must match bit for bit.
@@ -52,14 +52,14 @@ def plan(x, w, pad, dil):
 
 SHAPES = [
     # B, IC, H, W, OC, pad, dil, bias
-    (1, 8, 40, 40, 128, 1, 1, True),        # one k-tile, whole 64-pixel runs? (1600 = 25 x 64)
-    (2, 12, 33, 36, 200, 1, 1, True),       # partial last k-tile, ragged OC, runs past each image
-    (1, 4, 7, 32, 64, (2, 1), 1, False),    # tall pad, short image: most window rows are padding
-    (3, 16, 34, 36, 136, 0, 1, True),       # no padding: OW = 34
-    (2, 20, 38, 40, 72, 2, 2, True),        # dilation 2, pad 2
-    (1, 8, 40, 44, 96, (1, 0), 2, False),   # dilation 2, pads smaller than the reach
+    (1, 16, 48, 48, 64, 1, 1, True),        # one k-tile; 2304 pixels = 18 runs of 128
+    (2, 20, 33, 44, 100, 1, 1, True),       # partial last k-tile, ragged OC, runs past each image
+    (1, 4, 7, 44, 64, (2, 1), 1, False),    # tall pad, short image: most window rows are padding
+    (3, 36, 34, 48, 136, 0, 1, True),       # no padding: OW = 46
+    (2, 20, 38, 48, 72, 2, 2, True),        # dilation 2, pad 2
+    (1, 16, 40, 52, 96, (1, 0), 2, False),  # dilation 2, pads smaller than the reach: OW = 48
     (1, 12, 9, 60, 40, (1, 0), 1, True),    # widest row the window holds (W + pW + 4 = 64)
-    (2, 32, 56, 56, 256, 1, 1, True),       # the mid-stage shape at reduced batch and depth
+    (2, 64, 56, 56, 256, 1, 1, True),       # the mid-stage shape at reduced batch and depth
 ]
 
 
@@ -73,7 +73,7 @@ def test_window_conv(B, IC, H, W, OC, pad, dil, has_bias, spec, monkeypatch):
     p = plan(x, w, pad, dil)
     say(f"BAIM_CONV_WIN={spec!r} x=[{B},{IC},{H},{W}] OC={OC} p={pad} d={dil} plan {p}")
     assert p["kernel"] == 1
-    if spec == "2" and IC > 8:
+    if spec == "2" and IC > p["bk"] // 9:
         assert p["splits"] == 2
     if spec.startswith("s") and p["stream_blocks"] == 0:
         # fewer workers than tiles is required for a stream; else one tile per block
@@ -90,7 +90,7 @@ def test_window_stream_pieces_are_reproducible(monkeypatch):
     in an order-free way, so repeated launches give the same bits."""
     import bias_addmm_im2col_amd as baim
     monkeypatch.setenv("BAIM_CONV_WIN", "s13")
-    x, w, b = gen((2, 40, 36, 36), 7), gen((136, 40, 3, 3), 8), gen((136,), 9)
+    x, w, b = gen((2, 40, 36, 48), 7), gen((136, 40, 3, 3), 8), gen((136,), 9)
     assert plan(x, w, 1, 1)["stream_blocks"] == 13
     outs = [baim.conv2d(dev(x), dev(w), dev(b), 1, 1, 1).cpu() for _ in range(3)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
@@ -100,7 +100,7 @@ def test_window_stream_pieces_are_reproducible(monkeypatch):
 def test_window_matches_the_gather_kernel_bitwise(monkeypatch):
     """On integer inputs the window kernel and the general implicit-im2col
     kernel (BAIM_CONV_WIN=off) both give the exact result."""
-    x, w, b = gen((2, 24, 32, 40), 10, "I"), gen((96, 24, 3, 3), 11, "I"), gen((96,), 12, "I")
+    x, w, b = gen((2, 24, 32, 48), 10, "I"), gen((96, 24, 3, 3), 11, "I"), gen((96,), 12, "I")
     win = run(x, w, b, 1, 1)
     monkeypatch.setenv("BAIM_CONV_WIN", "off")
     import bias_addmm_im2col_amd as baim
@@ -114,8 +114,8 @@ def test_window_nonfinite_input_stays_local():
     """An Inf in the input reaches exactly the outputs whose taps read it
     (the padding columns and rows are zeros, not neighbouring data)."""
     import numpy as np
-    x, w, b = gen((1, 8, 34, 36), 13), gen((64, 8, 3, 3), 14), gen((64,), 15)
-    x[0, 3, 0, 35] = float("inf")   # last column of the first row
+    x, w, b = gen((1, 8, 34, 48), 13), gen((64, 8, 3, 3), 14), gen((64,), 15)
+    x[0, 3, 0, 47] = float("inf")   # last column of the first row
     x[0, 5, 33, 0] = float("-inf")  # first column of the last row
     out = run(x, w, b, 1, 1)
     ref = oracle.conv2d(x, w, b, 1, 1, 1)
