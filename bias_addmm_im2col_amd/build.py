@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libbaim.so")
-SOURCES = ["api.cpp", "tile_select.cpp", "conv_window_plan.cpp", "sdpa_plan.cpp", "addmm.hip", "conv2d_gemm.hip", "conv_window.hip",
+SOURCES = ["api.cpp", "tile_select.cpp", "conv_window_plan.cpp", "sdpa_plan.cpp", "addmm.hip", "conv2d_gemm.hip", "conv_window.hip", "conv_stem.hip",
            "conv_direct.hip", "sdpa.hip", "conv_transpose.hip"]
 ARCH = "gfx950"
 

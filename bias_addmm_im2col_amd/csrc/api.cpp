@@ -309,6 +309,15 @@ baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W, int64_
     *stream_blocks = wp.mode == baim::MODE_STREAM ? wp.workers : 0;
     return BAIM_OK;
   }
+  if (baim::plan_conv_stem(baim::win_shape(q), true, getenv("BAIM_CONV_WIN"))) {
+    *kernel = 3;
+    *bm = baim::kStemBM;
+    *bn = baim::kStemBN;
+    *bk = q.IC * q.KH * q.KW;
+    *waves = baim::kStemWaves;
+    *kgroups = 1;
+    return BAIM_OK;
+  }
   *kernel = 0;
   const int M = q.OC / q.groups, N = q.B * q.OH * q.OW, K = q.IC / q.groups * q.KH * q.KW;
   baim::GemmPlan p = baim::plan_gemm(M, N, K, getenv("BAIM_TILE"));

@@ -320,8 +320,10 @@ hipError_t launch_conv_out_init(float* out, const float* bias, bool sentinel, ui
 
 hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   const bool aligned = ((uintptr_t)q.x & 15) == 0 && ((uintptr_t)q.w & 15) == 0;
-  const WinPlan wp = plan_conv_window(win_shape(q), aligned, getenv("BAIM_CONV_WIN"));
+  const char* wspec = getenv("BAIM_CONV_WIN");
+  const WinPlan wp = plan_conv_window(win_shape(q), aligned, wspec);
   if (wp.geom >= 0) return launch_conv2d_window(q, wp, stream);
+  if (plan_conv_stem(win_shape(q), aligned, wspec)) return launch_conv2d_stem(q, stream);
   ConvArgs a;
   a.out = q.out;
   a.x = q.x;

@@ -1,0 +1,293 @@
+// conv_stem.hip -- the 3-channel patch-embed stem: groups==1 NCHW conv2d
+// with a 7x7 kernel at stride 4 on an image of few channels ("et_vk conv2d:
+// route standard (groups==1) conv through an im2col tiled GEMM", Problem
+// paragraph: the direct kernel re-reads the input for every output, which
+// the im2col GEMM fixes; Solution/Implementation: M = OC, N = B*OH*OW,
+// K = IC*KH*KW, B[kk, n] = x[b, ic, oh*s - pH + kh, ow*s - pW + kw] or 0,
+// bias per OC, NCHW output).
+//
+// K = 3*7*7 = 147 is too short for the k-tile pipeline of the GEMM kernels:
+// a block there spends most of its time filling and draining.  Here one
+// block computes 128 output channels x 144 consecutive output pixels of one
+// image (the stem's 192 x 192 x 128 output is exactly 256 such tiles, one
+// per CU) in a single pass over K:
+//   1. load the weights and the input the tile reads into LDS, once;
+//   2. run all of K on the matrix cores from LDS;
+//   3. add the bias and store NCHW.
+// LDS layouts, chosen so that every MFMA operand is one LDS read at a
+// compile-time offset (below 64 KB, so it fits the instruction) from a
+// per-lane base, without bank conflicts:
+//  * weights as they are in memory, [oc][ic][kh][kw] (147 floats a row, an
+//    odd stride: the 16 rows a lane group reads fall in 16 banks), copied
+//    with 16-byte stores; the padded tap kh' = 7 reads the next channel's
+//    first row (or the zeroed slack past the last row), which meets a zero
+//    input;
+//  * input "phase rows": for each (ic, kh'), input column u + pW (u the
+//    column relative to the padded image) is stored in phase row u % 4 at
+//    index u / 4, so the 144 pixels' taps for one kw are 144 consecutive
+//    floats.  A run of 144 pixels covers at most two output rows (OW >=
+//    144); each phase row holds both segments back to back.  Rows for
+//    kh' = 7, and input positions outside the image, are zeros.
+// MFMA: v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16, C 16x16; lane l supplies
+// A[l%16][l/16] and B[l/16][l%16], and holds C[4*(l/16) + r][l%16] in
+// register r).  Lane group j = l/16 takes kh' = 2j + q at step (ic, kw, q):
+// its A and B addresses differ from group 0's by constants (2j weight rows,
+// 2j phase-row blocks), which fold into the per-lane bases.  Each of the 16
+// waves owns 16 output channels and 5 or 4 of the 9 blocks of 16 pixels:
+// 42 steps of independent MFMAs, four waves to a SIMD.  The padded
+// kh' = 7 tap meets a zero input, so it adds exactly 0 for finite weights,
+// and an Inf or NaN in the input reaches only the outputs that read it.
+// The input window sits first in LDS so that its offsets, the larger ones,
+// fit the read instruction's immediate.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace baim {
+
+template <int IC_, int KH_, int KW_, int S_>
+struct StemCfg {
+  static constexpr int IC = IC_, KH = KH_, KW = KW_, S = S_;
+  static constexpr int KHP = 8;  // kh padded: four lane groups x two steps
+  static constexpr int BM = 128, BN = 144, NPB = BN / 16;
+  // 16 waves: wave w owns output channels 16*(w % 8) .. +15 and pixel
+  // blocks [0, PBH) (w < 8) or [PBH, NPB) (w >= 8)
+  static constexpr int PBH = (NPB + 1) / 2;
+  static constexpr int WAVES = 2 * (BM / 16), NT = 64 * WAVES;
+  static constexpr int E = (KW - 1) / S;  // extra phase slots per segment
+  // phase-row length: two segments of n1 + E and n2 + E slots; Q = 2 mod 4
+  // puts lane groups 0 and 1 (8Q floats apart) 16 banks apart
+  static constexpr int Q = ((BN + 2 * E + 1) / 4) * 4 + 2;
+  static constexpr int AS = IC * KH * KW;  // weight rows as in memory (odd)
+  // slack past the last row for the padded tap of the last channel
+  static constexpr int A_FLOATS = BM * AS + 16;
+  static constexpr int X_FLOATS = IC * KHP * S * Q;
+  static constexpr int SMEM_FLOATS = A_FLOATS + X_FLOATS;
+  static constexpr int WROW = IC * KH * KW;                 // weight floats per oc
+  static constexpr int W_ITEMS = (BM * WROW + 3) / 4;       // float4s of the block's weights
+  static constexpr int W_NQ = (W_ITEMS + NT - 1) / NT;
+  // input float4s per (ic, kh, segment): the segment's columns span
+  // S*(n-1) + KW floats, at most S*BN + KW - S, plus one for alignment
+  static constexpr int X_F4 = (S * BN + KW - S + 3) / 4 + 1;
+  static constexpr int X_NQI = (KH * 2 * X_F4 + NT - 1) / NT;  // per thread and channel
+  static_assert(KH < KHP && Q >= BN + 2 * E && Q % 4 == 2 && (S * Q) % 4 == 0, "stem layout");
+  static_assert(AS % 2 == 1 && (BM * AS) % 4 == 0, "odd weight rows, 16-byte copies");
+  static_assert(2 * 3 * KW + (IC - 1) * KH * KW + KW + KW - 1 < AS + 16, "padded tap stays in the slack");
+  static_assert(X_FLOATS * 4 <= 65536, "window offsets must fit the LDS read immediate");
+  static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS budget");
+};
+
+struct StemArgs {
+  float* out;
+  const float* x;
+  const float* w;
+  const float* bias;
+  int H, W, OC, pH, pW, OH, OW, P, tpi;
+  int x_elems, w_elems;
+};
+
+// One tile's input columns for one channel: item i covers float4 f of
+// the column span of (kh, segment g), row = kh*2 + g.  Items outside the
+// image (rows or columns) load zeros, which fill their window slots.
+template <class C>
+struct StemXItems {
+  f32x4 v[C::X_NQI];
+  int row[C::X_NQI];  // kh*2 + g, or -1 (no item)
+  int col[C::X_NQI];  // first input column of the float4
+
+  __device__ void load(const StemArgs& p, __amdgpu_buffer_rsrc_t xr, int b, int ic, int oh1,
+                       int n1, int n2, int f0_1, int f0_2, int colA1, int colA2) {
+#pragma unroll
+    for (int q = 0; q < C::X_NQI; ++q) {
+      const int i = threadIdx.x + C::NT * q;
+      const int r = i / C::X_F4, f = i - r * C::X_F4;
+      const int g = r & 1, kh = r >> 1;
+      const int n = g ? n2 : n1;
+      const int ih = (oh1 + g) * C::S - p.pH + kh;
+      const int c = ((g ? f0_2 : f0_1) + f) * 4;
+      const int colA = g ? colA2 : colA1;
+      const int colB = colA + C::S * (n - 1) + C::KW;  // one past the last column
+      const bool cover = kh < C::KH && n > 0 && c < colB && c + 4 > colA;
+      const bool ok = cover && ih >= 0 && ih < p.H && c >= 0 && c < p.W;
+      row[q] = cover ? r : -1;
+      col[q] = c;
+      // a float4 lies wholly inside the row (W % 4 == 0, aligned columns)
+      const int off = ((b * C::IC + ic) * p.H + ih) * p.W + c;
+      v[q] = Vec<4>::load(xr, ok ? (uint32_t)off * 4u : kOOB);
+    }
+  }
+  __device__ void store(float* Xs, int ic, int pW, int ow1, int n1, int n2, int seg2) const {
+#pragma unroll
+    for (int q = 0; q < C::X_NQI; ++q) {
+      if (row[q] < 0) continue;
+      const int g = row[q] & 1, kh = row[q] >> 1;
+      const int n = g ? n2 : n1;
+      const int owA = g ? 0 : ow1;
+      const int base = ((ic * C::KHP + kh) * C::S) * C::Q + (g ? seg2 : 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u = col[q] + e + pW;  // column in the padded image
+        const int rel = u - C::S * owA;  // within the segment's span
+        if (rel < 0 || rel >= C::S * (n - 1) + C::KW) continue;
+        Xs[base + (u % C::S) * C::Q + rel / C::S] = v[q][e];
+      }
+    }
+  }
+};
+
+// The steps of channel ic for pixel blocks [PB0, PB0 + NB) of the tile.
+template <class C, int NB>
+__device__ __forceinline__ void stem_mma(int ic, f32x4* acc, const float* Aw, const float* Xs,
+                                         const int* boff) {
+#pragma unroll
+  for (int kw = 0; kw < C::KW; ++kw)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      // weight [oc][ic][kh = 2j + q][kw]; window (ic, kh' = 2j + q, kw)
+      const float av = Aw[(ic * C::KH + q) * C::KW + kw];
+      const int off = ((ic * C::KHP + q) * C::S + kw % C::S) * C::Q + kw / C::S;
+      float bv[NB];
+#pragma unroll
+      for (int pb = 0; pb < NB; ++pb) bv[pb] = Xs[boff[pb] + off];
+#pragma unroll
+      for (int pb = 0; pb < NB; ++pb)
+        acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[pb], acc[pb], 0, 0, 0);
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
+  __shared__ __attribute__((aligned(16))) float smem[C::SMEM_FLOATS];
+  float* Xs = smem;
+  float* As = smem + C::X_FLOATS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // consecutive tiles (which share input rows) on the same XCD's L2
+  const int tm = blockIdx.y, tn = xcd_linear(blockIdx.x, gridDim.x);
+  const int m0 = tm * C::BM;
+  const int b = tn / p.tpi, p0 = (tn - b * p.tpi) * C::BN;
+  // the tile's pixels: segment 1 on output row oh1 from ow1, segment 2 on
+  // the next row from column 0
+  const int oh1 = p0 / p.OW, ow1 = p0 - oh1 * p.OW;
+  const int left = p.P - p0;
+  const int n1 = min(min(C::BN, p.OW - ow1), left);
+  const int n2 = min(C::BN - n1, left - n1);
+  const int seg2 = n1 + C::E;  // phase-row index where segment 2 starts
+
+  // 1. loads in flight, in the order they are needed: the block's weight
+  // rows (flat, 16-byte aligned), then the input columns channel by channel
+  const int wrows = min(C::BM, p.OC - m0);
+  const int wcount = wrows * C::WROW;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)m0 * C::WROW, wcount);
+  f32x4 wv[C::W_NQ];
+#pragma unroll
+  for (int q = 0; q < C::W_NQ; ++q) {
+    const int i = tid + C::NT * q;
+    wv[q] = Vec<4>::load(wr, i * 4 < wcount ? (uint32_t)i * 16u : kOOB);
+  }
+  const int colA1 = C::S * ow1 - p.pW, colA2 = -p.pW;  // first input column of each segment
+  const int f0_1 = colA1 >= 0 ? colA1 >> 2 : -((-colA1 + 3) >> 2);
+  const int f0_2 = colA2 >= 0 ? colA2 >> 2 : -((-colA2 + 3) >> 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, p.x_elems);
+  StemXItems<C> xi[C::IC];
+#pragma unroll
+  for (int ic = 0; ic < C::IC; ++ic) xi[ic].load(p, xr, b, ic, oh1, n1, n2, f0_1, f0_2, colA1, colA2);
+
+  // 2. zeros that no load writes: the padded tap's phase rows (kh' = 7)
+  // and the weight rows past OC with the slack after the last row
+  {
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int ZX = C::S * C::Q / 4;  // float4s of one channel's kh' = 7 rows
+    for (int i = tid; i < C::IC * ZX; i += C::NT) {
+      const int ic = i / ZX;
+      reinterpret_cast<f32x4*>(Xs + (ic * C::KHP + C::KHP - 1) * C::S * C::Q)[i - ic * ZX] = z;
+    }
+    const int za = ((C::BM - wrows) * C::AS + 16) / 4;
+    for (int i = tid; i < za; i += C::NT) reinterpret_cast<f32x4*>(As + wrows * C::AS)[i] = z;
+  }
+  // 3. weights and channel 0 into LDS
+#pragma unroll
+  for (int q = 0; q < C::W_NQ; ++q) {
+    const int i = tid + C::NT * q;
+    if (i * 4 < wcount) reinterpret_cast<f32x4*>(As)[i] = wv[q];
+  }
+  xi[0].store(Xs, 0, p.pW, ow1, n1, n2, seg2);
+  __syncthreads();
+
+  // 4. channel by channel: (after channel 0) wait for the channel's input,
+  // write it to LDS and sync, then run its steps on the matrix cores, the
+  // later channels' loads still in flight; wave w computes pixel blocks
+  // [0, PBH) (w < 8) or [PBH, NPB)
+  const int m = lane & 15, j = lane >> 4;
+  const int ocb = wave % (C::BM / 16), half = wave / (C::BM / 16);
+  const int pb0 = half ? C::PBH : 0, nb = half ? C::NPB - C::PBH : C::PBH;
+  const float* Aw = As + (ocb * 16 + m) * C::AS + 2 * j * C::KW;
+  int boff[C::PBH];
+#pragma unroll
+  for (int pb = 0; pb < C::PBH; ++pb) {
+    const int t = 16 * (pb0 + pb) + m;  // pixel within the tile
+    const int idx = t < n1 ? t : (t < n1 + n2 ? seg2 + (t - n1) : 0);
+    boff[pb] = idx + 2 * j * C::S * C::Q;
+  }
+  f32x4 acc[C::PBH];
+#pragma unroll
+  for (int pb = 0; pb < C::PBH; ++pb) acc[pb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ic = 0; ic < C::IC; ++ic) {
+    if (ic > 0) {
+      xi[ic].store(Xs, ic, p.pW, ow1, n1, n2, seg2);
+      __syncthreads();
+    }
+    if (half == 0)
+      stem_mma<C, C::PBH>(ic, acc, Aw, Xs, boff);
+    else
+      stem_mma<C, C::NPB - C::PBH>(ic, acc, Aw, Xs, boff);
+  }
+
+  // 5. + bias, NCHW store: lane (pixel m, group j) holds output channels
+  // 4j .. 4j+3 of the wave's 16
+  const int npix = n1 + n2;
+  float* ob = p.out + (size_t)b * p.OC * p.P + p0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int oc = m0 + ocb * 16 + 4 * j + r;
+    if (oc >= p.OC) continue;
+    const float bv = p.bias ? p.bias[oc] : 0.0f;
+#pragma unroll
+    for (int pb = 0; pb < C::PBH; ++pb) {
+      const int t = 16 * (pb0 + pb) + m;
+      if (pb < nb && t < npix) ob[(size_t)oc * p.P + t] = acc[pb][r] + bv;
+    }
+  }
+}
+
+typedef StemCfg<3, 7, 7, 4> Stem3x7x7S4;
+
+hipError_t launch_conv2d_stem(const ConvProblem& q, hipStream_t stream) {
+  typedef Stem3x7x7S4 C;
+  static_assert(C::IC == kStemIC && C::KH == kStemK && C::KW == kStemK && C::S == kStemS &&
+                    C::BM == kStemBM && C::BN == kStemBN && C::NT == 64 * kStemWaves,
+                "stem table out of sync with the compiled kernel");
+  StemArgs a;
+  a.out = q.out;
+  a.x = q.x;
+  a.w = q.w;
+  a.bias = q.bias;
+  a.H = q.H;
+  a.W = q.W;
+  a.OC = q.OC;
+  a.pH = q.pH;
+  a.pW = q.pW;
+  a.OH = q.OH;
+  a.OW = q.OW;
+  a.P = q.OH * q.OW;
+  a.tpi = (a.P + C::BN - 1) / C::BN;
+  a.x_elems = q.B * q.IC * q.H * q.W;
+  a.w_elems = q.OC * C::WROW;
+  const dim3 grid(q.B * a.tpi, (q.OC + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL(conv_stem_kernel<C>, grid, dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace baim

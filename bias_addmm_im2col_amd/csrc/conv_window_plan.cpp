@@ -72,4 +72,11 @@ WinPlan plan_conv_window(const WinShape& s, bool aligned, const char* spec) {
   return p;
 }
 
+bool plan_conv_stem(const WinShape& s, bool aligned, const char* spec) {
+  if (spec && strcmp(spec, "off") == 0) return false;
+  return aligned && s.groups == 1 && s.IC == kStemIC && s.KH == kStemK && s.KW == kStemK &&
+         s.sH == kStemS && s.sW == kStemS && s.dH == 1 && s.dW == 1 && s.OW >= kStemBN &&
+         s.W % 4 == 0 && s.OC % 4 == 0 && s.B >= 1 && s.OH >= 1;
+}
+
 }  // namespace baim

@@ -24,6 +24,12 @@ constexpr int kWinWR[WIN_NGEOM] = {6, 8};
 constexpr int kWinBM = 64, kWinBN = 128, kWinCI = 16, kWinRS = 64, kWinCL = 4;
 constexpr int kWinWaves = 16, kWinKGroups = 2;
 
+// The stem kernel (conv_stem.hip): IC = 3, 7 x 7 kernel, stride 4,
+// dilation 1, a block of 128 output channels x 144 output pixels in one
+// pass over K.  It needs OW >= 144 (a pixel run spans at most two output
+// rows), W % 4 == 0 and OC % 4 == 0 (16-byte input and weight loads).
+constexpr int kStemIC = 3, kStemK = 7, kStemS = 4, kStemBM = 128, kStemBN = 144, kStemWaves = 16;
+
 struct WinShape {
   int B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, OH, OW, groups;
 };
@@ -41,6 +47,10 @@ struct WinPlan {
 // (stream over P blocks, P below the tile count); an override the problem
 // cannot take falls back to one tile per block.
 WinPlan plan_conv_window(const WinShape& s, bool aligned, const char* spec);
+
+// Whether the stem kernel computes `s` (`aligned`: input and weight start
+// 16-byte aligned; `spec` as for plan_conv_window, "off" declines).
+bool plan_conv_stem(const WinShape& s, bool aligned, const char* spec);
 
 inline int64_t win_plan_blocks(const WinPlan& p) {
   if (p.mode == 2) return p.workers;

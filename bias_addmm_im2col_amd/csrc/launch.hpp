@@ -69,6 +69,9 @@ inline WinShape win_shape(const ConvProblem& q) {
                   q.OH, q.OW, q.groups};
 }
 hipError_t launch_conv2d_window(const ConvProblem& p, const WinPlan& plan, hipStream_t stream);
+// The 3-channel 7x7 stride-4 stem (plan_conv_stem): one pass over K per
+// block of 128 output channels x 144 output pixels.
+hipError_t launch_conv2d_stem(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);

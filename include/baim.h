@@ -285,10 +285,14 @@ baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn,
  *      IC % 4 == 0, groups == 1): block tile BM output channels x BN
  *      output pixels of one image, BK = 16 input channels x KH*KW taps;
  *   2  the direct kernels of grouped and depthwise convs (tile fields 0,
- *      splits 1).
+ *      splits 1);
+ *   3  the stem kernel for 3-channel 7x7 stride-4 convs (the patch-embed
+ *      stem the conv page motivates itself with; dilation 1, OW >= 144,
+ *      W % 4 == 0, OC % 4 == 0): one pass over all of K = 147 per block of
+ *      BM = 128 output channels x BN = 144 output pixels.
  * splits and stream_blocks mean what they mean for baim_gemm_plan.  The
  * overrides BAIM_TILE (kernel 0) and BAIM_CONV_WIN ("off", "tile", "2" or
- * "sP"; kernel 1) apply here as in the op.  Returns the status
+ * "sP"; kernel 1; "off" also declines kernel 3) apply here as in the op.  Returns the status
  * conv2d_gemm_f32 would return for these sizes (SHAPE, TOO_LARGE), or
  * BAIM_ERR_NULL if an output pointer is NULL.  Host-only; touches no GPU.
  */

@@ -43,7 +43,7 @@ def test_mid_stage_convs_take_the_window_kernel():
 
 def test_other_convs_keep_their_kernels():
     assert plan(4, 256, 57, 57, 256, s=2)["kernel"] == 0          # stride 2 (not compiled)
-    assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 0     # the 7x7 stem
+    assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 3     # the 7x7 stem: its own kernel
     assert plan(2, 16, 40, 42, 64)["kernel"] == 0                   # OW = 42: runs touch 5 rows
     assert plan(2, 16, 40, 44, 64)["kernel"] == 1                   # OW = 44: at most 4
     assert plan(2, 16, 40, 46, 64)["kernel"] == 0                   # W % 4 != 0
@@ -77,6 +77,29 @@ def test_window_schedules(monkeypatch):
     assert pl["kernel"] == 1 and pl["stream_blocks"] == 0 and pl["splits"] == 1
     monkeypatch.setenv("BAIM_CONV_WIN", "off")
     assert plan(4, 256, 56, 56, 256)["kernel"] == 0
+
+
+def test_stem_routing(monkeypatch):
+    pl = plan(1, 3, 768, 768, 128, 7, 7, 4, 3)
+    assert (pl["kernel"], pl["bm"], pl["bn"], pl["bk"], pl["waves"]) == (3, 128, 144, 147, 16)
+    assert plan(1, 3, 580, 572, 128, 7, 7, 4, 3)["kernel"] == 0     # OW = 143 < 144
+    assert plan(1, 3, 580, 580, 128, 7, 7, 4, 3)["kernel"] == 3     # OW = 145
+    assert plan(1, 3, 768, 766, 128, 7, 7, 4, 3)["kernel"] == 0     # W % 4 != 0
+    assert plan(1, 3, 768, 768, 126, 7, 7, 4, 3)["kernel"] == 0     # OC % 4 != 0
+    assert plan(1, 4, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 0     # 4 channels
+    assert plan(1, 3, 768, 768, 128, 7, 7, 2, 3)["kernel"] == 0     # stride 2
+    assert plan(1, 3, 768, 768, 128, 5, 5, 4, 2)["kernel"] == 0     # 5x5
+    assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3, d=2)["kernel"] == 0
+    monkeypatch.setenv("BAIM_CONV_WIN", "off")
+    assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 0
+
+
+def test_gpu_stem_shapes_are_planned_onto_the_stem_kernel():
+    from tests.test_parity_conv_stem import SHAPES
+    for B, H, W, OC, pad, _ in SHAPES:
+        pH, pW = (pad, pad) if isinstance(pad, int) else pad
+        st, pl = _capi.conv2d_plan(B, 3, H, W, OC, 7, 7, 4, 4, pH, pW, 1, 1, 1)
+        assert st == 0 and pl["kernel"] == 3, (B, H, W, OC, pad)
 
 
 def test_gpu_window_shapes_are_planned_onto_the_window_kernel():
