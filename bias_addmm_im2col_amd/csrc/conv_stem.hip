@@ -11,34 +11,35 @@
 // block computes 128 output channels x 144 consecutive output pixels of one
 // image (the stem's 192 x 192 x 128 output is exactly 256 such tiles, one
 // per CU) in a single pass over K:
-//   1. load the weights and the input the tile reads into LDS, once;
-//   2. run all of K on the matrix cores from LDS;
+//   1. issue the loads of the weights and of the input columns the tile
+//      reads, channel by channel;
+//   2. write the weights and channel 0 to LDS; run the MFMA steps whose
+//      taps are in channel 0 while channels 1 and 2 are still in flight;
+//      then channel 1's input, its steps, and so on;
 //   3. add the bias and store NCHW.
-// LDS layouts, chosen so that every MFMA operand is one LDS read at a
-// compile-time offset (below 64 KB, so it fits the instruction) from a
-// per-lane base, without bank conflicts:
+// LDS layouts, chosen so that every MFMA operand is one LDS read:
 //  * weights as they are in memory, [oc][ic][kh][kw] (147 floats a row, an
 //    odd stride: the 16 rows a lane group reads fall in 16 banks), copied
-//    with 16-byte stores; the padded tap kh' = 7 reads the next channel's
-//    first row (or the zeroed slack past the last row), which meets a zero
-//    input;
-//  * input "phase rows": for each (ic, kh'), input column u + pW (u the
-//    column relative to the padded image) is stored in phase row u % 4 at
-//    index u / 4, so the 144 pixels' taps for one kw are 144 consecutive
+//    with 16-byte stores;
+//  * input "phase rows": for each (ic, kh), input column u - pW (u the
+//    column in the padded image) is stored in phase row u % 4 at index
+//    u / 4, so tap (ic, kh, kw) of 16 consecutive pixels is 16 consecutive
 //    floats.  A run of 144 pixels covers at most two output rows (OW >=
-//    144); each phase row holds both segments back to back.  Rows for
-//    kh' = 7, and input positions outside the image, are zeros.
+//    144); each phase row holds both segments back to back, and rows are
+//    16 (mod 32) floats long so that neighbouring taps' rows sit 16 banks
+//    apart.  Input positions outside the image are zeros; one extra zero
+//    row serves the padding tap.
 // MFMA: v_mfma_f32_16x16x4_f32 (A 16x4, B 4x16, C 16x16; lane l supplies
 // A[l%16][l/16] and B[l/16][l%16], and holds C[4*(l/16) + r][l%16] in
-// register r).  Lane group j = l/16 takes kh' = 2j + q at step (ic, kw, q):
-// its A and B addresses differ from group 0's by constants (2j weight rows,
-// 2j phase-row blocks), which fold into the per-lane bases.  Each of the 16
-// waves owns 16 output channels and 5 or 4 of the 9 blocks of 16 pixels:
-// 42 steps of independent MFMAs, four waves to a SIMD.  The padded
-// kh' = 7 tap meets a zero input, so it adds exactly 0 for finite weights,
-// and an Inf or NaN in the input reaches only the outputs that read it.
-// The input window sits first in LDS so that its offsets, the larger ones,
-// fit the read instruction's immediate.
+// register r).  Step s takes taps k = 4s .. 4s+3 (k = (ic*7 + kh)*7 + kw in
+// memory order), lane group j = l/16 tap 4s + j: its weight is at a
+// compile-time offset from its row, and the window offset of its tap comes
+// from a 148-entry table in LDS.  K = 147 is 37 steps; the padding tap
+// k = 147 reads the next weight row (or zeroed slack) against the zero
+// row, adding exactly 0 for finite weights; an Inf or NaN in the input
+// reaches only the outputs that read it.  Each of the 16 waves owns 16
+// output channels and 5 or 4 of the 9 blocks of 16 pixels: four waves to a
+// SIMD, independent accumulators.  The window sits first in LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,34 +51,51 @@ namespace baim {
 template <int IC_, int KH_, int KW_, int S_>
 struct StemCfg {
   static constexpr int IC = IC_, KH = KH_, KW = KW_, S = S_;
-  static constexpr int KHP = 8;  // kh padded: four lane groups x two steps
+  static constexpr int K = IC * KH * KW;         // taps, weight floats per oc
+  static constexpr int KSTEPS = (K + 3) / 4;     // MFMA steps of 4 taps
   static constexpr int BM = 128, BN = 144, NPB = BN / 16;
   // 16 waves: wave w owns output channels 16*(w % 8) .. +15 and pixel
   // blocks [0, PBH) (w < 8) or [PBH, NPB) (w >= 8)
   static constexpr int PBH = (NPB + 1) / 2;
   static constexpr int WAVES = 2 * (BM / 16), NT = 64 * WAVES;
   static constexpr int E = (KW - 1) / S;  // extra phase slots per segment
-  // phase-row length: two segments of n1 + E and n2 + E slots; Q = 2 mod 4
-  // puts lane groups 0 and 1 (8Q floats apart) 16 banks apart
-  static constexpr int Q = ((BN + 2 * E + 1) / 4) * 4 + 2;
-  static constexpr int AS = IC * KH * KW;  // weight rows as in memory (odd)
-  // slack past the last row for the padded tap of the last channel
+  // phase-row length: two segments of n1 + E and n2 + E slots, rounded to
+  // 16 (mod 32) floats so that neighbouring taps' rows sit 16 banks apart
+  static constexpr int Q = ((BN + 2 * E + 16) / 32) * 32 + 16;
+  static constexpr int AS = K;  // weight rows as in memory (odd)
+  // slack past the last row: the padding tap k = K of the last row
   static constexpr int A_FLOATS = BM * AS + 16;
-  static constexpr int X_FLOATS = IC * KHP * S * Q;
-  static constexpr int SMEM_FLOATS = A_FLOATS + X_FLOATS;
-  static constexpr int WROW = IC * KH * KW;                 // weight floats per oc
-  static constexpr int W_ITEMS = (BM * WROW + 3) / 4;       // float4s of the block's weights
+  // window: [ic][kh][phase][Q], then one zero row for the padding tap
+  static constexpr int X_ROWS = IC * KH * S;
+  static constexpr int X_FLOATS = (X_ROWS + 1) * Q;
+  static constexpr int T_INTS = 4 * KSTEPS;  // per-tap window offsets
+  static constexpr int SMEM_FLOATS = X_FLOATS + A_FLOATS + T_INTS;
+  static constexpr int W_ITEMS = (BM * K + 3) / 4;  // float4s of the block's weights
   static constexpr int W_NQ = (W_ITEMS + NT - 1) / NT;
   // input float4s per (ic, kh, segment): the segment's columns span
   // S*(n-1) + KW floats, at most S*BN + KW - S, plus one for alignment
   static constexpr int X_F4 = (S * BN + KW - S + 3) / 4 + 1;
   static constexpr int X_NQI = (KH * 2 * X_F4 + NT - 1) / NT;  // per thread and channel
-  static_assert(KH < KHP && Q >= BN + 2 * E && Q % 4 == 2 && (S * Q) % 4 == 0, "stem layout");
-  static_assert(AS % 2 == 1 && (BM * AS) % 4 == 0, "odd weight rows, 16-byte copies");
-  static_assert(2 * 3 * KW + (IC - 1) * KH * KW + KW + KW - 1 < AS + 16, "padded tap stays in the slack");
-  static_assert(X_FLOATS * 4 <= 65536, "window offsets must fit the LDS read immediate");
+  static_assert(Q >= BN + 2 * E && Q % 32 == 16 && (S * Q) % 4 == 0, "stem layout");
+  static_assert(AS % 2 == 1 && (BM * AS) % 4 == 0 && (X_FLOATS + A_FLOATS) % 4 == 0,
+                "odd weight rows, 16-byte copies");
+  static_assert(T_INTS - K <= 16, "padding taps stay in the slack");
   static_assert(SMEM_FLOATS * 4 <= 160 * 1024, "LDS budget");
 };
+
+// Window offset of tap k = (ic*KH + kh)*KW + kw: phase row (ic, kh, kw % S)
+// at index kw / S; the padding taps (k >= K) read the zero row.
+template <class C>
+__host__ __device__ constexpr int stem_tap_off(int k) {
+  return k >= C::K ? C::X_ROWS * C::Q
+                   : (((k / C::KW) * C::S + (k % C::KW) % C::S) * C::Q + (k % C::KW) / C::S);
+}
+
+// The first MFMA step that needs channel ic (tap ic*KH*KW).
+template <class C>
+__host__ __device__ constexpr int stem_stage_step(int ic) {
+  return ic >= C::IC ? C::KSTEPS : (ic * C::KH * C::KW) / 4;
+}
 
 struct StemArgs {
   float* out;
@@ -125,7 +143,7 @@ struct StemXItems {
       const int g = row[q] & 1, kh = row[q] >> 1;
       const int n = g ? n2 : n1;
       const int owA = g ? 0 : ow1;
-      const int base = ((ic * C::KHP + kh) * C::S) * C::Q + (g ? seg2 : 0);
+      const int base = ((ic * C::KH + kh) * C::S) * C::Q + (g ? seg2 : 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int u = col[q] + e + pW;  // column in the padded image
@@ -137,24 +155,40 @@ struct StemXItems {
   }
 };
 
-// The steps of channel ic for pixel blocks [PB0, PB0 + NB) of the tile.
-template <class C, int NB>
-__device__ __forceinline__ void stem_mma(int ic, f32x4* acc, const float* Aw, const float* Xs,
-                                         const int* boff) {
+// Steps [S0, S1) for the wave's NB pixel blocks: lane group j takes tap
+// k = 4s + j, whose window offset it reads from the tap table.
+template <class C, int S0, int S1, int NB>
+__device__ __forceinline__ void stem_mma(f32x4* acc, const float* Aw, const int* Tj,
+                                         const float* Xs, const int* boff) {
 #pragma unroll
-  for (int kw = 0; kw < C::KW; ++kw)
+  for (int s = S0; s < S1; ++s) {
+    const float av = Aw[4 * s];
+    const int t = Tj[4 * s];
+    float bv[NB];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // weight [oc][ic][kh = 2j + q][kw]; window (ic, kh' = 2j + q, kw)
-      const float av = Aw[(ic * C::KH + q) * C::KW + kw];
-      const int off = ((ic * C::KHP + q) * C::S + kw % C::S) * C::Q + kw / C::S;
-      float bv[NB];
+    for (int pb = 0; pb < NB; ++pb) bv[pb] = Xs[boff[pb] + t];
 #pragma unroll
-      for (int pb = 0; pb < NB; ++pb) bv[pb] = Xs[boff[pb] + off];
-#pragma unroll
-      for (int pb = 0; pb < NB; ++pb)
-        acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[pb], acc[pb], 0, 0, 0);
+    for (int pb = 0; pb < NB; ++pb)
+      acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[pb], acc[pb], 0, 0, 0);
+  }
+}
+
+template <class C, int IC0>
+__device__ __forceinline__ void stem_stages(f32x4* acc, const float* Aw, const int* Tj, float* Xs,
+                                            const int* boff, int half, StemXItems<C>* xi,
+                                            int pW, int ow1, int n1, int n2, int seg2) {
+  if constexpr (IC0 < C::IC) {
+    if (IC0 > 0) {
+      xi[IC0].store(Xs, IC0, pW, ow1, n1, n2, seg2);
+      __syncthreads();
     }
+    constexpr int S0 = stem_stage_step<C>(IC0), S1 = stem_stage_step<C>(IC0 + 1);
+    if (half == 0)
+      stem_mma<C, S0, S1, C::PBH>(acc, Aw, Tj, Xs, boff);
+    else
+      stem_mma<C, S0, S1, C::NPB - C::PBH>(acc, Aw, Tj, Xs, boff);
+    stem_stages<C, IC0 + 1>(acc, Aw, Tj, Xs, boff, half, xi, pW, ow1, n1, n2, seg2);
+  }
 }
 
 template <class C>
@@ -162,6 +196,7 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[C::SMEM_FLOATS];
   float* Xs = smem;
   float* As = smem + C::X_FLOATS;
+  int* Ts = reinterpret_cast<int*>(smem + C::X_FLOATS + C::A_FLOATS);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // consecutive tiles (which share input rows) on the same XCD's L2
   const int tm = blockIdx.y, tn = xcd_linear(blockIdx.x, gridDim.x);
@@ -178,8 +213,8 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   // 1. loads in flight, in the order they are needed: the block's weight
   // rows (flat, 16-byte aligned), then the input columns channel by channel
   const int wrows = min(C::BM, p.OC - m0);
-  const int wcount = wrows * C::WROW;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)m0 * C::WROW, wcount);
+  const int wcount = wrows * C::K;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)m0 * C::K, wcount);
   f32x4 wv[C::W_NQ];
 #pragma unroll
   for (int q = 0; q < C::W_NQ; ++q) {
@@ -194,17 +229,15 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
 #pragma unroll
   for (int ic = 0; ic < C::IC; ++ic) xi[ic].load(p, xr, b, ic, oh1, n1, n2, f0_1, f0_2, colA1, colA2);
 
-  // 2. zeros that no load writes: the padded tap's phase rows (kh' = 7)
-  // and the weight rows past OC with the slack after the last row
+  // 2. what no load writes: the zero row, the weight rows past OC with the
+  // slack after the last row, and the tap table
   {
     const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int ZX = C::S * C::Q / 4;  // float4s of one channel's kh' = 7 rows
-    for (int i = tid; i < C::IC * ZX; i += C::NT) {
-      const int ic = i / ZX;
-      reinterpret_cast<f32x4*>(Xs + (ic * C::KHP + C::KHP - 1) * C::S * C::Q)[i - ic * ZX] = z;
-    }
+    for (int i = tid; i < C::Q / 4; i += C::NT)
+      reinterpret_cast<f32x4*>(Xs + C::X_ROWS * C::Q)[i] = z;
     const int za = ((C::BM - wrows) * C::AS + 16) / 4;
     for (int i = tid; i < za; i += C::NT) reinterpret_cast<f32x4*>(As + wrows * C::AS)[i] = z;
+    if (tid < C::T_INTS) Ts[tid] = stem_tap_off<C>(tid);
   }
   // 3. weights and channel 0 into LDS
 #pragma unroll
@@ -216,34 +249,24 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   __syncthreads();
 
   // 4. channel by channel: (after channel 0) wait for the channel's input,
-  // write it to LDS and sync, then run its steps on the matrix cores, the
-  // later channels' loads still in flight; wave w computes pixel blocks
-  // [0, PBH) (w < 8) or [PBH, NPB)
+  // write it to LDS and sync, then run the steps whose taps need no later
+  // channel, the later channels' loads still in flight; wave w computes
+  // pixel blocks [0, PBH) (w < 8) or [PBH, NPB)
   const int m = lane & 15, j = lane >> 4;
   const int ocb = wave % (C::BM / 16), half = wave / (C::BM / 16);
   const int pb0 = half ? C::PBH : 0, nb = half ? C::NPB - C::PBH : C::PBH;
-  const float* Aw = As + (ocb * 16 + m) * C::AS + 2 * j * C::KW;
+  const float* Aw = As + (ocb * 16 + m) * C::AS + j;  // tap k = 4s + j at Aw[4s]
+  const int* Tj = Ts + j;
   int boff[C::PBH];
 #pragma unroll
   for (int pb = 0; pb < C::PBH; ++pb) {
     const int t = 16 * (pb0 + pb) + m;  // pixel within the tile
-    const int idx = t < n1 ? t : (t < n1 + n2 ? seg2 + (t - n1) : 0);
-    boff[pb] = idx + 2 * j * C::S * C::Q;
+    boff[pb] = t < n1 ? t : (t < n1 + n2 ? seg2 + (t - n1) : 0);
   }
   f32x4 acc[C::PBH];
 #pragma unroll
   for (int pb = 0; pb < C::PBH; ++pb) acc[pb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int ic = 0; ic < C::IC; ++ic) {
-    if (ic > 0) {
-      xi[ic].store(Xs, ic, p.pW, ow1, n1, n2, seg2);
-      __syncthreads();
-    }
-    if (half == 0)
-      stem_mma<C, C::PBH>(ic, acc, Aw, Xs, boff);
-    else
-      stem_mma<C, C::NPB - C::PBH>(ic, acc, Aw, Xs, boff);
-  }
+  stem_stages<C, 0>(acc, Aw, Tj, Xs, boff, half, xi, p.pW, ow1, n1, n2, seg2);
 
   // 5. + bias, NCHW store: lane (pixel m, group j) holds output channels
   // 4j .. 4j+3 of the wave's 16
@@ -284,7 +307,7 @@ hipError_t launch_conv2d_stem(const ConvProblem& q, hipStream_t stream) {
   a.P = q.OH * q.OW;
   a.tpi = (a.P + C::BN - 1) / C::BN;
   a.x_elems = q.B * q.IC * q.H * q.W;
-  a.w_elems = q.OC * C::WROW;
+  a.w_elems = q.OC * C::K;
   const dim3 grid(q.B * a.tpi, (q.OC + C::BM - 1) / C::BM);
   hipLaunchKernelGGL(conv_stem_kernel<C>, grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
