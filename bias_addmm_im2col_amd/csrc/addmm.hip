@@ -57,12 +57,26 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
     al.init(p.A, m0, p.M, p.K);
   typename std::conditional<WNK, KRowLoader<T, VB, T::BN, true>, ColTileLoader<T, VB>>::type bl;
   bl.init(p.B, n0, p.N, p.K);
+  const int c = lane & 31;
+  // A whole tile with a full self [M,N] and one 32 x 32 block per wave:
+  // its 16 self values per lane are loaded before the k loop, so the
+  // epilogue does not wait for them (they arrive with the first k-tile).
+  constexpr bool kSelfAhead = T::FM * T::FN == 1 && T::WK < 4;  // registers to spare
+  float sv[16];
+  const bool self_ahead = kSelfAhead && epi == EPI_STORE && p.self_mode == 2 && ws.kgroup == 0;
+  if (kSelfAhead && self_ahead) {
+    const int n = n0 + ws.wn0 + c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + ws.wm0 + acc_row(r, lane);
+      sv[r] = (m < p.M && n < p.N) ? p.self[(size_t)m * p.N + n] : 0.0f;
+    }
+  }
   Accum<T> acc;
   mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // Fused epilogue: beta*self + alpha*acc, self broadcast from [N] or full.
-  const int c = lane & 31;
   if (epi == EPI_EXCHANGE) {
     // Two-piece tile: swap every partial in first (all swaps in flight at
     // once), then finish the elements whose other piece had already landed.
@@ -120,8 +134,8 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
         } else if (p.self_mode == 0) {
           p.out[o] = p.alpha * v;
         } else {
-          const float sv = p.self_mode == 1 ? srow : p.self[o];
-          p.out[o] = fmaf(p.alpha, v, p.beta * sv);
+          const float s = p.self_mode == 1 ? srow : ((kSelfAhead && self_ahead) ? sv[r] : p.self[o]);
+          p.out[o] = fmaf(p.alpha, v, p.beta * s);
         }
       }
   }
