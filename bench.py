@@ -33,12 +33,11 @@ METRIC = "fp32 TFLOP/s (addmm, im2col conv2d) and % of MI355X fp32 MFMA peak"
 STEP_CASES = ["conv3x3_56_s1", "conv3x3_56_d2", "conv3x3_57_s2",
               "up_proj_4096x1024x4096", "down_proj_4096x4096x1024",
               "ragged_577x1024x4096_full_self"]
-# Every source the step's kernels are built from (the .hip files and all the
-# headers they include) plus the compiler flags: the committed counter runs
-# are only valid for exactly these.
-KERNEL_SOURCES = ["gemm_core.hpp", "index_math.hpp", "tile_select.hpp", "tile_select.cpp",
-                  "launch.hpp", "im2col_nhwc.hpp", "conv_window_plan.hpp", "conv_window_plan.cpp",
-                  "addmm.hip", "conv2d_gemm.hip", "conv_window.hip"]
+# Every kernel and host source of the library plus the compiler flags: the
+# committed counter runs (which cover the step's cases and every other case
+# bench.py times) are only valid for exactly these.
+CSRC = os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc")
+KERNEL_SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp", ".h")))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -52,6 +51,11 @@ def parse():
                          "run at the GPU's steady clock")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--profile-cases", default=None, metavar="NAMES",
+                    help="instead of the metric, launch each named case (comma list; 'step' is the "
+                         "step's cases, 'all' every case) once when it is set up, then --steps "
+                         "times back to back, case after case: a fixed dispatch sequence for the "
+                         "rocprofv3 counter runs that bench_counters.py reads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="instead of the GEMM workload, run plain device-to-device copies of a "
                          "known size (reference for scaling the FETCH_SIZE/WRITE_SIZE counters)")
@@ -74,12 +78,47 @@ def calibrate_copy():
                       "copies": 10}), flush=True)
 
 
+def all_case_names(I):
+    return (STEP_CASES + OTHER_CONFIG_CASES + list(I.LINEAR_CASES) + list(I.GROUPED_CASES)
+            + list(I.NHWC_CASES) + list(I.CONVT_CASES) + list(I.SDPA_CASES))
+
+
+def profile_case_names(spec, I):
+    names = []
+    for n in spec.split(","):
+        names += STEP_CASES if n == "step" else all_case_names(I) if n == "all" else [n]
+    return names
+
+
+def profile_cases(torch, baim, I, names, steps):
+    """Dispatch order: every case's set-up launch, in the order given, then
+    `steps` launches of the first case, `steps` of the second, and so on.
+    A one-element torch fill (a kernel of torch's own, named after its fill
+    functor) follows the set-up launches and each case's run, so that a
+    counter trace splits into the cases' dispatches without knowing how many
+    kernels one call launches.  Prints the sequence as one JSON line."""
+    cases = [Case(n, torch, baim, I) for n in names]
+    marker = torch.empty(1, device="cuda")
+    torch.cuda.synchronize()
+    marker.fill_(1.0)
+    for cs in cases:
+        for _ in range(steps):
+            cs.launch()
+        marker.fill_(1.0)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_cases": names, "kernels": [cs.kernel for cs in cases],
+                      "algorithmic_bytes": [cs.bytes for cs in cases],
+                      "flops": [cs.flops for cs in cases], "launches": steps,
+                      "marker": "FillFunctor", "step_cases": STEP_CASES,
+                      "kernel_source_sha": kernel_source_hash()}), flush=True)
+
+
 def kernel_source_hash() -> str:
     from bias_addmm_im2col_amd import build
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in KERNEL_SOURCES + ["../../include/baim.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     h.update(" ".join(build.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
@@ -168,8 +207,8 @@ class Case:
         if c.kind == "conv" and not c.channels_last:
             p = baim.conv2d_plan((c.B, c.IC, c.H, c.W), (c.OC, c.IC // c.groups, c.KH, c.KW),
                                  c.stride, c.padding, c.dilation, c.groups)
-            if p["kernel"] == 1:
-                kname = "conv_window_kernel"
+            if p["kernel"] in (1, 3):  # the LDS-window and stem kernels
+                kname = "conv_window_kernel" if p["kernel"] == 1 else "conv_stem_kernel"
                 geom = (f"{c.KH}x{c.KW} s{c.stride[0]} d{c.dilation[0]}, ")
         self.plan = p
         # one kernel instance per (op, geometry, block tile, waves, wave groups, K split)
@@ -187,6 +226,7 @@ class Case:
             self.run()
             self.launch = raw_call(torch, "addmm_f32", self.out, self.s, int(c.self_2d), self.a,
                                    self.b, c.M, c.N, c.K, float(c.beta), float(c.alpha))
+            self.bytes = 4 * (a.numel() + b.numel() + s.numel() + self.out.numel())
         elif c.kind == "linear":
             x, w, b = I.linear_inputs(c)
             self.host = (x, w, b)
@@ -198,6 +238,8 @@ class Case:
             self.run()
             self.launch = raw_call(torch, "linear_f32", self.out, self.x, self.w, self.bias, c.M,
                                    c.N, c.K)
+            self.bytes = 4 * (x.numel() + w.numel() + (0 if b is None else b.numel())
+                              + self.out.numel())
         else:
             x, w, bias = I.conv_inputs(c)
             self.host = (x, w, bias)
@@ -338,6 +380,9 @@ def main():
     from bias_addmm_im2col_amd import _capi
     from bias_addmm_im2col_amd import inputs as I
     _capi.lib()  # fail loudly if libbaim.so is missing
+    if args.profile_cases:
+        profile_cases(torch, baim, I, profile_case_names(args.profile_cases, I), args.steps)
+        return
 
     cases = [Case(n, torch, baim, I) for n in STEP_CASES]
     torch.cuda.synchronize()

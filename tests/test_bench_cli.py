@@ -35,19 +35,23 @@ def test_counter_figures_only_for_the_hashed_kernel_sources(tmp_path, monkeypatc
     assert bench.load_counters(kern) == (None, None)
 
 
-def test_source_hash_covers_the_gemm_and_conv_sources():
-    # the step's kernel sources and, transitively, every local header they
-    # include
+def test_source_hash_covers_every_library_source():
+    # every kernel, header and host source of the library, and, transitively,
+    # every local header they include
     import re
     csrc = os.path.join(ROOT, "bias_addmm_im2col_amd", "csrc")
-    todo, seen = ["addmm.hip", "conv2d_gemm.hip", "conv_window.hip", "tile_select.cpp",
-                  "conv_window_plan.cpp"], set()
+    todo = [f for f in os.listdir(csrc) if f.endswith((".hip", ".cpp"))]
+    seen = set()
     while todo:
         f = todo.pop()
         if f in seen:
             continue
         seen.add(f)
+        if f == "baim.h":  # the public header, hashed from include/
+            continue
         todo += re.findall(r'^#include "([^"]+)"', open(os.path.join(csrc, f)).read(), flags=re.M)
+    seen.discard("baim.h")
+    assert "conv_stem.hip" in seen and "sdpa.hip" in seen
     assert seen <= set(bench.KERNEL_SOURCES), seen - set(bench.KERNEL_SOURCES)
     assert len(bench.kernel_source_hash()) == 16
 
