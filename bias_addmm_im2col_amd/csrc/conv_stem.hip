@@ -12,11 +12,11 @@
 // image (the stem's 192 x 192 x 128 output is exactly 256 such tiles, one
 // per CU) in a single pass over K:
 //   1. issue the loads of the weights and of the input columns the tile
-//      reads, channel by channel;
-//   2. write the weights and channel 0 to LDS; run the MFMA steps whose
-//      taps are in channel 0 while channels 1 and 2 are still in flight;
-//      then channel 1's input, its steps, and so on;
+//      reads;
+//   2. write them to LDS, one barrier, then all 37 MFMA steps from LDS;
 //   3. add the bias and store NCHW.
+// (Writing channel 0 first and running its steps while channels 1 and 2
+// were still in flight, with a barrier per channel, measured 1% slower.)
 // LDS layouts, chosen so that every MFMA operand is one LDS read:
 //  * weights as they are in memory, [oc][ic][kh][kw] (147 floats a row, an
 //    odd stride: the 16 rows a lane group reads fall in 16 banks), copied
@@ -89,12 +89,6 @@ template <class C>
 __host__ __device__ constexpr int stem_tap_off(int k) {
   return k >= C::K ? C::X_ROWS * C::Q
                    : (((k / C::KW) * C::S + (k % C::KW) % C::S) * C::Q + (k % C::KW) / C::S);
-}
-
-// The first MFMA step that needs channel ic (tap ic*KH*KW).
-template <class C>
-__host__ __device__ constexpr int stem_stage_step(int ic) {
-  return ic >= C::IC ? C::KSTEPS : (ic * C::KH * C::KW) / 4;
 }
 
 struct StemArgs {
@@ -173,24 +167,6 @@ __device__ __forceinline__ void stem_mma(f32x4* acc, const float* Aw, const int*
   }
 }
 
-template <class C, int IC0>
-__device__ __forceinline__ void stem_stages(f32x4* acc, const float* Aw, const int* Tj, float* Xs,
-                                            const int* boff, int half, StemXItems<C>* xi,
-                                            int pW, int ow1, int n1, int n2, int seg2) {
-  if constexpr (IC0 < C::IC) {
-    if (IC0 > 0) {
-      xi[IC0].store(Xs, IC0, pW, ow1, n1, n2, seg2);
-      __syncthreads();
-    }
-    constexpr int S0 = stem_stage_step<C>(IC0), S1 = stem_stage_step<C>(IC0 + 1);
-    if (half == 0)
-      stem_mma<C, S0, S1, C::PBH>(acc, Aw, Tj, Xs, boff);
-    else
-      stem_mma<C, S0, S1, C::NPB - C::PBH>(acc, Aw, Tj, Xs, boff);
-    stem_stages<C, IC0 + 1>(acc, Aw, Tj, Xs, boff, half, xi, pW, ow1, n1, n2, seg2);
-  }
-}
-
 template <class C>
 __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[C::SMEM_FLOATS];
@@ -210,8 +186,8 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   const int n2 = min(C::BN - n1, left - n1);
   const int seg2 = n1 + C::E;  // phase-row index where segment 2 starts
 
-  // 1. loads in flight, in the order they are needed: the block's weight
-  // rows (flat, 16-byte aligned), then the input columns channel by channel
+  // 1. loads in flight: the block's weight rows (flat, 16-byte aligned),
+  // then the input columns
   const int wrows = min(C::BM, p.OC - m0);
   const int wcount = wrows * C::K;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)m0 * C::K, wcount);
@@ -239,19 +215,17 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
     for (int i = tid; i < za; i += C::NT) reinterpret_cast<f32x4*>(As + wrows * C::AS)[i] = z;
     if (tid < C::T_INTS) Ts[tid] = stem_tap_off<C>(tid);
   }
-  // 3. weights and channel 0 into LDS
+  // 3. weights and input into LDS
 #pragma unroll
   for (int q = 0; q < C::W_NQ; ++q) {
     const int i = tid + C::NT * q;
     if (i * 4 < wcount) reinterpret_cast<f32x4*>(As)[i] = wv[q];
   }
-  xi[0].store(Xs, 0, p.pW, ow1, n1, n2, seg2);
+#pragma unroll
+  for (int ic = 0; ic < C::IC; ++ic) xi[ic].store(Xs, ic, p.pW, ow1, n1, n2, seg2);
   __syncthreads();
 
-  // 4. channel by channel: (after channel 0) wait for the channel's input,
-  // write it to LDS and sync, then run the steps whose taps need no later
-  // channel, the later channels' loads still in flight; wave w computes
-  // pixel blocks [0, PBH) (w < 8) or [PBH, NPB)
+  // 4. all of K: wave w computes pixel blocks [0, PBH) (w < 8) or [PBH, NPB)
   const int m = lane & 15, j = lane >> 4;
   const int ocb = wave % (C::BM / 16), half = wave / (C::BM / 16);
   const int pb0 = half ? C::PBH : 0, nb = half ? C::NPB - C::PBH : C::PBH;
@@ -266,7 +240,10 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   f32x4 acc[C::PBH];
 #pragma unroll
   for (int pb = 0; pb < C::PBH; ++pb) acc[pb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  stem_stages<C, 0>(acc, Aw, Tj, Xs, boff, half, xi, p.pW, ow1, n1, n2, seg2);
+  if (half == 0)
+    stem_mma<C, 0, C::KSTEPS, C::PBH>(acc, Aw, Tj, Xs, boff);
+  else
+    stem_mma<C, 0, C::KSTEPS, C::NPB - C::PBH>(acc, Aw, Tj, Xs, boff);
 
   // 5. + bias, NCHW store: lane (pixel m, group j) holds output channels
   // 4j .. 4j+3 of the wave's 16
