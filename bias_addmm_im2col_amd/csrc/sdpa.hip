@@ -103,12 +103,32 @@ __device__ __forceinline__ void scale_rows(f32x16 (&o)[ND], float f, float* slot
     for (int j = 0; j < 16; ++j) o[db][j] *= r[j / 4][j % 4];
 }
 
+// The mask tile of a key tile, for the shapes with several key groups (a
+// wave's lanes then read 32 different mask rows at a few keys each, which
+// as direct loads touch a cache line per lane): the block's BQ query rows x
+// BKV keys, loaded along the keys (coalesced: MV floats per load, 16 bytes
+// where the rows allow) one tile ahead like k and v, and staged in LDS with
+// row stride BKV + 4 (an odd multiple of 4 floats mod 32), from where each
+// lane reads its four keys per 16-byte read.  The 128-row shape keeps
+// direct loads: its registers are spent on three blocks per CU.
+template <int BQ, int BKV, int NT, int MV>
+struct SdpaMaskTile {
+  static constexpr int MS = BKV + 4;
+  static constexpr int ITEMS = BQ * BKV / MV;
+  static constexpr int NQ = (ITEMS + NT - 1) / NT;  // loads per thread and tile
+  static constexpr int FLOATS = BQ * MS;
+  static_assert(BKV % 32 == 0 && MS % 8 == 4, "mask tile rows");
+};
+
 template <int DP, int QW, int KW, int NB, bool MASK, int MV>
 __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) void sdpa_kernel(SdpaArgs a) {
   using S = SdpaShape<DP, QW, KW, NB>;
-  __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS];
+  using MT = SdpaMaskTile<S::BQ, S::BKV, S::NT, MV>;
+  constexpr bool MSTAGE = MASK && KW > 1;  // mask tile staged through LDS
+  __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS + (MSTAGE ? MT::FLOATS : 0)];
   float* Ks = smem;
   float* Vs = smem + S::BKV * S::KS;
+  float* Ms = smem + S::LDS_FLOATS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave % QW, kg = wave / QW;  // query group, key group
@@ -137,7 +157,10 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
   }
 
   // k/v tile loads: chunk i of thread tid is row idx / CH, column 4*(idx % CH).
+  // Mask tile loads: item i of thread tid is query row idx / (BKV/MV) of the
+  // block, keys MV*(idx % (BKV/MV)) .. +MV-1 of the tile.
   f32x4 kreg[S::NCH], vreg[S::NCH];
+  typename Vec<MV>::T mreg[MSTAGE ? MT::NQ : 1];
   auto fetch = [&](int kv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < S::NCH; ++i) {
@@ -148,6 +171,18 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
       kreg[i] = Vec<4>::load(kr, off);
       vreg[i] = Vec<4>::load(vr, off);
     }
+    if constexpr (MSTAGE) {
+#pragma unroll
+      for (int i = 0; i < MT::NQ; ++i) {
+        const int idx = i * S::NT + tid;
+        const int row = idx / (S::BKV / MV), col = MV * (idx - row * (S::BKV / MV));
+        const int qq = qb * S::BQ + row, kv = kv0 + col;
+        // keys past Skv get -inf later; with MV == 4, Skv % 4 == 0 keeps a
+        // whole group inside the row
+        const bool ok = idx < MT::ITEMS && qq < Sq && kv < Skv;
+        mreg[i] = Vec<MV>::load(mr, ok ? (uint32_t)(qq * Skv + kv) * 4u : kOOB);
+      }
+    }
   };
   auto put = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -156,6 +191,15 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
       const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
       *reinterpret_cast<f32x4*>(Ks + row * S::KS + d) = kreg[i];
       *reinterpret_cast<f32x4*>(Vs + row * S::KS + d) = vreg[i];
+    }
+    if constexpr (MSTAGE) {
+#pragma unroll
+      for (int i = 0; i < MT::NQ; ++i) {
+        const int idx = i * S::NT + tid;
+        if (MT::ITEMS % S::NT != 0 && idx >= MT::ITEMS) continue;
+        const int row = idx / (S::BKV / MV), col = MV * (idx - row * (S::BKV / MV));
+        *reinterpret_cast<typename Vec<MV>::T*>(Ms + row * MT::MS + col) = mreg[i];
+      }
     }
   };
 
@@ -183,7 +227,14 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
     for (int kb = 0; kb < NB; ++kb) blk[kb] = active && kv0 + kb0 + 32 * kb < Skv;
 
     f32x4 mk[NB][4];
-    if constexpr (MASK) {
+    if constexpr (MSTAGE) {
+      const float* mrow = Ms + (32 * qg + c) * MT::MS + kb0 + 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          mk[kb][g] = *reinterpret_cast<const f32x4*>(mrow + 32 * kb + 8 * g);
+    } else if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
