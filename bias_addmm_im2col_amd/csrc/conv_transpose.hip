@@ -29,6 +29,7 @@
 // initialisation kernel writes bias[oc] into the output and each slice adds
 // its partial sums atomically (the summation order then varies run to run).
 #include <stdlib.h>
+#include <string.h>
 
 #include <vector>
 
@@ -210,7 +211,98 @@ struct TWeightLoader {
   __device__ void meta(int) {}
 };
 
+// Phases with a single tap and the input grid as their output grid (kernel
+// equal to the stride, no padding: the 2x2 stride-2 upsampling): B[kk, n]
+// = x[b, g*ICg + kk, t, u] is a plain row-major [K, N] matrix per image, so
+// B tiles load as 16-byte quads of four output pixels (H*W % 4 == 0 keeps a
+// quad inside one image) into the [BK][BN+8] layout, and A[oc, kk] =
+// w[g*ICg + kk, oc, kh0, kw0] needs no table.
 template <class T>
+struct TUnitColLoader {
+  static constexpr bool kHasMeta = false;
+  static constexpr bool kBTransposed = false;
+  static constexpr int QPR = T::BN / 4;                  // quads per tile row
+  static constexpr int NI = T::BK * QPR / T::NT;         // quads per thread
+  static_assert((T::BK * QPR) % T::NT == 0, "tile splits evenly");
+  __amdgpu_buffer_rsrc_t rs;
+  int HW, K;
+  int base[NI], kk[NI], n4[NI];
+  bool nok[NI];
+  f32x4 reg[2][NI];
+
+  __device__ void init(const ConvTArgs& a, const ConvTPhase& P, int n0, int4*, int g) {
+    rs = make_rsrc(a.x, a.x_elems);
+    HW = a.H * a.W;
+    K = P.K;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = (int)threadIdx.x + T::NT * i;
+      kk[i] = idx / QPR;
+      n4[i] = idx - kk[i] * QPR;
+      const int n = n0 + 4 * n4[i];
+      nok[i] = n < P.N;
+      const uint32_t nn = nok[i] ? (uint32_t)n : 0u;
+      const uint32_t b = fdiv(nn, P.div_p);
+      base[i] = ((int)b * a.IC + g * a.ICg) * HW + (int)(nn - b * P.div_p.d);
+    }
+  }
+  __device__ void meta(int) {}
+  template <int S>
+  __device__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int k = k0 + kk[i];
+      reg[S][i] = Vec<4>::load(rs, (nok[i] && k < K) ? (uint32_t)(base[i] + k * HW) * 4u : kOOB);
+    }
+  }
+  template <int S>
+  __device__ void store(float* Bs) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<f32x4*>(&Bs[kk[i] * T::BS + 4 * n4[i]]) = reg[S][i];
+  }
+};
+
+template <class T>
+struct TUnitWeightLoader {
+  static constexpr int NCH = T::BM * T::BK / T::NT;
+  static_assert((T::BM * T::BK) % T::NT == 0 && T::NT % T::BK == 0, "weight tile split");
+  __amdgpu_buffer_rsrc_t rs;
+  int col, r0, rows_left, khw, ockk, tap0, K;
+  float reg[2][NCH];
+
+  __device__ void init(const ConvTArgs& a, const ConvTPhase& P, int m0, int g) {
+    khw = a.KH * a.KW;
+    const int64_t base = ((int64_t)g * a.ICg * a.OCg + m0) * khw;
+    rs = make_rsrc(a.w + base, a.w_elems - base);
+    col = threadIdx.x % T::BK;
+    r0 = threadIdx.x / T::BK;
+    rows_left = a.OCg - m0;
+    ockk = a.OCg * khw;
+    tap0 = P.kh0 * a.KW + P.kw0;
+    K = P.K;
+  }
+  template <int S>
+  __device__ void load(int k0) {
+    const int k = k0 + col;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int r = r0 + i * (T::NT / T::BK);
+      const bool ok = k < K && r < rows_left;
+      reg[S][i] = Vec<1>::load(rs, ok ? (uint32_t)(k * ockk + tap0 + r * khw) * 4u : kOOB);
+    }
+  }
+  template <int S>
+  __device__ void store(float* As) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) As[(r0 + i * (T::NT / T::BK)) * T::AS + col] = reg[S][i];
+  }
+  __device__ void meta(int) {}
+};
+
+// UNIT: every phase has one tap and the input grid as its output grid
+// (TUnitColLoader); else the table-driven gathers.
+template <class T, bool UNIT>
 __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
   __shared__ __attribute__((aligned(16))) float smem[T::SMEM_FLOATS];
   const ConvTPhase& P = a.ph[blockIdx.y];
@@ -227,13 +319,21 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int lane = threadIdx.x & 63;
   const WaveSlot ws = wave_slot<T>();
-  int4* table = reinterpret_cast<int4*>(smem + 2 * T::STAGE);
-  TWeightLoader<T> al;
-  al.init(a, m0, table, g);
-  TImColLoader<T> bl;
-  bl.init(a, P, n0, table, g);
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
+  if constexpr (UNIT) {
+    TUnitWeightLoader<T> al;
+    al.init(a, P, m0, g);
+    TUnitColLoader<T> bl;
+    bl.init(a, P, n0, nullptr, g);
+    mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
+  } else {
+    int4* table = reinterpret_cast<int4*>(smem + 2 * T::STAGE);
+    TWeightLoader<T> al;
+    al.init(a, m0, table, g);
+    TImColLoader<T> bl;
+    bl.init(a, P, n0, table, g);
+    mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
+  }
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // + bias[oc]; column n = (b, t, u) goes to out[b, oc, rh + sH*t, rw + sW*u].
@@ -330,23 +430,27 @@ AxisTaps axis_taps(int r, int s, int p, int d, int KK) {
 }
 
 template <class T>
-hipError_t launch_phases(const ConvTArgs& a, int nph, int groups, hipStream_t s) {
+hipError_t launch_phases(const ConvTArgs& a, int nph, int groups, bool unit, hipStream_t s) {
   const dim3 grid(a.slice_row * a.splits, nph, groups);
-  hipLaunchKernelGGL((conv_transpose_kernel<T>), grid, dim3(T::NT), 0, s, a);
+  if (unit)
+    hipLaunchKernelGGL((conv_transpose_kernel<T, true>), grid, dim3(T::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_transpose_kernel<T, false>), grid, dim3(T::NT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int groups, hipStream_t s) {
+hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int groups, bool unit,
+                      hipStream_t s) {
   switch (cfg) {
-    case TILE_128x64: return launch_phases<T128x64>(a, nph, groups, s);
-    case TILE_64x128: return launch_phases<T64x128>(a, nph, groups, s);
-    case TILE_64x64: return launch_phases<T64x64>(a, nph, groups, s);
-    case TILE_128x128_K2: return launch_phases<T128x128K2>(a, nph, groups, s);
-    case TILE_128x64_K2: return launch_phases<T128x64K2>(a, nph, groups, s);
-    case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, groups, s);
-    case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, groups, s);
-    case TILE_32x128: return launch_phases<T32x128>(a, nph, groups, s);
-    default: return launch_phases<T128x128>(a, nph, groups, s);
+    case TILE_128x64: return launch_phases<T128x64>(a, nph, groups, unit, s);
+    case TILE_64x128: return launch_phases<T64x128>(a, nph, groups, unit, s);
+    case TILE_64x64: return launch_phases<T64x64>(a, nph, groups, unit, s);
+    case TILE_128x128_K2: return launch_phases<T128x128K2>(a, nph, groups, unit, s);
+    case TILE_128x64_K2: return launch_phases<T128x64K2>(a, nph, groups, unit, s);
+    case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, groups, unit, s);
+    case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, groups, unit, s);
+    case TILE_32x128: return launch_phases<T32x128>(a, nph, groups, unit, s);
+    default: return launch_phases<T128x128>(a, nph, groups, unit, s);
   }
 }
 
@@ -409,6 +513,11 @@ hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
       all.push_back(P);
     }
   const int nall = (int)all.size();
+  // Single-tap phases over the input grid: the 16-byte B loads
+  bool unit = (q.H * q.W) % 4 == 0 && ((uintptr_t)q.x & 15) == 0 && nall > 0;
+  for (const ConvTPhase& P : all)
+    unit = unit && P.K == a.ICg && P.c0h == 0 && P.c0w == 0 && P.Th == q.H && P.Tw == q.W;
+  if (getenv("BAIM_CONVT_UNIT") && strcmp(getenv("BAIM_CONVT_UNIT"), "off") == 0) unit = false;
   // Tile choice for all phases side by side.  Both operands are 4-byte
   // gathers here, so the 8-wave 64x128 tile (a 64-row weight tile against
   // 128 output pixels) is preferred while it still gives half the CUs a
@@ -476,7 +585,7 @@ hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
       a.ph[i] = P;
     }
     a.slice_row = a.tiles_m * max_tiles_n;
-    err = launch_cfg(plan.cfg, a, nph, q.groups, stream);
+    err = launch_cfg(plan.cfg, a, nph, q.groups, unit, stream);
   }
   return err;
 }

@@ -152,3 +152,36 @@ def test_workload_convt(name):
     got = out.reshape(-1)[torch.from_numpy(idx).cuda()].cpu().numpy()
     res = oracle.conv_transpose2d_at(x, w, b, c.stride, c.padding, c.dilation, c.output_padding, idx)
     check_close(got, res, c.IC * c.KH * c.KW, 1.0, name)
+
+
+UNIT_SHAPES = [
+    # B, IC, H, W, OC, k, stride, groups: kernel = stride, no padding, H*W % 4 == 0
+    (2, 40, 8, 6, 70, 2, 2, 1),     # a partial k-tile (40 = 32 + 8), ragged output channels
+    (1, 64, 12, 16, 33, 3, 3, 1),   # 3x3 / stride 3: nine single-tap phases
+    (2, 32, 8, 8, 48, 2, 2, 4),     # four groups of 8 -> 12 channels
+    (3, 24, 4, 5, 20, 2, 2, 1),     # images of 20 pixels: quads stay inside one image
+]
+
+
+@pytest.mark.parametrize("spec", ["", "0", "2", "3", "7", "8", "2,2", "3,3"])
+@pytest.mark.parametrize("B,IC,H,W,OC,k,stride,groups", UNIT_SHAPES)
+def test_convt_single_tap_phases(B, IC, H, W, OC, k, stride, groups, spec, monkeypatch):
+    """Kernel equal to the stride and no padding: every phase is one tap over
+    the input grid, and B loads as 16-byte quads of output pixels.  Checked
+    against the oracle, and bit for bit on integers against the table-driven
+    gathers (BAIM_CONVT_UNIT=off)."""
+    if spec:
+        monkeypatch.setenv("BAIM_TILE", spec)
+    say(f"BAIM_TILE={spec!r} conv_transpose2d_f32 single-tap x=[{B},{IC},{H},{W}] OC={OC} "
+        f"k={k} s={stride} g={groups}")
+    x, w, b = gen((B, IC, H, W), 31), gen((IC, OC // groups, k, k), 32), gen((OC,), 33)
+    check_close(run(x, w, b, stride, 0, 0, groups),
+                oracle.conv_transpose2d(x, w, b, stride, 0, 1, 0, groups), IC // groups * k * k,
+                1.0, f"convT single-tap {spec}")
+    xi, wi, bi = (gen((B, IC, H, W), 34, "I"), gen((IC, OC // groups, k, k), 35, "I"),
+                  gen((OC,), 36, "I"))
+    fast = run(xi, wi, bi, stride, 0, 0, groups)
+    check_bitwise(fast, oracle.conv_transpose2d(xi, wi, bi, stride, 0, 1, 0, groups),
+                  f"convT single-tap integer {spec}")
+    monkeypatch.setenv("BAIM_CONVT_UNIT", "off")
+    assert (run(xi, wi, bi, stride, 0, 0, groups) == fast).all()
