@@ -454,9 +454,178 @@ hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int groups, bool uni
   }
 }
 
+// ------------------------------------------------ kernel = stride, no pad
+//
+// When the kernel equals the stride and there is no padding (the 2x2
+// stride-2 upsampling), every output pixel takes exactly one tap, and all
+// phases read the same input pixel: out[b, oc, sH*t + kh, sW*u + kw] =
+// bias[oc] + sum_ic x[b, ic, t, u] * w[ic, oc, kh, kw].  So the phases fuse
+// into one GEMM per group, M = OCg*KH*KW rows m = (oc, kh, kw), N = B*H*W,
+// K = ICg: A[m, ic] = w[ic, m] (the weight viewed [ICg, M], row-major: A
+// transposed), B[ic, n] = x[b, ic, t, u] (row-major [K, H*W] per image),
+// each B tile loaded once for all phases.  A's tiles load as 16-byte quads
+// along m and go to LDS transposed, lanes along k (conflict-free 4-byte
+// stores); a B tile lies inside one image (H*W % BN == 0).  With KW == 2 a
+// lane holds both kw of an output pair and stores them as 8 bytes.
+
+// A tile [BM][BK+4] from a row-major [K][M] matrix (A transposed).
+template <class T>
+struct TColALoader {
+  static constexpr int CPR = T::BM / 4;  // quads per k row
+  static constexpr int NCH = T::BK * CPR / T::NT;
+  static_assert((T::BK * CPR) % T::NT == 0 && T::NT % T::BK == 0, "A tile split");
+  const float* base;  // column m0 of row 0
+  int M, K, cols_left;
+  f32x4 reg[2][NCH];
+
+  __device__ void init(const float* At, int m0, int M_, int K_) {
+    base = At + m0;
+    M = M_;
+    K = K_;
+    cols_left = M_ - m0;
+  }
+  // item q: k row q % BK (consecutive lanes, consecutive rows), quad q / BK
+  template <int S>
+  __device__ void load(int k0) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(base + (size_t)k0 * M, (int64_t)(K - k0) * M - (M - cols_left));
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q % T::BK, c = (q / T::BK) * 4;
+      const bool ok = k0 + r < K && c < cols_left;  // M % 4 == 0: whole quads
+      reg[S][i] = Vec<4>::load(rs, ok ? (uint32_t)(r * M + c) * 4u : kOOB);
+    }
+  }
+  template <int S>
+  __device__ void store(float* As) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + T::NT * i;
+      const int r = q % T::BK, c = (q / T::BK) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[(c + e) * T::AS + r] = reg[S][i][e];
+    }
+  }
+  __device__ void meta(int) {}
+};
+
+struct ConvTFusedArgs {
+  float* out;
+  const float* x;
+  const float* w;
+  const float* bias;
+  int IC, ICg, OC, OCg, KH, KW, W, OH, OW;
+  int M, HW, tiles_m, tiles_n;
+  FastDiv div_khw, div_kw, div_w;
+};
+
+template <class T>
+__global__ __launch_bounds__(T::NT) void convt_fused_kernel(ConvTFusedArgs a) {
+  __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+  const int g = blockIdx.z;
+  const int lid = xcd_linear(blockIdx.x, gridDim.x);
+  int tm, tn;
+  grouped_tile(lid, a.tiles_m, a.tiles_n, 8, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  const int b = n0 / a.HW, p0 = n0 - b * a.HW;  // the tile lies in image b
+  const int lane = threadIdx.x & 63;
+  const WaveSlot ws = wave_slot<T>();
+  TColALoader<T> al;
+  al.init(a.w + (size_t)g * a.ICg * a.M, m0, a.M, a.ICg);
+  ColTileLoader<T, 4> bl;
+  bl.init(a.x + ((size_t)b * a.IC + (size_t)g * a.ICg) * a.HW, p0, a.HW, a.ICg);
+  Accum<T> acc;
+  mainloop<T>(acc, al, bl, 0, (a.ICg + T::BK - 1) / T::BK, smem, ws, lane);
+  if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
+
+  // row m = (oc, kh, kw), column p = (t, u) of image b
+  const int c = lane & 31;
+  const size_t plane = (size_t)a.OH * a.OW;
+  float* ob = a.out + ((size_t)b * a.OC + (size_t)g * a.OCg) * plane;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const uint32_t pix = (uint32_t)(p0 + ws.wn0 + 32 * j + c);
+    const uint32_t t = fdiv(pix, a.div_w), u = pix - t * a.div_w.d;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      if (a.KW == 2) {
+        // rows m (kw = 0) and m + 1 (kw = 1) sit in registers r and r + 1
+        // of the lane: one 8-byte store of two neighbouring outputs
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          if (m >= a.M) continue;
+          const uint32_t oc = fdiv((uint32_t)m, a.div_khw), kh = ((uint32_t)m - oc * a.div_khw.d) >> 1;
+          const float bv = a.bias ? a.bias[g * a.OCg + oc] : 0.0f;
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<f32x2*>(&ob[oc * plane + (size_t)(a.KH * t + kh) * a.OW + 2 * u]) =
+              f32x2{acc.c[i][j][r] + bv, acc.c[i][j][r + 1] + bv};
+        }
+        continue;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+        if (m >= a.M) continue;
+        const uint32_t oc = fdiv((uint32_t)m, a.div_khw), tap = (uint32_t)m - oc * a.div_khw.d;
+        const uint32_t kh = fdiv(tap, a.div_kw), kw = tap - kh * a.div_kw.d;
+        ob[oc * plane + (size_t)(a.KH * t + kh) * a.OW + a.KW * u + kw] =
+            acc.c[i][j][r] + (a.bias ? a.bias[g * a.OCg + oc] : 0.0f);
+      }
+    }
+  }
+}
+
+// Whether q takes the fused path, and with which tile (64 x 128 below 128
+// rows, else 128 x 128; both 128 pixels wide).
+int convt_fused_cfg(const ConvTProblem& q) {
+  const int ICg = q.IC / q.groups, OCg = q.OC / q.groups;
+  const int64_t M = (int64_t)OCg * q.KH * q.KW;
+  if (q.KH != q.sH || q.KW != q.sW || q.pH != 0 || q.pW != 0) return -1;
+  if (q.OH != q.sH * q.H || q.OW != q.sW * q.W) return -1;  // no output padding
+  if ((q.H * q.W) % 128 != 0 || M % 4 != 0 || ICg < 1) return -1;
+  if (((uintptr_t)q.x & 15) != 0 || ((uintptr_t)q.w & 15) != 0) return -1;
+  if (((uintptr_t)q.out & 7) != 0) return -1;  // the 8-byte output stores
+  if (q.groups > 65535) return -1;
+  return M >= 128 ? TILE_128x128 : TILE_64x128;
+}
+
+template <class T>
+hipError_t launch_fused(const ConvTProblem& q, hipStream_t s) {
+  ConvTFusedArgs a;
+  a.out = q.out;
+  a.x = q.x;
+  a.w = q.w;
+  a.bias = q.bias;
+  a.IC = q.IC;
+  a.ICg = q.IC / q.groups;
+  a.OC = q.OC;
+  a.OCg = q.OC / q.groups;
+  a.KH = q.KH;
+  a.KW = q.KW;
+  a.W = q.W;
+  a.OH = q.OH;
+  a.OW = q.OW;
+  a.M = a.OCg * q.KH * q.KW;
+  a.HW = q.H * q.W;
+  a.tiles_m = (a.M + T::BM - 1) / T::BM;
+  a.tiles_n = q.B * (a.HW / T::BN);
+  a.div_khw = make_fastdiv((uint32_t)(q.KH * q.KW));
+  a.div_kw = make_fastdiv((uint32_t)q.KW);
+  a.div_w = make_fastdiv((uint32_t)q.W);
+  const dim3 grid(a.tiles_m * a.tiles_n, 1, q.groups);
+  hipLaunchKernelGGL((convt_fused_kernel<T>), grid, dim3(T::NT), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
+  const char* fspec = getenv("BAIM_CONVT_UNIT");
+  const int fcfg = fspec && strcmp(fspec, "off") == 0 ? -1 : convt_fused_cfg(q);
+  if (fcfg == TILE_128x128) return launch_fused<T128x128>(q, stream);
+  if (fcfg == TILE_64x128) return launch_fused<T64x128>(q, stream);
   ConvTArgs a;
   a.out = q.out;
   a.x = q.x;

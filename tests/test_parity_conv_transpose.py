@@ -185,3 +185,58 @@ def test_convt_single_tap_phases(B, IC, H, W, OC, k, stride, groups, spec, monke
                   f"convT single-tap integer {spec}")
     monkeypatch.setenv("BAIM_CONVT_UNIT", "off")
     assert (run(xi, wi, bi, stride, 0, 0, groups) == fast).all()
+
+
+FUSED_SHAPES = [
+    # B, IC, H, W, OC, (KH, KW), groups: kernel = stride, no padding, H*W % 128 == 0
+    (2, 40, 16, 8, 70, (2, 2), 1),   # M = 280 rows in three 128-row tiles, K = 40
+    (1, 96, 8, 32, 48, (2, 2), 2),   # two groups: M = 96 (the 64-row tile), K = 48
+    (2, 64, 16, 16, 32, (3, 3), 1),  # 3x3 / stride 3: M = 288
+    (1, 24, 32, 8, 20, (2, 4), 1),   # kernel 2x4 / stride (2, 4): the (kh, kw) decode
+    (4, 256, 16, 16, 64, (2, 2), 1), # the upsampling's channels at a smaller image
+]
+
+
+@pytest.mark.parametrize("B,IC,H,W,OC,k,groups", FUSED_SHAPES)
+def test_convt_fused_phases(B, IC, H, W, OC, k, groups, monkeypatch):
+    """Kernel equal to the stride, no padding, whole 128-pixel tiles per
+    image: all phases in one GEMM (rows (oc, kh, kw), the weight read as its
+    transpose).  Checked against the oracle, and bit for bit on integers
+    against the per-phase path (BAIM_CONVT_UNIT=off)."""
+    KH, KW = k
+    say(f"conv_transpose2d_f32 fused x=[{B},{IC},{H},{W}] OC={OC} k={k} g={groups}")
+    x, w, b = gen((B, IC, H, W), 41), gen((IC, OC // groups, KH, KW), 42), gen((OC,), 43)
+    check_close(run(x, w, b, k, 0, 0, groups),
+                oracle.conv_transpose2d(x, w, b, k, 0, 1, 0, groups), IC // groups * KH * KW,
+                1.0, "convT fused")
+    xi, wi, bi = (gen((B, IC, H, W), 44, "I"), gen((IC, OC // groups, KH, KW), 45, "I"),
+                  gen((OC,), 46, "I"))
+    fused = run(xi, wi, bi, k, 0, 0, groups)
+    check_bitwise(fused, oracle.conv_transpose2d(xi, wi, bi, k, 0, 1, 0, groups),
+                  "convT fused integer")
+    monkeypatch.setenv("BAIM_CONVT_UNIT", "off")
+    assert (run(xi, wi, bi, k, 0, 0, groups) == fused).all()
+
+
+def test_convt_fused_output_padding_falls_back():
+    """Output padding adds rows that no tap reaches (bias only): such convs
+    keep the per-phase path, and still match the oracle."""
+    x, w, b = gen((1, 16, 8, 16), 47), gen((16, 12, 2, 2), 48), gen((12,), 49)
+    check_close(run(x, w, b, 2, 0, 1), oracle.conv_transpose2d(x, w, b, 2, 0, 1, 1), 16 * 4, 1.0,
+                "convT output padding")
+
+
+def test_convt_fused_with_an_output_off_8_byte_alignment():
+    """An output that starts 4 bytes past an 8-byte boundary cannot take the
+    fused path's 8-byte stores: the per-phase path runs, with the same
+    result."""
+    import bias_addmm_im2col_amd as baim
+    x, w, b = gen((2, 32, 16, 8), 50, "I"), gen((32, 16, 2, 2), 51, "I"), gen((16,), 52, "I")
+    ref = oracle.conv_transpose2d(x, w, b, 2, 0, 1, 0)
+    buf = torch.empty(2 * 16 * 32 * 16 + 1, dtype=torch.float32, device="cuda")
+    out = buf[1:].view(2, 16, 32, 16)
+    assert out.data_ptr() % 8 == 4
+    baim.conv_transpose2d_f32(out, dev(x), dev(w), dev(b), 2, 0, 0)
+    torch.cuda.synchronize()
+    check_bitwise(out.cpu().numpy(), ref, "convT fused, offset output")
+    assert (out.cpu().numpy() == run(x, w, b, 2, 0, 0)).all()
