@@ -300,11 +300,11 @@ baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W, int64_
   const baim::WinPlan wp = baim::plan_conv_window(baim::win_shape(q), true, getenv("BAIM_CONV_WIN"));
   if (wp.geom >= 0) {
     *kernel = 1;
-    *bm = baim::kWinBM;
-    *bn = baim::kWinBN;
+    *bm = baim::kWinBM[wp.geom];
+    *bn = baim::kWinBN[wp.geom];
     *bk = baim::kWinCI * q.KH * q.KW;
     *waves = baim::kWinWaves;
-    *kgroups = baim::kWinKGroups;
+    *kgroups = baim::kWinKGroups[wp.geom];
     *splits = wp.mode == baim::MODE_SLICES ? wp.splits : 1;
     *stream_blocks = wp.mode == baim::MODE_STREAM ? wp.workers : 0;
     return BAIM_OK;

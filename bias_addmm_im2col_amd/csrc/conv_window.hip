@@ -16,6 +16,15 @@
 // A 3x3 stride-1 k-tile of 16 channels and 128 pixels then costs 21 window
 // loads per block instead of 288 gathers.
 //
+// At stride 2 each input element serves about 2.25 outputs instead of 9, so
+// the window saves fewer loads, but it still replaces one 4-byte gather per
+// im2col element by 16-byte row copies: per k-tile of 16 channels and 64
+// pixels a block issues about 4 loads per thread (weights and window)
+// against 10 for the gather kernel's 128-deep k-tile.  Stride-2 rows need
+// not be a multiple of 4 floats (57 x 57 feature maps); their whole quads
+// load 16 bytes at a time from the 4-byte-aligned row start and the last
+// W % 4 columns 4 bytes at a time.
+//
 // Block tile: BM output channels x BN consecutive output pixels of one
 // image (a run of (oh, ow) in row-major order; 128 pixels touch at most four
 // output rows when OW >= 43).  16 waves: WM x WN waves of 32 x 32 outputs,
@@ -45,7 +54,8 @@
 namespace baim {
 
 template <int KH_, int KW_, int SH_, int SW_, int DH_, int DW_, int WR_, int BM_ = 128,
-          int BN_ = 64, int CI_ = 8, int WM_ = 4, int WN_ = 2, int WK_ = 2>
+          int BN_ = 64, int CI_ = 8, int WM_ = 4, int WN_ = 2, int WK_ = 2, bool TAIL_ = false,
+          int MAXQ_ = 15>
 struct WinCfg {
   static constexpr int KH = KH_, KW = KW_, SH = SH_, SW = SW_, DH = DH_, DW = DW_;
   static constexpr int TAPS = KH * KW;
@@ -78,8 +88,14 @@ struct WinCfg {
   static constexpr int SMEM_FLOATS = 2 * STAGE;
   static constexpr int A_ITEMS = BM * BK / 4;  // float4 loads of one A tile
   static constexpr int A_NQ = (A_ITEMS + NT - 1) / NT;
-  static constexpr int B_ITEMS = CI * WR * ((RS - CL) / 4);  // upper bound (W + CL <= RS)
+  // Input rows: W / 4 <= MAXQ whole quads each; with TAIL, also W % 4 != 0,
+  // the last W % 4 columns then taking one 4-byte load per thread.
+  static constexpr bool TAIL = TAIL_;
+  static constexpr int MAXQ = MAXQ_;
+  static constexpr int B_ITEMS = CI * WR * MAXQ;  // upper bound
   static constexpr int B_NQ = (B_ITEMS + NT - 1) / NT;
+  static_assert(CL + 4 * MAXQ <= RS, "whole quads fit a window row");
+  static_assert(!TAIL || CI * WR * 3 <= NT, "one tail column per thread");
   static_assert(CI % (2 * WK) == 0 && HALF % 2 == 0 && BKW == 2 * HALF, "lane-half channels");
   static_assert(AS % 8 == 4, "A rows must start an odd multiple of 4 floats apart (mod 32)");
   static_assert((WK - 1) * BM * BN <= SMEM_FLOATS, "k-group reduction must fit in LDS");
@@ -93,13 +109,13 @@ struct WinArgs {
   const float* bias;
   int IC, H, W, OC, pH, pW, OH, OW;
   int P;       // OH*OW
-  int tpi;     // 64-pixel tiles per image
+  int tpi;     // BN-pixel tiles per image
   int K;       // IC*TAPS
   int x_elems;
   Sched sched;
 };
 
-// One 128 x BK tile of the weight [OC, IC*TAPS] per k-tile: float4 loads
+// One BM x BK tile of the weight [OC, IC*TAPS] per k-tile: float4 loads
 // along K, written to LDS as two 8-byte halves into their segments.
 template <class C>
 struct WinALoader {
@@ -146,23 +162,44 @@ struct WinALoader {
   }
 };
 
-// The input window of one k-tile: channels 8t..8t+7 of image b, input rows
-// ih_first .. ih_first + WR - 1, all W columns, as float4 loads (W % 4 == 0,
-// 16-byte aligned input).  Which (channel, row, column quad) a thread copies
-// is fixed for the whole piece; rows outside the image and channels past IC
-// load as 0 (out-of-range offset).
+// The input window of one k-tile: channels CI*t .. CI*t + CI-1 of image b,
+// input rows ih_first .. ih_first + WR - 1, all W columns.  Columns
+// [0, 4*(W/4)) load as float4s; a row starts 16 bytes aligned when W % 4 == 0
+// and the input is, and 4 bytes aligned otherwise, which buffer loads
+// accept.  With TAIL the last W % 4 columns load 4 bytes at a time.  Which
+// (channel, row, column quad) a thread copies is fixed for the whole piece;
+// rows outside the image and channels past IC load as 0 (out-of-range
+// offset).
 template <class C>
 struct WinBLoader {
-  int goff[C::B_NQ];  // float offset of the item in channel 8t + icl at t = 0
+  int goff[C::B_NQ];  // float offset of the item in channel CI*t + icl at t = 0
   int ldst[C::B_NQ];  // LDS float offset in the window (-1: no item)
   int icl[C::B_NQ];
   bool rok[C::B_NQ];
+  int tgoff, tldst, ticl;  // the thread's tail column (TAIL; tldst -1: none)
+  bool trok;
   const WinArgs* a;
   f32x4 reg[2][C::B_NQ];
+  float treg[2];
 
   __device__ void init(const WinArgs& args, int b, int ih_first) {
     a = &args;
     const int W4 = args.W >> 2;
+    tgoff = ticl = 0;
+    tldst = -1;
+    trok = false;
+    if constexpr (C::TAIL) {
+      const int tw = args.W & 3, i = threadIdx.x;
+      if (i < C::CI * C::WR * tw) {
+        const int ch = i / (C::WR * tw), rem = i - ch * (C::WR * tw);
+        const int wr = rem / tw, col = 4 * W4 + rem - wr * tw;
+        const int ih = ih_first + wr;
+        ticl = ch;
+        trok = ih >= 0 && ih < args.H;
+        tgoff = ((b * args.IC + ch) * args.H + ih) * args.W + col;
+        tldst = ch * C::PS + wr * C::RS + C::CL + col;
+      }
+    }
     const int items = C::CI * C::WR * W4;
 #pragma unroll
     for (int q = 0; q < C::B_NQ; ++q) {
@@ -192,12 +229,18 @@ struct WinBLoader {
       const bool ok = rok[q] && ic0 + icl[q] < a->IC;
       reg[S][q] = Vec<4>::load(rs, ok ? (uint32_t)(goff[q] + step) * 4u : kOOB);
     }
+    if constexpr (C::TAIL) {
+      const bool ok = trok && ic0 + ticl < a->IC;
+      treg[S] = Vec<1>::load(rs, ok ? (uint32_t)(tgoff + step) * 4u : kOOB);
+    }
   }
   template <int S>
   __device__ void store(float* Bs) const {
 #pragma unroll
     for (int q = 0; q < C::B_NQ; ++q)
       if (ldst[q] >= 0) *reinterpret_cast<f32x4*>(&Bs[ldst[q]]) = reg[S][q];
+    if constexpr (C::TAIL)
+      if (tldst >= 0) Bs[tldst] = treg[S];
   }
 };
 
@@ -374,15 +417,18 @@ __global__ __launch_bounds__(C::NT) void conv_window_kernel(WinArgs p) {
 // Compiled geometries (the host plan's table, conv_window_plan.hpp).
 typedef WinCfg<3, 3, 1, 1, 1, 1, 6, 64, 128, 16, 2, 4, 2> Win3x3S1D1;
 typedef WinCfg<3, 3, 1, 1, 2, 2, 8, 64, 128, 16, 2, 4, 2> Win3x3S1D2;
+typedef WinCfg<3, 3, 2, 2, 1, 1, 9, 64, 64, 16, 2, 2, 4, true, 14> Win3x3S2D1;
 
 template <class C>
 constexpr bool same_geom(int g) {
   return C::KH == kWinKH[g] && C::KW == kWinKW[g] && C::SH == kWinSH[g] && C::SW == kWinSW[g] &&
-         C::DH == kWinDH[g] && C::DW == kWinDW[g] && C::WR == kWinWR[g] && C::BM == kWinBM &&
-         C::BN == kWinBN && C::CI == kWinCI && C::RS == kWinRS && C::CL == kWinCL &&
-         C::NT == 64 * kWinWaves && C::WK == kWinKGroups;
+         C::DH == kWinDH[g] && C::DW == kWinDW[g] && C::WR == kWinWR[g] && C::BM == kWinBM[g] &&
+         C::BN == kWinBN[g] && C::CI == kWinCI && C::RS == kWinRS && C::CL == kWinCL &&
+         C::NT == 64 * kWinWaves && C::WK == kWinKGroups[g] && C::TAIL == kWinTail[g] &&
+         C::MAXQ == kWinMaxQ[g];
 }
-static_assert(same_geom<Win3x3S1D1>(WIN_3x3_S1_D1) && same_geom<Win3x3S1D2>(WIN_3x3_S1_D2),
+static_assert(same_geom<Win3x3S1D1>(WIN_3x3_S1_D1) && same_geom<Win3x3S1D2>(WIN_3x3_S1_D2) &&
+                  same_geom<Win3x3S2D1>(WIN_3x3_S2_D1),
               "window geometry table out of sync with the compiled kernels");
 
 template <class C, int MODE>
@@ -391,7 +437,7 @@ static hipError_t win_launch(const WinArgs& a, int nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class C>
+template <class C, bool STREAM>
 static hipError_t win_run(const ConvProblem& q, const WinPlan& pl, hipStream_t stream) {
   WinArgs a;
   a.out = q.out;
@@ -420,7 +466,8 @@ static hipError_t win_run(const ConvProblem& q, const WinPlan& pl, hipStream_t s
   const int nblocks = (int)win_plan_blocks(pl);
   switch (pl.mode) {
     case MODE_STREAM:
-      return win_launch<C, MODE_STREAM>(a, nblocks, stream);
+      if constexpr (STREAM) return win_launch<C, MODE_STREAM>(a, nblocks, stream);
+      return hipErrorInvalidValue;
     case MODE_SLICES:
       return win_launch<C, MODE_SLICES>(a, nblocks, stream);
     default:
@@ -433,9 +480,11 @@ hipError_t launch_conv2d_window(const ConvProblem& q, const WinPlan& pl, hipStre
   if (pl.mode == MODE_SLICES && pl.splits != 2) return hipErrorInvalidValue;
   switch (pl.geom) {
     case WIN_3x3_S1_D1:
-      return win_run<Win3x3S1D1>(q, pl, stream);
+      return win_run<Win3x3S1D1, kWinStream[WIN_3x3_S1_D1]>(q, pl, stream);
     case WIN_3x3_S1_D2:
-      return win_run<Win3x3S1D2>(q, pl, stream);
+      return win_run<Win3x3S1D2, kWinStream[WIN_3x3_S1_D2]>(q, pl, stream);
+    case WIN_3x3_S2_D1:
+      return win_run<Win3x3S2D1, kWinStream[WIN_3x3_S2_D1]>(q, pl, stream);
     default:
       return hipErrorInvalidValue;
   }

@@ -9,20 +9,37 @@
 namespace baim {
 
 // Compiled window geometries: kernel KH x KW, stride, dilation, and WR, the
-// window rows held per input channel (enough for the four output rows a
-// run of kWinBN pixels touches at OW >= 43).
-enum WinGeom { WIN_3x3_S1_D1 = 0, WIN_3x3_S1_D2 = 1, WIN_NGEOM = 2 };
-constexpr int kWinKH[WIN_NGEOM] = {3, 3};
-constexpr int kWinKW[WIN_NGEOM] = {3, 3};
-constexpr int kWinSH[WIN_NGEOM] = {1, 1};
-constexpr int kWinSW[WIN_NGEOM] = {1, 1};
-constexpr int kWinDH[WIN_NGEOM] = {1, 2};
-constexpr int kWinDW[WIN_NGEOM] = {1, 2};
-constexpr int kWinWR[WIN_NGEOM] = {6, 8};
-// Block tile (output channels x output pixels of one image), input
-// channels per k-tile, LDS window row stride and the column of iw = 0.
-constexpr int kWinBM = 64, kWinBN = 128, kWinCI = 16, kWinRS = 64, kWinCL = 4;
-constexpr int kWinWaves = 16, kWinKGroups = 2;
+// window rows held per input channel (enough for the output rows a run of
+// the geometry's kWinBN pixels touches: four at stride 1 with OW >= 43, four
+// at stride 2 with 64 pixels and OW >= 21).
+enum WinGeom { WIN_3x3_S1_D1 = 0, WIN_3x3_S1_D2 = 1, WIN_3x3_S2_D1 = 2, WIN_NGEOM = 3 };
+constexpr int kWinKH[WIN_NGEOM] = {3, 3, 3};
+constexpr int kWinKW[WIN_NGEOM] = {3, 3, 3};
+constexpr int kWinSH[WIN_NGEOM] = {1, 1, 2};
+constexpr int kWinSW[WIN_NGEOM] = {1, 1, 2};
+constexpr int kWinDH[WIN_NGEOM] = {1, 2, 1};
+constexpr int kWinDW[WIN_NGEOM] = {1, 2, 1};
+constexpr int kWinWR[WIN_NGEOM] = {6, 8, 9};
+// Block tile per geometry (output channels x output pixels of one image) and
+// its wave groups splitting each k-tile.  The stride-2 conv has a quarter of
+// the pixels of a stride-1 conv of the same input, so it takes half the tile
+// width to keep about one tile per CU.
+constexpr int kWinBM[WIN_NGEOM] = {64, 64, 64};
+constexpr int kWinBN[WIN_NGEOM] = {128, 128, 64};
+constexpr int kWinKGroups[WIN_NGEOM] = {2, 2, 4};
+// Input rows: the stride-1 instances copy rows of W % 4 == 0 floats as
+// 16-byte quads; the stride-2 instance also takes any other W, copying the
+// W / 4 whole quads (at most kWinMaxQ) 16 bytes at a time from wherever the
+// row starts and the last W % 4 columns 4 bytes at a time.
+constexpr bool kWinTail[WIN_NGEOM] = {false, false, true};
+constexpr int kWinMaxQ[WIN_NGEOM] = {15, 15, 14};
+// Whether the geometry has a streamed (two-piece) kernel: the stride-2
+// instance's would not fit its registers, so its tiles always run one per
+// block (or in two K slices when forced).
+constexpr bool kWinStream[WIN_NGEOM] = {true, true, false};
+// Input channels per k-tile, LDS window row stride, the column of iw = 0.
+constexpr int kWinCI = 16, kWinRS = 64, kWinCL = 4;
+constexpr int kWinWaves = 16;
 
 // The stem kernel (conv_stem.hip): IC = 3, 7 x 7 kernel, stride 4,
 // dilation 1, a block of 128 output channels x 144 output pixels in one
@@ -38,7 +55,7 @@ struct WinPlan {
   int geom;  // WinGeom, or -1 when the window kernel does not apply
   int mode;  // PlanMode (tile_select.hpp)
   int workers, splits, kt_per_split;
-  int tiles_m, tiles_n, tpi, nkt;  // tpi: kWinBN-pixel tiles per image
+  int tiles_m, tiles_n, tpi, nkt;  // tpi: kWinBN[geom]-pixel tiles per image
 };
 
 // Plan for `s`; `aligned` says input and weight start 16-byte aligned.

@@ -42,7 +42,7 @@ def test_mid_stage_convs_take_the_window_kernel():
 
 
 def test_other_convs_keep_their_kernels():
-    assert plan(4, 256, 57, 57, 256, s=2)["kernel"] == 0          # stride 2 (not compiled)
+    assert plan(4, 256, 57, 57, 256, s=2, d=2, p=2)["kernel"] == 0  # stride 2 dilation 2
     assert plan(1, 3, 768, 768, 128, 7, 7, 4, 3)["kernel"] == 3     # the 7x7 stem: its own kernel
     assert plan(2, 16, 40, 42, 64)["kernel"] == 0                   # OW = 42: runs touch 5 rows
     assert plan(2, 16, 40, 44, 64)["kernel"] == 1                   # OW = 44: at most 4
@@ -115,3 +115,24 @@ def test_invalid_sizes_are_rejected_like_the_op():
     assert st == 2
     st, _ = _capi.conv2d_plan(1, 6, 5, 5, 8, 3, 3, 1, 1, 0, 0, 1, 1, 4)   # groups do not divide
     assert st == 2
+
+
+def test_stride2_convs_take_the_window_kernel(monkeypatch):
+    # [4,256,57,57] s2: OW = 29, runs of 64 pixels touch 4 output rows = 9
+    # input rows; 4 x 56 tiles of 64 x 64, one per block
+    pl = plan(4, 256, 57, 57, 256, s=2)
+    assert pl["kernel"] == 1 and pl["stream_blocks"] == 0 and pl["splits"] == 1
+    assert (pl["bm"], pl["bn"], pl["bk"], pl["waves"], pl["kgroups"]) == (64, 64, 144, 16, 4)
+    for W in (44, 45, 46, 47, 57, 59):                              # any W % 4 up to 14 quads
+        assert plan(1, 16, 40, W, 64, s=2)["kernel"] == 1, W
+    assert plan(1, 16, 40, 60, 64, s=2, p=0)["kernel"] == 0         # 15 quads: not compiled
+    assert plan(1, 16, 43, 42, 64, s=2)["kernel"] == 1              # OW = 21: 4 output rows
+    assert plan(1, 16, 41, 40, 64, s=2)["kernel"] == 0              # OW = 20: 5 rows
+    assert plan(1, 18, 40, 57, 64, s=2)["kernel"] == 0              # IC % 4 != 0
+    assert plan(4, 256, 57, 57, 256, 1, 1, 2, 0)["kernel"] == 0     # 1x1 stride 2
+    # no streamed instance: 257..511 tiles still run one per block
+    assert plan(5, 256, 57, 57, 256, s=2)["stream_blocks"] == 0     # 4 x 70 tiles
+    monkeypatch.setenv("BAIM_CONV_WIN", "s7")
+    assert plan(4, 256, 57, 57, 256, s=2)["stream_blocks"] == 0
+    monkeypatch.setenv("BAIM_CONV_WIN", "2")
+    assert plan(4, 256, 57, 57, 256, s=2)["splits"] == 2
