@@ -73,7 +73,9 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
     }
   }
   Accum<T> acc;
-  mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
+  // 16 waves with 4-byte loads on both operands: the peeled loop would spill
+  mainloop<T, decltype(al), decltype(bl), !(T::NT == 1024 && VA == 1 && VB == 1)>(
+      acc, al, bl, tb, te, smem, ws, lane);
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 
   // Fused epilogue: beta*self + alpha*acc, self broadcast from [N] or full.

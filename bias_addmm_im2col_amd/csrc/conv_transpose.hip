@@ -332,7 +332,8 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
     al.init(a, m0, table, g);
     TImColLoader<T> bl;
     bl.init(a, P, n0, table, g);
-    mainloop<T>(acc, al, bl, tb, te, smem, ws, lane);
+    // the unpeeled k loop: 62.4 against 65.0 us peeled on the 4x4 stride-2 case
+    mainloop<T, decltype(al), decltype(bl), false>(acc, al, bl, tb, te, smem, ws, lane);
   }
   if (!reduce_k_groups<T>(acc, smem, ws, lane)) return;
 

@@ -358,12 +358,23 @@ struct MainLoop {
       if (BL::kHasMeta && t + 2 < t_end) bl.meta(t + 2);
     }
     mma_tile<T, BL::kBTransposed>(acc, cur, cur + T::A_FLOATS, ws, lane);
-    if (t + 1 < t_end) put<NEXT>(t + 1, nxt);
+    // Loaders without metadata fetch every iteration (the last ones again
+    // fetch tile t_end - 1), so their write to the idle stage can be
+    // unconditional: nothing reads that stage before the next barrier.
+    if (!BL::kHasMeta || t + 1 < t_end) put<NEXT>(t + 1, nxt);
     __syncthreads();
   }
 };
 
-template <class T, class AL, class BL>
+// With PF = 2 the loop body runs both register slots' iterations and a lone
+// last iteration is peeled after the loop, so every path into the loop
+// header carries the same outstanding loads.  (With the second iteration
+// under an `if`, the path that skips it reaches the header with the other
+// slot's loads in flight, and the compiler then waits for every load --
+// including the prefetch just issued -- before the first LDS read of each
+// iteration.)  PEEL = false keeps the unpeeled loop, for instances whose
+// registers the duplicated iteration would spill.
+template <class T, class AL, class BL, bool PEEL = true>
 __device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_begin, int t_end,
                                          float* smem, const WaveSlot& ws, int lane) {
   acc.zero();
@@ -380,7 +391,14 @@ __device__ __forceinline__ void mainloop(Accum<T>& acc, AL& al, BL& bl, int t_be
     ml.template fetch<1>(t_begin + 1 < t_end ? t_begin + 1 : t_begin);
   ml.template put<0>(t_begin, smem);
   __syncthreads();
-  if (T::PF == 2) {
+  if (T::PF == 2 && PEEL) {
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+      ml.template step<0>(t, t - t_begin);
+      ml.template step<1>(t + 1, t + 1 - t_begin);
+    }
+    if (t < t_end) ml.template step<0>(t, t - t_begin);
+  } else if (T::PF == 2) {
     for (int t = t_begin; t < t_end; t += 2) {
       ml.template step<0>(t, t - t_begin);
       if (t + 1 < t_end) ml.template step<1>(t + 1, t + 1 - t_begin);
