@@ -118,6 +118,40 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
     }
     return;
   }
+  if (epi == EPI_STORE && p.self_mode == 1 && m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
+    // A whole tile with self [N]: no bounds tests and no mode choice per
+    // element (with them, the epilogue cost 3.7 us of the 4096 x 4096 x
+    // 1024 down-projection and 3.3 us of the 2048 x 768 x 3072 FFN).
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int n = n0 + ws.wn0 + 32 * j + c;
+        const float bs = p.beta * p.self[n];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          p.out[(size_t)m * p.N + n] = fmaf(p.alpha, acc.c[i][j][r], bs);
+        }
+      }
+    return;
+  }
+  if (epi == EPI_STORE && p.self_mode == 2 && m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
+    // the same with a full self (ragged-577 addmm 56.8 -> 55.6 us)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int n = n0 + ws.wn0 + 32 * j + c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t o = (size_t)(m0 + ws.wm0 + 32 * i + acc_row(r, lane)) * p.N + n;
+          const float sv = (kSelfAhead && self_ahead) ? sv[r] : p.self[o];
+          p.out[o] = fmaf(p.alpha, acc.c[i][j][r], p.beta * sv);
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
     const int n = n0 + ws.wn0 + 32 * j + c;
@@ -207,6 +241,191 @@ static_assert(same_tile<T128x128>(TILE_128x128) && same_tile<T128x64>(TILE_128x6
                   same_tile<T32x128>(TILE_32x128),
               "tile table out of sync with the compiled tiles");
 
+// ------------------------------------------------------ the 256x256 tile
+// Large addmm, one 256x256 output tile per block: 8 waves of 128x64
+// outputs (4 x 2 blocks of 32x32, 128 accumulator registers, two waves per
+// SIMD), k-tiles of 16 with two k-tiles of register prefetch and
+// double-buffered LDS, as in the tile core (same LDS layouts and MFMA
+// step order).  Per MFMA a wave reads a third of what a 64x32 wave of the
+// 128x128 tile reads.  It is a kernel of its own: built from the tile core
+// (per-k-tile buffer descriptors, the schedule hooks) the same tile held
+// about 20 more registers through the k loop, the compiler then issued
+// each B read right before its MFMAs, and it ran 262 us against 244 us in
+// this form on the 4096 x 1024 x 4096 up-projection.
+//
+// mat1 rows of the block and all of mat2 (from the block's first column)
+// are addressed with 32-bit offsets: the planner takes this tile only with
+// 256*K and K*N below 2^29.  Rows past M or K read past the buffer ranges
+// (0); columns past K (mat1) or N (mat2) are masked per load.
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 16, NT = 512, WTM = 128, WTN = 64;
+constexpr int FM = WTM / 32, FN = WTN / 32;
+constexpr int AS = BK + 4, BS = BN + 8;  // LDS row strides, as in Tile
+constexpr int A_FLOATS = BM * AS, B_FLOATS = BK * BS, STAGE = A_FLOATS + B_FLOATS;
+static_assert(BM == kTileBM[TILE_256x256] && BN == kTileBN[TILE_256x256] &&
+                  BK == kTileBK[TILE_256x256] && NT == 64 * kTileWaves[TILE_256x256] &&
+                  kTileKGroups[TILE_256x256] == 1,
+              "tile table out of sync with the 256x256 kernel");
+}  // namespace big
+
+template <int VA, int VB>
+__global__ __launch_bounds__(big::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void addmm_big_kernel(AddmmArgs p) {
+  using namespace big;
+  __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, p.sched.tiles_m, p.sched.tiles_n, p.sched.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm0 = (wave / (BN / WTN)) * WTM, wn0 = (wave % (BN / WTN)) * WTN;
+  const int K = p.K, N = p.N;
+  const int rows = min(BM, p.M - m0), cols = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (size_t)m0 * K, (int64_t)rows * K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + n0, (int64_t)(K - 1) * N + cols);
+  constexpr int A_NQ = BM * BK / VA / NT, B_NQ = BK * BN / VB / NT;
+  typedef typename Vec<VA>::T TA;
+  typedef typename Vec<VB>::T TB;
+  TA xa0[A_NQ], xa1[A_NQ];
+  TB xb0[B_NQ], xb1[B_NQ];
+  auto fetch = [&](TA* xa, TB* xb, int t) __attribute__((always_inline)) {
+    const int k0 = t * BK;
+#pragma unroll
+    for (int q = 0; q < A_NQ; ++q) {
+      const int i = tid + NT * q, r = i / (BK / VA), cc = (i % (BK / VA)) * VA;
+      xa[q] = Vec<VA>::load(ra, k0 + cc < K ? (uint32_t)(r * K + k0 + cc) * 4u : kOOB);
+    }
+#pragma unroll
+    for (int q = 0; q < B_NQ; ++q) {
+      const int i = tid + NT * q, r = i / (BN / VB), cc = (i % (BN / VB)) * VB;
+      xb[q] = Vec<VB>::load(rb, cc < cols ? (uint32_t)((k0 + r) * N + cc) * 4u : kOOB);
+    }
+  };
+  auto put = [&](const TA* xa, const TB* xb, float* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < A_NQ; ++q) {
+      const int i = tid + NT * q, r = i / (BK / VA), cc = (i % (BK / VA)) * VA;
+      *reinterpret_cast<TA*>(&buf[r * AS + cc]) = xa[q];
+    }
+#pragma unroll
+    for (int q = 0; q < B_NQ; ++q) {
+      const int i = tid + NT * q, r = i / (BN / VB), cc = (i % (BN / VB)) * VB;
+      *reinterpret_cast<TB*>(&buf[A_FLOATS + r * BS + cc]) = xb[q];
+    }
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // one k-tile: step s of lane half h takes k = 8g + 4h + s (the tile
+  // core's order), A four k at a time from [BM][BK+4], B from [BK][BN+8]
+  auto mma = [&](const float* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < BK / 8; ++g) {
+      const int k = 8 * g + 4 * h;
+      f32x4 a[FM];
+      float b[FN][4];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const f32x4*>(&buf[(wm0 + 32 * i + c) * AS + k]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[j][s] = buf[A_FLOATS + (k + s) * BS + wn0 + 32 * j + c];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+    }
+  };
+  // the k loop: both register slots' iterations per trip and a lone last
+  // one after it (every path into the loop header carries the same loads);
+  // the last fetches reload tile nkt - 1 into a slot never written to LDS
+  const int nkt = (K + BK - 1) / BK;
+  fetch(xa0, xb0, 0);
+  fetch(xa1, xb1, nkt > 1 ? 1 : 0);
+  put(xa0, xb0, smem);
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < nkt; t += 2) {
+    fetch(xa0, xb0, t + 2 < nkt ? t + 2 : nkt - 1);
+    mma(smem);
+    put(xa1, xb1, smem + STAGE);
+    __syncthreads();
+    fetch(xa1, xb1, t + 3 < nkt ? t + 3 : nkt - 1);
+    mma(smem + STAGE);
+    put(xa0, xb0, smem);
+    __syncthreads();
+  }
+  if (t < nkt) mma(smem);
+
+  // beta*self + alpha*acc, self broadcast from [N] or full [M,N].  The
+  // self mode is uniform: with self [N] (the bias case) a tile wholly
+  // inside out has a loop of its own without bounds tests.  With the
+  // tests and the mode choice inside the innermost loop this epilogue cost
+  // 11 us of the 4096 x 1024 x 4096 up-projection's 256.  (Loops of their
+  // own for the other modes hoisted their loads or addresses and spilled.)
+  const float alpha = p.alpha, beta = p.beta;
+  float* const out = p.out;
+  const float* const self = p.self;
+  if (rows == BM && cols == BN && p.self_mode == 1) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn0 + 32 * j + c;
+        const float bs = beta * self[n];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
+          out[(size_t)m * N + n] = fmaf(alpha, acc[i][j][r], bs);
+        }
+      }
+    return;
+  }
+  // no self, a full self or an edge tile: every element tested
+  // against M and N
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn0 + 32 * j + c;
+    if (n >= N) continue;
+    const float srow = p.self_mode == 1 ? self[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
+        if (m >= p.M) continue;
+        const size_t o = (size_t)m * N + n;
+        const float v = acc[i][j][r];
+        if (p.self_mode == 0) {
+          out[o] = alpha * v;
+        } else {
+          const float sv = p.self_mode == 1 ? srow : self[o];
+          out[o] = fmaf(alpha, v, beta * sv);
+        }
+      }
+  }
+}
+
+static hipError_t launch_big(const AddmmArgs& a, int nblocks, bool va, bool vb, hipStream_t s) {
+  if (va && vb)
+    hipLaunchKernelGGL((addmm_big_kernel<4, 4>), dim3(nblocks), dim3(big::NT), 0, s, a);
+  else if (va)
+    hipLaunchKernelGGL((addmm_big_kernel<4, 1>), dim3(nblocks), dim3(big::NT), 0, s, a);
+  else if (vb)
+    hipLaunchKernelGGL((addmm_big_kernel<1, 4>), dim3(nblocks), dim3(big::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((addmm_big_kernel<1, 1>), dim3(nblocks), dim3(big::NT), 0, s, a);
+  return hipGetLastError();
+}
+
 template <class T, int VA, int VB, int MODE, bool WNK = false, int AK = A_ROWS>
 static hipError_t launch_t(const AddmmArgs& a, int nblocks, hipStream_t s) {
   hipLaunchKernelGGL((addmm_kernel<T, VA, VB, MODE, WNK, AK>), dim3(nblocks), dim3(T::NT), 0, s, a);
@@ -259,6 +478,10 @@ static hipError_t launch_cfg(int cfg, const AddmmArgs& a, int nblocks, bool va, 
       return launch_vec<T64x64K4, TILE_64x64_K4, MODE, WNK, AK>(a, nblocks, va, vb, s);
     case TILE_32x128:
       return launch_vec<T32x128, TILE_32x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
+    case TILE_256x256:
+      // addmm, one tile per block (the other callers plan with plan_core_tile)
+      if constexpr (AK == A_ROWS && !WNK && MODE == MODE_TILE) return launch_big(a, nblocks, va, vb, s);
+      return hipErrorInvalidValue;
     default:
       return launch_vec<T128x128, TILE_128x128, MODE, WNK, AK>(a, nblocks, va, vb, s);
   }
@@ -272,6 +495,8 @@ static hipError_t launch_gemm(const AddmmProblem& p, AddmmArgs& a, bool va, bool
   // mat2 [K, N] is read BK rows at a time with 32-bit offsets
   if (AK == A_ROWS && !p.weight_nk) plan = plan_fit_col_operand(plan, p.M, p.N, p.K);
   if (plan.mode == MODE_STREAM && !(va && vb)) plan = plan_tiles_only(plan, p.M, p.N, p.K);
+  if (AK == A_NHWC || p.weight_nk || !plan_big_fits(p.N, p.K))
+    plan = plan_core_tile(plan, p.M, p.N, p.K);
   if (AK == A_NHWC && !(va && vb) && plan.cfg == TILE_128x128_K2)
     plan = plan_gemm(p.M, p.N, p.K, "0");  // same block tile, 8 waves
   a.out = p.out;

@@ -87,7 +87,9 @@ baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn, in
   if (M < 0 || N < 0 || K < 0) return fail(BAIM_ERR_SHAPE, "baim_gemm_plan: sizes must be >= 0");
   if (M >= kMaxElems || N >= kMaxElems || K >= kMaxElems)
     return fail(BAIM_ERR_TOO_LARGE, "baim_gemm_plan: size too large");
-  const baim::GemmPlan p = baim::plan_gemm((int)M, (int)N, (int)K, getenv("BAIM_TILE"));
+  baim::GemmPlan p = baim::plan_gemm((int)M, (int)N, (int)K, getenv("BAIM_TILE"));
+  // as addmm_f32 launches it
+  if (!baim::plan_big_fits((int)N, (int)K)) p = baim::plan_core_tile(p, (int)M, (int)N, (int)K);
   *bm = baim::kTileBM[p.cfg];
   *bn = baim::kTileBN[p.cfg];
   *bk = baim::kTileBK[p.cfg];
@@ -320,7 +322,7 @@ baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W, int64_
   }
   *kernel = 0;
   const int M = q.OC / q.groups, N = q.B * q.OH * q.OW, K = q.IC / q.groups * q.KH * q.KW;
-  baim::GemmPlan p = baim::plan_gemm(M, N, K, getenv("BAIM_TILE"));
+  baim::GemmPlan p = baim::plan_core_tile(baim::plan_gemm(M, N, K, getenv("BAIM_TILE")), M, N, K);
   if (p.mode == baim::MODE_STREAM && K % 4 != 0) p = baim::plan_tiles_only(p, M, N, K);
   *bm = baim::kTileBM[p.cfg];
   *bn = baim::kTileBN[p.cfg];

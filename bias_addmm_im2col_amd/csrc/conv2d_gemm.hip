@@ -303,6 +303,8 @@ static hipError_t launch_cfg(int cfg, const ConvArgs& a, int nblocks, bool va, h
       return launch_vec<T64x64K2, TILE_64x64_K2, MODE>(a, nblocks, va, s);
     case TILE_64x64_K4:
       return launch_vec<T64x64K4, TILE_64x64_K4, MODE>(a, nblocks, va, s);
+    case TILE_256x256:
+      return hipErrorInvalidValue;  // not compiled here (plan_core_tile)
     case TILE_32x128:
       return launch_vec<T32x128, TILE_32x128, MODE>(a, nblocks, va, s);
     default:
@@ -355,7 +357,7 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   a.div_p = make_fastdiv((uint32_t)(q.OH * q.OW));
   a.div_ow = make_fastdiv((uint32_t)q.OW);
   const bool va = a.K % 4 == 0 && ((uintptr_t)q.w & 15) == 0;
-  GemmPlan plan = plan_gemm(a.M, a.N, a.K, getenv("BAIM_TILE"));
+  GemmPlan plan = plan_core_tile(plan_gemm(a.M, a.N, a.K, getenv("BAIM_TILE")), a.M, a.N, a.K);
   if (plan.mode == MODE_STREAM && !va) plan = plan_tiles_only(plan, a.M, a.N, a.K);
   a.sched = Sched{plan.tiles_m, plan.tiles_n, 8, plan.nkt, plan.splits, plan.kt_per_split};
   const int nblocks = (int)plan_blocks(plan);

@@ -451,6 +451,7 @@ hipError_t launch_cfg(int cfg, const ConvTArgs& a, int nph, int groups, bool uni
     case TILE_64x64_K2: return launch_phases<T64x64K2>(a, nph, groups, unit, s);
     case TILE_64x64_K4: return launch_phases<T64x64K4>(a, nph, groups, unit, s);
     case TILE_32x128: return launch_phases<T32x128>(a, nph, groups, unit, s);
+    case TILE_256x256: return hipErrorInvalidValue;  // not compiled here (plan_core_tile)
     default: return launch_phases<T128x128>(a, nph, groups, unit, s);
   }
 }
@@ -696,7 +697,7 @@ hipError_t launch_conv_transpose2d(const ConvTProblem& q, hipStream_t stream) {
   const int n_all = (int)(n_sum < 0x7FFFFFFF ? n_sum : 0x7FFFFFFF);
   const char* spec = getenv("BAIM_TILE");
   const bool forced = spec && *spec;
-  GemmPlan plan = plan_gemm(a.OCg, n_all, k_max, spec);
+  GemmPlan plan = plan_core_tile(plan_gemm(a.OCg, n_all, k_max, spec), a.OCg, n_all, k_max);
   // K slices only from a "cfg,S" override here; the automatic choice follows.
   int splits = forced && plan.mode == MODE_SLICES ? plan.splits : 1;
   const int64_t t64x128 = (int64_t)((a.OCg + 63) / 64) * ((n_all + 127) / 128);

@@ -3,6 +3,10 @@
 // The choice follows how the chip fills (256 CUs) and how deep K is; the
 // thresholds come from timing every configuration on the workload shapes
 // (large / down / up projections, FFN, ragged 577-row, 3x3 and 7x7 convs):
+//  * >= 256 tiles of 256x256 that fill the CUs evenly, K >= 512: the
+//    256x256 tile (8 waves of 128x64; a third of the LDS reads per MFMA
+//    of the 128x128 tile's 64x32 waves).  addmm only: its kernel indexes
+//    the whole of mat2 and a 256-row panel of mat1 with 32-bit offsets.
 //  * >= 512 tiles of 128x128: the 128x128 tile (most reuse per byte).
 //  * >= 192 such tiles and deep K: 128x128 with each k-tile split over two
 //    wave groups (16 waves per block: one block per CU still keeps four
@@ -106,6 +110,10 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
     if (s > nkt / 8) s = nkt / 8;
     return make(TILE_32x128, M, N, K, s < 1 ? 1 : s);
   }
+  const int64_t t256 = tiles_of(TILE_256x256, M, N);
+  if (t256 >= kNumCUs && (t256 % kNumCUs == 0 || t256 >= 4 * kNumCUs) && K >= 512 &&
+      plan_big_fits(N, K))
+    return make(TILE_256x256, M, N, K, 1);
   const int64_t t128 = tiles_of(TILE_128x128, M, N);
   if (t128 >= 2 * kNumCUs) return make(TILE_128x128, M, N, K, 1);
   if (t128 >= (3 * kNumCUs) / 4 && nkt >= 48) {
@@ -137,6 +145,10 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec) {
 
 GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K) {
   return make(p.cfg, M, N, K, 1);
+}
+
+GemmPlan plan_core_tile(const GemmPlan& p, int M, int N, int K) {
+  return kTileCore[p.cfg] ? p : make(TILE_128x128, M, N, K, 1);
 }
 
 bool plan_col_tile_fits(int cfg, int N) {

@@ -19,18 +19,23 @@ enum TileCfg {
   TILE_64x64_K2 = 6,    // BK 64, 8 waves
   TILE_64x64_K4 = 7,    // BK 128, 16 waves
   TILE_32x128 = 8,      // BK 32, 4 waves, 32x32 per wave: GEMMs with M <= 32
-  TILE_NCFG = 9
+  TILE_256x256 = 9,     // BK 16, 8 waves, 128x64 per wave: large addmm (own kernel)
+  TILE_NCFG = 10
 };
 
-constexpr int kTileBM[TILE_NCFG] = {128, 128, 64, 64, 128, 128, 64, 64, 32};
-constexpr int kTileBN[TILE_NCFG] = {128, 64, 128, 64, 128, 64, 64, 64, 128};
-constexpr int kTileBK[TILE_NCFG] = {32, 32, 32, 32, 64, 64, 64, 128, 32};
-constexpr int kTileWaves[TILE_NCFG] = {8, 8, 8, 4, 16, 16, 8, 16, 4};
-constexpr int kTileKGroups[TILE_NCFG] = {1, 1, 1, 1, 2, 2, 2, 4, 1};
+constexpr int kTileBM[TILE_NCFG] = {128, 128, 64, 64, 128, 128, 64, 64, 32, 256};
+constexpr int kTileBN[TILE_NCFG] = {128, 64, 128, 64, 128, 64, 64, 64, 128, 256};
+constexpr int kTileBK[TILE_NCFG] = {32, 32, 32, 32, 64, 64, 64, 128, 32, 16};
+constexpr int kTileWaves[TILE_NCFG] = {8, 8, 8, 4, 16, 16, 8, 16, 4, 8};
+constexpr int kTileKGroups[TILE_NCFG] = {1, 1, 1, 1, 2, 2, 2, 4, 1, 1};
 // Configurations compiled with the K-slice and stream schedules (the
 // others would exceed their register budget with the extra state).
-constexpr bool kTileSlices[TILE_NCFG] = {true, true, true, true, false, true, true, true, true};
-constexpr bool kTileStream[TILE_NCFG] = {true, true, true, true, false, true, true, false, true};
+constexpr bool kTileSlices[TILE_NCFG] = {true, true, true, true, false, true, true, true, true, false};
+constexpr bool kTileStream[TILE_NCFG] = {true, true, true, true, false, true, true, false, true, false};
+// Configurations the tile-core kernels run (addmm's other instances,
+// linear, the im2col convs): the 256x256 tile has a kernel of its own for
+// addmm, and plan_core_tile maps it to the 128x128 tile for the others.
+constexpr bool kTileCore[TILE_NCFG] = {true, true, true, true, true, true, true, true, true, false};
 constexpr int kNumCUs = 256;  // MI355X
 
 // How blocks map to work (the kernels' scheduling modes).
@@ -58,6 +63,18 @@ GemmPlan plan_gemm(int M, int N, int K, const char* override_spec);
 
 // The same tile configuration with one tile per block.
 GemmPlan plan_tiles_only(const GemmPlan& p, int M, int N, int K);
+
+// `p` for a tile-core kernel: the 256x256 configuration, which only the
+// dedicated addmm kernel runs, becomes the 128x128 tile, one tile per
+// block (what the planner chose for such sizes before the 256x256 tile
+// existed).
+GemmPlan plan_core_tile(const GemmPlan& p, int M, int N, int K);
+
+// Whether the 256x256 kernel's 32-bit offsets reach all of mat2 [K, N] and
+// a 256-row panel of mat1 [M, K].
+inline bool plan_big_fits(int N, int K) {
+  return (int64_t)K * N < ((int64_t)1 << 29) && (int64_t)256 * K < ((int64_t)1 << 29);
+}
 
 // Whether a B tile read from a row-major [K, N] matrix (mat2) keeps every
 // in-tile byte offset below 2^31: the tile spans BK rows of N floats, so

@@ -263,9 +263,11 @@ baim_status baim_conv2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW,
  * A tile cut into exactly two pieces is combined with a fixed, order-free
  * sum (bit-reproducible).  Only with splits > 2 (grids too small to fill
  * the chip otherwise) are the slices added with atomics, and the last bits
- * may then differ from run to run.  The environment variable BAIM_TILE
- * ("cfg", "cfg,S" or "cfg,sP", cfg 0..7) overrides the choice for tuning,
- * here and in the two ops.  Host-only; touches no GPU.
+ * may then differ from run to run.  The 256 x 256 tile (BK 16, 8 waves) is
+ * addmm's alone: linear_f32 and the convs run the 128 x 128 tile where it
+ * is planned.  The environment variable BAIM_TILE ("cfg", "cfg,S" or
+ * "cfg,sP", cfg 0..9) overrides the choice for tuning, here and in the
+ * ops.  Host-only; touches no GPU.
  */
 baim_status baim_gemm_plan(int64_t M, int64_t N, int64_t K, int* bm, int* bn,
                            int* bk, int* waves, int* kgroups, int* splits,

@@ -7,7 +7,8 @@ S > 2 atomic adds) or "cfg,sP" (P blocks stream over the (tile, k-tile)
 units; two-piece exchange).  Configurations (bm x bn x bk, waves):
 0 = 128x128x32 (8), 1 = 128x64x32 (8), 2 = 64x128x32 (8), 3 = 64x64x32 (4),
 4 = 128x128x64 (16), 5 = 128x64x64 (16), 6 = 64x64x64 (8),
-7 = 64x64x128 (16), 8 = 32x128x32 (4).
+7 = 64x64x128 (16), 8 = 32x128x32 (4), 9 = 256x256x16 (8; addmm only: linear
+and the im2col conv paths run configuration 0 for it).
 
 Configuration 5 streamed over P blocks carries the 3x3 mid-stage convs; its
 specs ("5,sP", "5,2", "5,3") are here on purpose.  Every spec must change
@@ -20,6 +21,9 @@ hide in these lists.
 GEMM_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "8",
               "0,3", "1,2", "2,4", "3,5", "0,64", "5,2", "5,3", "6,3", "7,2", "7,3", "8,2", "8,3",
               "3,s7", "0,s2", "5,s7", "5,s13", "6,s5", "2,s9", "1,s4", "8,s5"]
+
+# addmm also forces the 256x256 tile
+ADDMM_SPECS = GEMM_SPECS + ["9"]
 
 NHWC_SPECS = ["0", "1", "2", "3", "4", "5", "6", "7", "8",
               "0,3", "2,3", "5,2", "5,3", "7,2",

@@ -161,6 +161,8 @@ def test_gemm_plan(lib, monkeypatch):
     import bias_addmm_im2col_amd as baim
     monkeypatch.delenv("BAIM_TILE", raising=False)
     p = baim.gemm_plan(4096, 4096, 1024)
+    assert (p["bm"], p["bn"], p["bk"], p["waves"], p["kgroups"], p["splits"]) == (256, 256, 16, 8, 1, 1)
+    p = baim.gemm_plan(8192, 4096, 256)  # K below 512: the 128x128 tile
     assert (p["bm"], p["bn"], p["bk"], p["waves"], p["kgroups"], p["splits"]) == (128, 128, 32, 8, 1, 1)
     # every workload shape is planned without a cross-block K split
     from bias_addmm_im2col_amd import inputs as I

@@ -20,7 +20,7 @@ from tests import _specs
 CFG = {  # bm, bn, bk, waves
     0: (128, 128, 32, 8), 1: (128, 64, 32, 8), 2: (64, 128, 32, 8), 3: (64, 64, 32, 4),
     4: (128, 128, 64, 16), 5: (128, 64, 64, 16), 6: (64, 64, 64, 8), 7: (64, 64, 128, 16),
-    8: (32, 128, 32, 4)}
+    8: (32, 128, 32, 4), 9: (256, 256, 16, 8)}
 
 
 @pytest.fixture(scope="module")
@@ -56,7 +56,7 @@ def effective(spec, M, N, K, vec, nhwc, monkeypatch):
     return tile, splits, stream
 
 
-CASES = ([("addmm", s) for s in _specs.GEMM_SPECS] + [("linear", s) for s in _specs.GEMM_SPECS] +
+CASES = ([("addmm", s) for s in _specs.ADDMM_SPECS] + [("linear", s) for s in _specs.GEMM_SPECS] +
          [("conv", s) for s in _specs.GEMM_SPECS] + [("nhwc", s) for s in _specs.NHWC_SPECS])
 GEMMS = {"addmm": _specs.addmm_gemms, "linear": _specs.linear_gemms, "conv": _specs.conv_gemms,
          "nhwc": _specs.nhwc_gemms}
@@ -84,3 +84,33 @@ def test_spec_lists_hold_the_dominant_conv_instance():
     for lst in (_specs.GEMM_SPECS, _specs.NHWC_SPECS):
         for s in ("5,s7", "5,s13", "5,2", "5,3"):
             assert s in lst
+
+
+def plan_tile(M, N, K):
+    st, p = _capi.gemm_plan(M, N, K)
+    assert st == 0
+    return p["bm"], p["bn"], p["bk"], p["waves"]
+
+
+def test_large_gemms_take_the_256_tile(lib, monkeypatch):
+    monkeypatch.delenv("BAIM_TILE", raising=False)
+    big = CFG[9]
+    assert plan_tile(4096, 4096, 1024) == big       # up-proj: 256 tiles, one per CU
+    assert plan_tile(4096, 4096, 4096) == big
+    assert plan_tile(8192, 8192, 512) == big        # 1024 tiles
+    assert plan_tile(4000, 4096, 1024) == big       # ragged rows: still 256 tiles
+    assert plan_tile(4096, 1024, 4096) != big       # down-proj: 64 tiles
+    assert plan_tile(4096, 4096, 256) != big        # K below 512
+    assert plan_tile(4096, 4352, 1024) != big       # 272 tiles: a second round mostly idle
+    assert plan_tile(2048, 3072, 768) != big        # FFN: 96 tiles
+
+
+def test_conv_paths_never_run_the_256_tile(lib, monkeypatch):
+    """The im2col conv kernels are not compiled with the 256x256 tile: a
+    plan (or a forced spec) for it becomes the 128x128 tile."""
+    for spec in ("", "9"):
+        monkeypatch.setenv("BAIM_TILE", spec)
+        # a 1x1 conv with M = 512, N = 64*56*56, K = 512: 1568 tiles of 256x256
+        st, p = _capi.conv2d_plan(64, 512, 56, 56, 512, 1, 1, 1, 1, 0, 0, 1, 1, 1)
+        assert st == 0 and p["kernel"] == 0
+        assert (p["bm"], p["bn"], p["bk"], p["waves"]) == CFG[0]

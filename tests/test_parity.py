@@ -326,7 +326,7 @@ def test_repeated_launches_are_deterministic():
 TILE_SPECS = _specs.GEMM_SPECS
 
 
-@pytest.mark.parametrize("spec", TILE_SPECS)
+@pytest.mark.parametrize("spec", _specs.ADDMM_SPECS)
 def test_addmm_forced_tile_configs(spec, monkeypatch):
     monkeypatch.setenv("BAIM_TILE", spec)
     for M, K, N, self_2d, beta, alpha in _specs.ADDMM_SHAPES:
