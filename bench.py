@@ -209,6 +209,11 @@ class Case:
             M, N = N, M
         p = baim.gemm_plan(M, N, K)
         kname = "conv2d_gemm_kernel" if c.kind == "conv" and not c.channels_last else "addmm_kernel"
+        if p["bm"] == 256:  # the 256x256 tile: addmm's own kernel; the others run 128x128
+            if c.kind == "addmm":
+                kname = "addmm_big_kernel"
+            else:
+                p = dict(p, bm=128, bn=128, bk=32, waves=8, kgroups=1)
         geom = ""
         if c.kind == "conv" and not c.channels_last:
             p = baim.conv2d_plan((c.B, c.IC, c.H, c.W), (c.OC, c.IC // c.groups, c.KH, c.KW),
