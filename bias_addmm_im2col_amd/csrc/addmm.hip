@@ -146,8 +146,8 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const size_t o = (size_t)(m0 + ws.wm0 + 32 * i + acc_row(r, lane)) * p.N + n;
-          const float sv = (kSelfAhead && self_ahead) ? sv[r] : p.self[o];
-          p.out[o] = fmaf(p.alpha, acc.c[i][j][r], p.beta * sv);
+          const float s = (kSelfAhead && self_ahead) ? sv[r] : p.self[o];
+          p.out[o] = fmaf(p.alpha, acc.c[i][j][r], p.beta * s);
         }
       }
     return;
