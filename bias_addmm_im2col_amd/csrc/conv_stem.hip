@@ -249,6 +249,22 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   // 4j .. 4j+3 of the wave's 16
   const int npix = n1 + n2;
   float* ob = p.out + (size_t)b * p.OC * p.P + p0;
+  if (m0 + C::BM <= p.OC && npix == C::BN) {
+    // A whole tile: the four bias values first, then stores without the
+    // per-element channel and pixel tests (22.9 -> 21.3 us on the
+    // 768 x 768 stem, whose 256 tiles are all whole).
+    float bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bv[r] = p.bias ? p.bias[m0 + ocb * 16 + 4 * j + r] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* orow = ob + (size_t)(m0 + ocb * 16 + 4 * j + r) * p.P + 16 * pb0 + m;
+#pragma unroll
+      for (int pb = 0; pb < C::PBH; ++pb)
+        if (pb < nb) orow[16 * pb] = acc[pb][r] + bv[r];
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int oc = m0 + ocb * 16 + 4 * j + r;
