@@ -252,7 +252,8 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   if (m0 + C::BM <= p.OC && npix == C::BN) {
     // A whole tile: the four bias values first, then stores without the
     // per-element channel and pixel tests (22.9 -> 21.3 us on the
-    // 768 x 768 stem, whose 256 tiles are all whole).
+    // 768 x 768 stem, whose 256 tiles are all whole), marked non-temporal:
+    // the output is written once, all tiles at the end (19.9 -> 19.0 us).
     float bv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) bv[r] = p.bias ? p.bias[m0 + ocb * 16 + 4 * j + r] : 0.0f;
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
       float* orow = ob + (size_t)(m0 + ocb * 16 + 4 * j + r) * p.P + 16 * pb0 + m;
 #pragma unroll
       for (int pb = 0; pb < C::PBH; ++pb)
-        if (pb < nb) orow[16 * pb] = acc[pb][r] + bv[r];
+        if (pb < nb) __builtin_nontemporal_store(acc[pb][r] + bv[r], &orow[16 * pb]);
     }
     return;
   }
