@@ -189,6 +189,26 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
         }
     return;
   }
+  if (epi == EPI_STORE && m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
+    // A whole tile: per 32-row block the bias values first, then stores
+    // without tests (the grouped 3x3 conv with 8 groups of 32 channels:
+    // 42.4 -> 39.5 us).
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      float bv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bv[r] = p.bias ? p.bias[g * p.OCg + m0 + ws.wm0 + 32 * i + acc_row(r, lane)] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ocx = g * p.OCg + m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          p.out[obase[j] + (size_t)ocx * P] = acc.c[i][j][r] + bv[r];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
     const int n = n0 + ws.wn0 + 32 * j + c;

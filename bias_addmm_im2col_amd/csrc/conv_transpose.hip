@@ -354,6 +354,25 @@ __global__ __launch_bounds__(T::NT) void conv_transpose_kernel(ConvTArgs a) {
     obase[j] = (size_t)b * a.OC * plane + (size_t)(P.rh + a.sH * (int)t) * a.OW +
                (size_t)(P.rw + a.sW * (int)u);
   }
+  if (a.splits == 1 && m0 + T::BM <= a.OCg && n0 + T::BN <= P.N) {
+    // A whole tile: per 32-row block the bias values first, then stores
+    // without tests (the 4x4 stride-2 upsampling 62.3 -> 60.9 us).
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      float bv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bv[r] = a.bias ? a.bias[g * a.OCg + m0 + ws.wm0 + 32 * i + acc_row(r, lane)] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ocx = g * a.OCg + m0 + ws.wm0 + 32 * i + acc_row(r, lane);
+          a.out[obase[j] + (size_t)ocx * plane] = acc.c[i][j][r] + bv[r];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
     if (!nok[j]) continue;
@@ -557,7 +576,7 @@ __global__ __launch_bounds__(T::NT) void convt_fused_kernel(ConvTFusedArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
-          if (m >= a.M) continue;
+          if (m0 + T::BM > a.M && m >= a.M) continue;  // only an edge tile tests
           const uint32_t oc = fdiv((uint32_t)m, a.div_khw), kh = ((uint32_t)m - oc * a.div_khw.d) >> 1;
           const float bv = a.bias ? a.bias[g * a.OCg + oc] : 0.0f;
           typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -569,7 +588,7 @@ __global__ __launch_bounds__(T::NT) void convt_fused_kernel(ConvTFusedArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
-        if (m >= a.M) continue;
+        if (m0 + T::BM > a.M && m >= a.M) continue;  // only an edge tile tests
         const uint32_t oc = fdiv((uint32_t)m, a.div_khw), tap = (uint32_t)m - oc * a.div_khw.d;
         const uint32_t kh = fdiv(tap, a.div_kw), kw = tap - kh * a.div_kw.d;
         ob[oc * plane + (size_t)(a.KH * t + kh) * a.OW + a.KW * u + kw] =
