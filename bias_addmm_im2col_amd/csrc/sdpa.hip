@@ -385,6 +385,16 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
   }
   scale_rows(o, inv, slot, c, h);
   float* out = a.out + (size_t)bh * Sq * D;
+  if (qrow0 + 32 <= Sq && D == DP) {
+    // a whole block of 32 rows and every d: no test per element (the
+    // masked 64 x 577 cross-attention 25.1 -> 24.4 us)
+#pragma unroll
+    for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        out[(size_t)(qrow0 + 8 * (j / 4) + 4 * h + (j % 4)) * DP + 32 * db + c] = o[db][j];
+    return;
+  }
 #pragma unroll
   for (int db = 0; db < S::ND; ++db) {
     const int d = 32 * db + c;
