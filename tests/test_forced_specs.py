@@ -114,3 +114,13 @@ def test_conv_paths_never_run_the_256_tile(lib, monkeypatch):
         st, p = _capi.conv2d_plan(64, 512, 56, 56, 512, 1, 1, 1, 1, 0, 0, 1, 1, 1)
         assert st == 0 and p["kernel"] == 0
         assert (p["bm"], p["bn"], p["bk"], p["waves"]) == CFG[0]
+
+
+def test_forced_256_tile_respects_its_32_bit_offsets(lib, monkeypatch):
+    """The 256x256 kernel addresses all of mat2 [K, N] and a 256-row panel
+    of mat1 with 32-bit offsets: forced where K*N or 256*K reaches 2^29,
+    the plan (as addmm_f32 launches it) is the 128x128 tile instead."""
+    monkeypatch.setenv("BAIM_TILE", "9")
+    assert plan_tile(512, 4096, 1024) == CFG[9]
+    assert plan_tile(512, 4096, 1 << 17) == CFG[0]          # K*N = 2^29
+    assert plan_tile(512, 64, 1 << 21) == CFG[0]            # 256*K = 2^29

@@ -308,6 +308,28 @@ def test_workload_addmm_integer_bitwise(name):
     check_bitwise(out.cpu().numpy(), oracle.addmm(a, b, s, c.self_2d, 2.0, 0.5), f"integer {name}")
 
 
+@pytest.mark.parametrize("self_2d", [False, True])
+def test_addmm_256_tile_ragged_full_output(self_2d):
+    """The planner's 256x256 kernel on a shape with ragged M (4000 = 15*256
+    + 160) and K (520 = 32*16 + 8): whole tiles (the untested store loop
+    with self [N]), edge tiles and the partial last k-tile, every output
+    against the oracle.  Uniform inputs to the bound with alpha/beta;
+    integer inputs (every partial sum exact) bit for bit."""
+    import bias_addmm_im2col_amd as baim
+    M, K, N = 4000, 520, 4096
+    p = baim.gemm_plan(M, N, K)
+    say(f"addmm 256x256 tile M={M} K={K} N={N} self_2d={self_2d} plan {p}")
+    assert (p["bm"], p["bn"], p["bk"], p["waves"]) == (256, 256, 16, 8)
+    a, b = gen((M, K), 70), gen((K, N), 71)
+    s = gen((M, N) if self_2d else (N,), 72)
+    out = run_addmm(a, b, s, 0.5, 2.0)
+    check_close(out, oracle.addmm(a, b, s, self_2d, 0.5, 2.0), K, 2.0, "256 tile")
+    ai, bi = gen((M, K), 73, "I"), gen((K, N), 74, "I")
+    si = gen((M, N) if self_2d else (N,), 75, "I")
+    check_bitwise(run_addmm(ai, bi, si, 2.0, 0.5), oracle.addmm(ai, bi, si, self_2d, 2.0, 0.5),
+                  "256 tile integer")
+
+
 def test_repeated_launches_are_deterministic():
     """The same call twice gives the same bits (no cross-launch state)."""
     import bias_addmm_im2col_amd as baim
