@@ -11,13 +11,15 @@
 // per query row (maximum and sum rescaled as the maximum grows), so the
 // scores stay in registers and nothing is allocated.
 //
-// Work split: a block of four waves owns 32*QW query rows of one (batch,
-// head): QW query groups of 32 rows times KW key groups (QW*KW = 4).  The
-// block stages tiles of 32*NB*KW keys; in each, key group g takes the NB
-// 32-key blocks g*NB .. g*NB+NB-1, and keeps its own running softmax, so a
-// short query range still keeps four waves busy.  At the end the key groups'
-// (maximum, sum, O) are merged through LDS in group order.  Per 32-key block
-// a wave computes
+// Work split: a block of four (or eight) waves owns 32*QW query rows of one
+// (batch, head): QW query groups of 32 rows times KW key groups (QW*KW = 4,
+// or 1 x 8).  The block stages tiles of 32*NB*KW keys; in each, key group g
+// takes the NB 32-key blocks g*NB .. g*NB+NB-1, and keeps its own running
+// softmax, so a short query range still keeps every wave busy.  At the end
+// the key groups' (maximum, sum, O) are merged through LDS in group order.
+// The eight-wave shape puts two waves on each SIMD of a block; to fit their
+// registers it reads Q from LDS instead of holding it.  Per 32-key block a
+// wave computes
 //   S^T[kv, q] = K[kv, :] . Q[q, :]        (a 32x32 block, k = d)
 // on v_mfma_f32_32x32x2_f32 with K as the A operand (16-byte LDS reads) and
 // Q as the B operand (kept in registers for the whole pass), then
@@ -81,9 +83,16 @@ struct SdpaShape {
   static constexpr int STAT_FLOATS = 2 * KW * BQ;
   static constexpr int MERGE_FLOATS = RED_FLOATS + STAT_FLOATS;
   static constexpr int SLOT_OFS = TILE_FLOATS > MERGE_FLOATS ? TILE_FLOATS : MERGE_FLOATS;
-  static constexpr int LDS_FLOATS = SLOT_OFS + 32 * QW * KW;
+  // eight-wave blocks keep the block's Q rows in LDS (stride KS)
+  static constexpr bool QLDS = QW * KW == 8;
+  static constexpr int Q_OFS = SLOT_OFS + 32 * QW * KW;
+  static constexpr int LDS_FLOATS = Q_OFS + (QLDS ? BQ * KS : 0);
+  // their merge: every wave's partial O, the groups' (maximum, sum) and the
+  // rows' 1/sum, over the tile area
+  static constexpr int RED8_FLOATS = KW * QW * 32 * DP + 2 * KW * BQ + BQ;
   static_assert(DP % 32 == 0 && DP <= 128, "D is padded to 32, 64, 96 or 128");
-  static_assert(QW * KW == 4, "four waves per block");
+  static_assert(QW * KW == 4 || (QW == 1 && KW == 8 && DP <= 64), "four waves, or 1 x 8 for D <= 64");
+  static_assert(!QLDS || (RED8_FLOATS <= TILE_FLOATS && (ND * 16) % KW == 0), "eight-wave merge");
   static_assert((BKV * CH) % NT == 0, "tile splits evenly");
 };
 
@@ -121,10 +130,12 @@ struct SdpaMaskTile {
 };
 
 template <int DP, int QW, int KW, int NB, bool MASK, int MV>
-__global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) void sdpa_kernel(SdpaArgs a) {
+__global__ __launch_bounds__(64 * QW * KW, QW * KW == 8 ? 1 : DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1)
+void sdpa_kernel(SdpaArgs a) {
   using S = SdpaShape<DP, QW, KW, NB>;
   using MT = SdpaMaskTile<S::BQ, S::BKV, S::NT, MV>;
-  constexpr bool MSTAGE = MASK && KW > 1;  // mask tile staged through LDS
+  // mask tile staged through LDS (the eight-wave shape's tiles leave no room)
+  constexpr bool MSTAGE = MASK && KW > 1 && !S::QLDS;
   __shared__ __attribute__((aligned(16))) float smem[S::LDS_FLOATS + (MSTAGE ? MT::FLOATS : 0)];
   float* Ks = smem;
   float* Vs = smem + S::BKV * S::KS;
@@ -147,13 +158,29 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
   __amdgpu_buffer_rsrc_t mr;
   if constexpr (MASK) mr = make_rsrc(a.mask + (size_t)bh * Sq * Skv, (int64_t)Sq * Skv);
 
-  // Q fragments: chunk t holds Q[q][8t + 4h .. 8t + 4h + 3].
-  f32x4 qf[S::NQ];
+  // Q fragments: chunk t holds Q[q][8t + 4h .. 8t + 4h + 3], in registers,
+  // or (eight waves) read from the block's Q rows in LDS, which the first
+  // tile's barrier publishes.
+  f32x4 qf[S::QLDS ? 1 : S::NQ];
+  float* Qs = smem + S::Q_OFS;
+  if constexpr (S::QLDS) {
 #pragma unroll
-  for (int t = 0; t < S::NQ; ++t) {
-    const int d = 8 * t + 4 * h;
-    const uint32_t off = (q < Sq && d < D) ? (uint32_t)(q * D + d) * 4u : kOOB;
-    qf[t] = Vec<4>::load(qr, off);
+    for (int i = 0; i < (S::BQ * S::CH + S::NT - 1) / S::NT; ++i) {
+      const int idx = i * S::NT + tid;
+      const int row = idx / S::CH, d = 4 * (idx - row * S::CH);
+      const int qq = qb * S::BQ + row;
+      const bool in = (S::BQ * S::CH) % S::NT == 0 || row < S::BQ;
+      const uint32_t off = (in && qq < Sq && d < D) ? (uint32_t)(qq * D + d) * 4u : kOOB;
+      const f32x4 v4 = Vec<4>::load(qr, off);
+      if (in) *reinterpret_cast<f32x4*>(Qs + row * S::KS + d) = v4;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < S::NQ; ++t) {
+      const int d = 8 * t + 4 * h;
+      const uint32_t off = (q < Sq && d < D) ? (uint32_t)(q * D + d) * 4u : kOOB;
+      qf[t] = Vec<4>::load(qr, off);
+    }
   }
 
   // k/v tile loads: chunk i of thread tid is row idx / CH, column 4*(idx % CH).
@@ -263,12 +290,18 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
       for (int j = 0; j < 16; ++j) s[kb][j] = 0.0f;
       if (blk[kb]) {
         const float* krow = Ks + (kb0 + 32 * kb + c) * S::KS + 4 * h;
+        const float* qrow = Qs + (32 * qg + c) * S::KS + 4 * h;
 #pragma unroll
         for (int t2 = 0; t2 < S::NQ; ++t2) {
           const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + 8 * t2);
+          f32x4 b4;
+          if constexpr (S::QLDS)
+            b4 = *reinterpret_cast<const f32x4*>(qrow + 8 * t2);
+          else
+            b4 = qf[S::QLDS ? 0 : t2];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[r], qf[t2][r], s[kb], 0, 0, 0);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[r], b4[r], s[kb], 0, 0, 0);
         }
       }
     }
@@ -338,7 +371,55 @@ __global__ __launch_bounds__(256, DP <= 64 ? (QW == 4 && NB == 1 ? 3 : 2) : 1) v
   }
 
   float inv;
-  if constexpr (KW == 1) {
+  if constexpr (S::QLDS) {
+    // Eight key groups: every wave stores its partial O scaled by
+    // e^(m_g - M), then each wave sums one slice of the O registers over the
+    // groups in group order (the same sums as one wave adding the others to
+    // its own) and writes it.
+    float* red = smem;
+    float* stat_m = red + KW * QW * 32 * DP;
+    float* stat_l = stat_m + KW * S::BQ;
+    float* inv_row = stat_l + KW * S::BQ;
+    const float l_w = l_lane + __shfl_xor(l_lane, 32);
+    __syncthreads();  // the tile area is reused below
+    if (h == 0) {
+      stat_m[kg * S::BQ + 32 * qg + c] = m_run;
+      stat_l[kg * S::BQ + 32 * qg + c] = l_w;
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < KW; ++g) mx = fmaxf(mx, stat_m[g * S::BQ + 32 * qg + c]);
+    const float m_use = mx == -INFINITY ? 0.0f : mx;
+    scale_rows(o, __builtin_amdgcn_exp2f(m_run - m_use), slot, c, h);
+    float* mine = red + (kg * QW + qg) * 32 * DP;
+#pragma unroll
+    for (int db = 0; db < S::ND; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mine[(db * 16 + j) * 64 + lane] = o[db][j];
+    if (kg == 0 && h == 0) {
+      float L = 0.0f;
+#pragma unroll
+      for (int g = 0; g < KW; ++g)
+        L += stat_l[g * S::BQ + 32 * qg + c] *
+             __builtin_amdgcn_exp2f(stat_m[g * S::BQ + 32 * qg + c] - m_use);
+      inv_row[32 * qg + c] = 1.0f / L;
+    }
+    __syncthreads();
+    constexpr int SL = S::ND * 16 / KW;  // O registers per wave's slice
+    float* out = a.out + (size_t)bh * Sq * D;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int r = kg * SL + i, db = r / 16, j = r % 16;
+      float acc = red[(0 * QW + qg) * 32 * DP + r * 64 + lane];
+#pragma unroll
+      for (int g = 1; g < KW; ++g) acc += red[(g * QW + qg) * 32 * DP + r * 64 + lane];
+      const int rr = 8 * (j / 4) + 4 * h + (j % 4);  // row within the query group
+      const int row = qrow0 + rr, d = 32 * db + c;
+      if (row < Sq && d < D) out[(size_t)row * D + d] = acc * inv_row[32 * qg + rr];
+    }
+    return;
+  } else if constexpr (KW == 1) {
     inv = 1.0f / (l_lane + __shfl_xor(l_lane, 32));
   } else {
     // Merge the key groups of each query row: with M the largest group
@@ -427,9 +508,13 @@ hipError_t launch_dp(const SdpaArgs& a, int cfg, bool mask_vec, hipStream_t s) {
   static_assert(kSdpaQW[SDPA_Q4] == 4 && kSdpaKW[SDPA_Q4] == 1, "");
   static_assert(kSdpaQW[SDPA_Q2K2] == 2 && kSdpaKW[SDPA_Q2K2] == 2 && sdpa_nb(SDPA_Q2K2, DP) == 1, "");
   static_assert(kSdpaQW[SDPA_K4] == 1 && kSdpaKW[SDPA_K4] == 4 && sdpa_nb(SDPA_K4, DP) == 1, "");
+  static_assert(kSdpaQW[SDPA_K8] == 1 && kSdpaKW[SDPA_K8] == 8 && sdpa_nb(SDPA_K8, DP) == 1, "");
   switch (cfg) {
     case SDPA_Q2K2: return launch_cfg<DP, 2, 2, 1>(a, mask_vec, s);
     case SDPA_K4: return launch_cfg<DP, 1, 4, 1>(a, mask_vec, s);
+    case SDPA_K8:
+      if constexpr (DP <= kSdpaK8MaxD) return launch_cfg<DP, 1, 8, 1>(a, mask_vec, s);
+      else return hipErrorInvalidValue;  // the planner never picks it above
     default: return launch_cfg<DP, 4, 1, NBQ4>(a, mask_vec, s);
   }
 }

@@ -21,7 +21,10 @@ int main() {
             const int c = plan_sdpa(BH, Sq, Skv, D, s);
             if (c < 0 || c >= SDPA_NCFG) bad += printf("bad cfg %d\n", c) > 0;
             if (sdpa_nb(c, D) < 1 || sdpa_nb(c, D) > 2) bad += printf("bad key blocks\n") > 0;
-            if (kSdpaQW[c] * kSdpaKW[c] != 4) bad += printf("not four waves\n") > 0;
+            if (kSdpaQW[c] * kSdpaKW[c] != (c == SDPA_K8 ? 8 : 4)) bad += printf("wave count\n") > 0;
+            if (c == SDPA_K8 && D > kSdpaK8MaxD) bad += printf("eight waves above D %d\n", kSdpaK8MaxD) > 0;
+            if (c == SDPA_K8 && !(s && s[0] == '3' && !s[1]) && BH * ((Sq + 31) / 32) > 256)
+              bad += printf("eight waves over several rounds\n") > 0;
             const long bq = 32 * kSdpaQW[c];
             if (BH * ((Sq + bq - 1) / bq) >= (1L << 31)) bad += printf("grid too large\n") > 0;
           }
@@ -31,8 +34,14 @@ int main() {
   }
   if (plan_sdpa(96, 64, 577, 64, "7") != plan_sdpa(96, 64, 577, 64, nullptr))
     bad += printf("bad override not ignored\n") > 0;
-  // few (batch, head) slices with few queries: split the keys four ways
-  if (plan_sdpa(8, 1024, 4096, 64, nullptr) != SDPA_K4) bad += printf("pooled\n") > 0;
+  // the eight-wave shape is not compiled above D 64: its override falls back
+  if (plan_sdpa(8, 1024, 4096, 128, "3") != plan_sdpa(8, 1024, 4096, 128, nullptr) ||
+      plan_sdpa(8, 1024, 4096, 128, nullptr) == SDPA_K8)
+    bad += printf("eight waves at D 128\n") > 0;
+  // few (batch, head) slices with few queries: split the keys four ways,
+  // or eight ways (two waves per SIMD) over a long key range
+  if (plan_sdpa(8, 1024, 4096, 64, nullptr) != SDPA_K8) bad += printf("pooled\n") > 0;
+  if (plan_sdpa(16, 256, 2048, 64, nullptr) != SDPA_K8) bad += printf("long keys\n") > 0;
   if (plan_sdpa(96, 64, 577, 64, nullptr) != SDPA_K4) bad += printf("cross-attention\n") > 0;
   // enough query blocks to fill the chip: 128-row blocks
   if (plan_sdpa(64, 1024, 1024, 128, nullptr) != SDPA_Q4) bad += printf("long self-attention\n") > 0;

@@ -93,11 +93,12 @@ CFG_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", ["0", "1", "2"])
+@pytest.mark.parametrize("cfg", ["0", "1", "2", "3"])
 def test_sdpa_forced_block_shapes(cfg, monkeypatch):
     """Every block shape (query groups x key groups) on ragged sizes, forced
     through BAIM_SDPA: 128 query rows; 64 rows with two key groups; 32 rows
-    with four key groups merged at the end."""
+    with four key groups merged at the end; 32 rows with eight key groups in
+    eight waves (D <= 64; the larger D fall back to the plan)."""
     monkeypatch.setenv("BAIM_SDPA", cfg)
     for i, (BH, Sq, Skv, D, masked) in enumerate(CFG_SHAPES):
         say(f"BAIM_SDPA={cfg} sdpa_f32 BH={BH} Sq={Sq} Skv={Skv} D={D} mask={masked}")
