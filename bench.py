@@ -221,6 +221,15 @@ class Case:
             if p["kernel"] in (1, 3):  # the LDS-window and stem kernels
                 kname = "conv_window_kernel" if p["kernel"] == 1 else "conv_stem_kernel"
                 geom = (f"{c.KH}x{c.KW} s{c.stride[0]} d{c.dilation[0]}, ")
+        nhwc_stem = False
+        if c.kind == "conv" and c.channels_last:
+            nhwc_stem = baim.conv2d_nhwc_plan((c.B, c.H, c.W, c.IC), (c.OC, c.KH, c.KW, c.IC),
+                                              c.stride, c.padding, c.dilation)["kernel"] == 3
+            if nhwc_stem:  # the stem kernel's channels-last instance
+                kname = "conv_stem_kernel"
+                geom = (f"{c.KH}x{c.KW} s{c.stride[0]} d{c.dilation[0]}, ")
+                p = dict(p, bm=128, bn=144, bk=c.IC * c.KH * c.KW, waves=16, kgroups=1, splits=1,
+                         stream_blocks=0)
         self.plan = p
         # one kernel instance per (op, geometry, block tile, waves, wave groups, K split)
         self.kernel = (f"baim::{kname}"
@@ -263,7 +272,7 @@ class Case:
             geo = (c.B, c.IC, c.H, c.W, c.OC, c.KH, c.KW, *c.stride, *c.padding, *c.dilation)
             if c.channels_last:
                 self.out = torch.empty((c.B, OH, OW, c.OC), dtype=torch.float32, device="cuda")
-                self.kernel += " (im2col NHWC)"
+                self.kernel += " (NHWC)" if nhwc_stem else " (im2col NHWC)"
                 self.run = lambda: baim.conv2d_nhwc_f32(self.out, self.x, self.w, self.bias,
                                                         c.stride, c.padding, c.dilation)
                 self.run()

@@ -39,7 +39,7 @@ from . import _capi
 
 __all__ = ["addmm", "linear", "conv2d", "conv2d_nhwc", "conv_transpose2d", "sdpa", "addmm_f32",
            "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32", "conv_transpose2d_f32", "sdpa_f32",
-           "conv_transpose2d_out_hw", "conv2d_out_hw", "gemm_plan", "conv2d_plan",
+           "conv_transpose2d_out_hw", "conv2d_out_hw", "gemm_plan", "conv2d_plan", "conv2d_nhwc_plan",
            "BaimError", "library_path"]
 
 
@@ -215,6 +215,19 @@ def gemm_plan(M, N, K):
     """How the library computes an M x N x K GEMM (dict with bm, bn, bk,
     waves, kgroups, splits, stream_blocks).  Host-only."""
     st, plan = _capi.gemm_plan(M, N, K)
+    _check(st)
+    return plan
+
+
+def conv2d_nhwc_plan(input_shape, weight_shape, stride=1, padding=0, dilation=1):
+    """Which kernel conv2d_nhwc_f32 runs for these shapes (input [B,H,W,IC],
+    weight [OC,KH,KW,IC]): dict with kernel (0 the addmm kernels with an
+    im2col A operand, 3 the stem kernel).  Host-only."""
+    B, H, W, IC = (int(v) for v in input_shape)
+    OC, KH, KW, _ = (int(v) for v in weight_shape)
+    (sH, sW), (pH, pW), (dH, dW) = (_pair(stride, "stride"), _pair(padding, "padding"),
+                                    _pair(dilation, "dilation"))
+    st, plan = _capi.conv2d_nhwc_plan(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW)
     _check(st)
     return plan
 

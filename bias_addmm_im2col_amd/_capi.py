@@ -27,7 +27,8 @@ STATUS_NAMES = {
 # Every symbol include/baim.h declares.
 EXPORTS = ("addmm_f32", "linear_f32", "conv2d_gemm_f32", "conv2d_nhwc_f32",
            "conv_transpose2d_f32", "sdpa_f32", "baim_conv2d_out_hw", "baim_conv_transpose2d_out_hw",
-           "baim_gemm_plan", "baim_conv2d_plan", "baim_last_error", "baim_version")
+           "baim_gemm_plan", "baim_conv2d_plan", "baim_conv2d_nhwc_plan", "baim_last_error",
+           "baim_version")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -65,6 +66,8 @@ def lib():
     L.baim_gemm_plan.restype = ctypes.c_int
     L.baim_conv2d_plan.argtypes = [_i64] * 14 + [ctypes.POINTER(ctypes.c_int)] * 8
     L.baim_conv2d_plan.restype = ctypes.c_int
+    L.baim_conv2d_nhwc_plan.argtypes = [_i64] * 13 + [ctypes.POINTER(ctypes.c_int)]
+    L.baim_conv2d_nhwc_plan.restype = ctypes.c_int
     L.baim_last_error.argtypes = []
     L.baim_last_error.restype = ctypes.c_char_p
     L.baim_version.argtypes = []
@@ -130,6 +133,14 @@ def conv2d_plan(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, groups):
                                 *[ctypes.byref(o) for o in outs])
     keys = ("kernel", "bm", "bn", "bk", "waves", "kgroups", "splits", "stream_blocks")
     return st, {k: o.value for k, o in zip(keys, outs)}
+
+
+def conv2d_nhwc_plan(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW):
+    """(status, dict) with the kernel conv2d_nhwc_f32 uses."""
+    k = ctypes.c_int(0)
+    st = lib().baim_conv2d_nhwc_plan(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW,
+                                     ctypes.byref(k))
+    return st, {"kernel": k.value}
 
 
 def conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW):

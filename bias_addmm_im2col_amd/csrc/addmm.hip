@@ -553,6 +553,12 @@ hipError_t launch_addmm(const AddmmProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_conv2d_nhwc(const ConvProblem& q, hipStream_t stream) {
+  // the 3-channel 7x7 stride-4 stem has its own kernel (16-byte stores of
+  // four output channels need an aligned out as well)
+  const bool stem_aligned = ((uintptr_t)q.x & 15) == 0 && ((uintptr_t)q.w & 15) == 0 &&
+                            ((uintptr_t)q.out & 15) == 0;
+  if (plan_conv_stem(win_shape(q), stem_aligned, getenv("BAIM_CONV_WIN")))
+    return launch_conv2d_stem(q, true, stream);
   // out[B*OH*OW, OC] = im2col_nhwc(x)[B*OH*OW, KH*KW*IC] @ w[OC, KH*KW*IC]^T + bias
   AddmmProblem p;
   p.out = q.out;

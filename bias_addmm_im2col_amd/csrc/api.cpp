@@ -377,53 +377,86 @@ extern "C" baim_status sdpa_f32(float* out, const float* q, const float* k, cons
   return launched(baim::launch_sdpa(p, (hipStream_t)stream), "sdpa_f32");
 }
 
+// Size checks of a channels-last conv (as conv2d_nhwc_f32 applies them)
+// and its problem description without pointers.
+static baim_status nhwc_sizes(int64_t B, int64_t IC, int64_t H, int64_t W, int64_t OC, int64_t KH,
+                              int64_t KW, int64_t sH, int64_t sW, int64_t pH, int64_t pW,
+                              int64_t dH, int64_t dW, baim::ConvProblem* q, int64_t* n_x,
+                              int64_t* n_w, int64_t* n_out) {
+  if (B < 1 || IC < 1 || OC < 1)
+    return fail(BAIM_ERR_SHAPE, "conv2d_nhwc: B, IC and OC must be >= 1");
+  int64_t OH = 0, OW = 0;
+  const baim_status hs = baim_conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, &OH, &OW);
+  if (hs != BAIM_OK) return hs;  // message already set
+  *n_x = elems({B, H, W, IC});
+  *n_w = elems({OC, KH, KW, IC});
+  *n_out = elems({B, OH, OW, OC});
+  const int64_t K = elems({KH, KW, IC});
+  if (*n_x < 0 || *n_w < 0 || *n_out < 0 || *n_x >= kMaxElems || *n_w >= kMaxElems ||
+      *n_out >= kMaxElems)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: every tensor must have fewer than 2^31 elements");
+  if (*n_x >= kMaxConvInput)
+    return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: input must have fewer than 2^29 elements");
+  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: KH*KW*IC must be below 2^21");
+  if (OC >= kMaxAddmmN) return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: OC must be below 2^23");
+  q->out = nullptr;
+  q->x = nullptr;
+  q->w = nullptr;
+  q->bias = nullptr;
+  q->B = (int)B;
+  q->IC = (int)IC;
+  q->H = (int)H;
+  q->W = (int)W;
+  q->OC = (int)OC;
+  q->KH = (int)KH;
+  q->KW = (int)KW;
+  q->sH = (int)sH;
+  q->sW = (int)sW;
+  q->pH = (int)pH;
+  q->pW = (int)pW;
+  q->dH = (int)dH;
+  q->dW = (int)dW;
+  q->OH = (int)OH;
+  q->OW = (int)OW;
+  q->groups = 1;
+  return BAIM_OK;
+}
+
 extern "C" baim_status conv2d_nhwc_f32(float* out, const float* input, const float* weight,
                                        const float* bias, int64_t B, int64_t IC, int64_t H,
                                        int64_t W, int64_t OC, int64_t KH, int64_t KW, int64_t sH,
                                        int64_t sW, int64_t pH, int64_t pW, int64_t dH, int64_t dW,
                                        void* stream) {
   g_err.clear();
-  if (B < 1 || IC < 1 || OC < 1)
-    return fail(BAIM_ERR_SHAPE, "conv2d_nhwc: B, IC and OC must be >= 1");
-  int64_t OH = 0, OW = 0;
-  const baim_status hs = baim_conv2d_out_hw(H, W, KH, KW, sH, sW, pH, pW, dH, dW, &OH, &OW);
-  if (hs != BAIM_OK) return hs;  // message already set
-  const int64_t n_x = elems({B, H, W, IC}), n_w = elems({OC, KH, KW, IC});
-  const int64_t n_out = elems({B, OH, OW, OC}), K = elems({KH, KW, IC});
-  if (n_x < 0 || n_w < 0 || n_out < 0 || n_x >= kMaxElems || n_w >= kMaxElems ||
-      n_out >= kMaxElems)
-    return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: every tensor must have fewer than 2^31 elements");
-  if (n_x >= kMaxConvInput)
-    return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: input must have fewer than 2^29 elements");
-  if (K >= kMaxK) return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: KH*KW*IC must be below 2^21");
-  if (OC >= kMaxAddmmN) return fail(BAIM_ERR_TOO_LARGE, "conv2d_nhwc: OC must be below 2^23");
+  baim::ConvProblem q;
+  int64_t n_x = 0, n_w = 0, n_out = 0;
+  const baim_status st =
+      nhwc_sizes(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, &q, &n_x, &n_w, &n_out);
+  if (st != BAIM_OK) return st;
   if (!out || !input || !weight) return fail(BAIM_ERR_NULL, "conv2d_nhwc: out/input/weight is NULL");
   if (overlap(out, n_out, input, n_x) || overlap(out, n_out, weight, n_w) ||
       overlap(out, n_out, bias, OC))
     return fail(BAIM_ERR_ALIAS, "conv2d_nhwc: out overlaps an input");
-
-  baim::ConvProblem q;
   q.out = out;
   q.x = input;
   q.w = weight;
   q.bias = bias;
-  q.B = (int)B;
-  q.IC = (int)IC;
-  q.H = (int)H;
-  q.W = (int)W;
-  q.OC = (int)OC;
-  q.KH = (int)KH;
-  q.KW = (int)KW;
-  q.sH = (int)sH;
-  q.sW = (int)sW;
-  q.pH = (int)pH;
-  q.pW = (int)pW;
-  q.dH = (int)dH;
-  q.dW = (int)dW;
-  q.OH = (int)OH;
-  q.OW = (int)OW;
-  q.groups = 1;
   return launched(baim::launch_conv2d_nhwc(q, (hipStream_t)stream), "conv2d_nhwc_f32");
+}
+
+extern "C" baim_status baim_conv2d_nhwc_plan(int64_t B, int64_t IC, int64_t H, int64_t W,
+                                             int64_t OC, int64_t KH, int64_t KW, int64_t sH,
+                                             int64_t sW, int64_t pH, int64_t pW, int64_t dH,
+                                             int64_t dW, int* kernel) {
+  g_err.clear();
+  if (!kernel) return fail(BAIM_ERR_NULL, "baim_conv2d_nhwc_plan: kernel must not be NULL");
+  baim::ConvProblem q;
+  int64_t n_x = 0, n_w = 0, n_out = 0;
+  const baim_status st =
+      nhwc_sizes(B, IC, H, W, OC, KH, KW, sH, sW, pH, pW, dH, dW, &q, &n_x, &n_w, &n_out);
+  if (st != BAIM_OK) return st;
+  *kernel = baim::plan_conv_stem(baim::win_shape(q), true, getenv("BAIM_CONV_WIN")) ? 3 : 0;
+  return BAIM_OK;
 }
 
 extern "C" baim_status baim_conv_transpose2d_out_hw(int64_t H, int64_t W, int64_t KH, int64_t KW,

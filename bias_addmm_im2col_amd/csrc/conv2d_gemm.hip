@@ -345,7 +345,7 @@ hipError_t launch_conv2d(const ConvProblem& q, hipStream_t stream) {
   const char* wspec = getenv("BAIM_CONV_WIN");
   const WinPlan wp = plan_conv_window(win_shape(q), aligned, wspec);
   if (wp.geom >= 0) return launch_conv2d_window(q, wp, stream);
-  if (plan_conv_stem(win_shape(q), aligned, wspec)) return launch_conv2d_stem(q, stream);
+  if (plan_conv_stem(win_shape(q), aligned, wspec)) return launch_conv2d_stem(q, false, stream);
   ConvArgs a;
   a.out = q.out;
   a.x = q.x;

@@ -40,6 +40,14 @@
 // reaches only the outputs that read it.  Each of the 16 waves owns 16
 // output channels and 5 or 4 of the 9 blocks of 16 pixels: four waves to a
 // SIMD, independent accumulators.  The window sits first in LDS.
+//
+// Channels-last (x [B,H,W,IC], w [OC,KH,KW,IC], out [B,OH,OW,OC]) runs the
+// same kernel with three changes: the input columns of a row arrive
+// interleaved (IC floats per column), so each 16-byte load is split into
+// its (column, channel) slots of the same phase rows; the weight rows hold
+// the taps in (kh, kw, ic) order, which the tap table maps onto the window;
+// and a lane's four consecutive output channels of one pixel go out as one
+// 16-byte store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,6 +97,14 @@ template <class C>
 __host__ __device__ constexpr int stem_tap_off(int k) {
   return k >= C::K ? C::X_ROWS * C::Q
                    : (((k / C::KW) * C::S + (k % C::KW) % C::S) * C::Q + (k % C::KW) / C::S);
+}
+
+// The same for a channels-last weight row, tap k = (kh*KW + kw)*IC + ic.
+template <class C>
+__host__ __device__ constexpr int stem_tap_off_nhwc(int k) {
+  return k >= C::K ? C::X_ROWS * C::Q
+                   : stem_tap_off<C>(((k % C::IC) * C::KH + (k / C::IC) / C::KW) * C::KW +
+                                     (k / C::IC) % C::KW);
 }
 
 struct StemArgs {
@@ -149,6 +165,62 @@ struct StemXItems {
   }
 };
 
+// Channels-last input: item i covers float4 f of the interleaved span of
+// (kh, segment g), whose floats iw*IC + ic run over the segment's columns
+// [colA, colB) and every channel; row = kh*2 + g.  Rows W*IC floats long
+// (W % 4 == 0) start on 16-byte boundaries, so a float4 lies wholly inside
+// or wholly outside the row; outside ones load zeros.
+template <class C>
+struct StemXItemsNhwc {
+  static constexpr int F4 = (C::IC * (C::S * C::BN + C::KW - C::S) + 3) / 4 + 1;
+  static constexpr int NQ = (C::KH * 2 * F4 + C::NT - 1) / C::NT;
+  f32x4 v[NQ];
+  int row[NQ];  // kh*2 + g, or -1 (no item)
+  int fl[NQ];   // first float of the float4 within its input row
+
+  __device__ void load(const StemArgs& p, __amdgpu_buffer_rsrc_t xr, int b, int oh1, int n1,
+                       int n2, int colA1, int colA2) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = threadIdx.x + C::NT * q;
+      const int r = i / F4, f = i - r * F4;
+      const int g = r & 1, kh = r >> 1;
+      const int n = g ? n2 : n1;
+      const int ih = (oh1 + g) * C::S - p.pH + kh;
+      const int colA = g ? colA2 : colA1;
+      const int fA = colA * C::IC, fB = (colA + C::S * (n - 1) + C::KW) * C::IC;
+      const int f0 = fA >= 0 ? fA >> 2 : -((-fA + 3) >> 2);
+      const int c = (f0 + f) * 4;
+      const bool cover = kh < C::KH && n > 0 && c < fB && c + 4 > fA;
+      const bool ok = cover && ih >= 0 && ih < p.H && c >= 0 && c < p.W * C::IC;
+      row[q] = cover ? r : -1;
+      fl[q] = c;
+      const int off = ((b * p.H + ih) * p.W) * C::IC + c;
+      v[q] = Vec<4>::load(xr, ok ? (uint32_t)off * 4u : kOOB);
+    }
+  }
+  __device__ void store(float* Xs, int pW, int ow1, int n1, int n2, int seg2) const {
+    // a multiple of IC that makes every float index of the span >= 0
+    const int shift = C::IC * (pW + 4);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (row[q] < 0) continue;
+      const int g = row[q] & 1, kh = row[q] >> 1;
+      const int n = g ? n2 : n1;
+      const int owA = g ? 0 : ow1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int fs = fl[q] + e + shift;
+        const int ic = fs % C::IC;
+        const int u = fs / C::IC - 4;    // column in the padded image
+        const int rel = u - C::S * owA;  // within the segment's span
+        if (rel < 0 || rel >= C::S * (n - 1) + C::KW) continue;
+        Xs[((ic * C::KH + kh) * C::S + u % C::S) * C::Q + (g ? seg2 : 0) + rel / C::S] = v[q][e];
+      }
+    }
+  }
+};
+
 // Steps [S0, S1) for the wave's NB pixel blocks: lane group j takes tap
 // k = 4s + j, whose window offset it reads from the tap table.
 template <class C, int S0, int S1, int NB>
@@ -167,7 +239,7 @@ __device__ __forceinline__ void stem_mma(f32x4* acc, const float* Aw, const int*
   }
 }
 
-template <class C>
+template <class C, bool NHWC>
 __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   __shared__ __attribute__((aligned(16))) float smem[C::SMEM_FLOATS];
   float* Xs = smem;
@@ -201,9 +273,15 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   const int f0_1 = colA1 >= 0 ? colA1 >> 2 : -((-colA1 + 3) >> 2);
   const int f0_2 = colA2 >= 0 ? colA2 >> 2 : -((-colA2 + 3) >> 2);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, p.x_elems);
-  StemXItems<C> xi[C::IC];
+  StemXItems<C> xi[NHWC ? 1 : C::IC];
+  StemXItemsNhwc<C> xn;
+  if constexpr (NHWC) {
+    xn.load(p, xr, b, oh1, n1, n2, colA1, colA2);
+  } else {
 #pragma unroll
-  for (int ic = 0; ic < C::IC; ++ic) xi[ic].load(p, xr, b, ic, oh1, n1, n2, f0_1, f0_2, colA1, colA2);
+    for (int ic = 0; ic < C::IC; ++ic)
+      xi[ic].load(p, xr, b, ic, oh1, n1, n2, f0_1, f0_2, colA1, colA2);
+  }
 
   // 2. what no load writes: the zero row, the weight rows past OC with the
   // slack after the last row, and the tap table
@@ -213,7 +291,7 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
       reinterpret_cast<f32x4*>(Xs + C::X_ROWS * C::Q)[i] = z;
     const int za = ((C::BM - wrows) * C::AS + 16) / 4;
     for (int i = tid; i < za; i += C::NT) reinterpret_cast<f32x4*>(As + wrows * C::AS)[i] = z;
-    if (tid < C::T_INTS) Ts[tid] = stem_tap_off<C>(tid);
+    if (tid < C::T_INTS) Ts[tid] = NHWC ? stem_tap_off_nhwc<C>(tid) : stem_tap_off<C>(tid);
   }
   // 3. weights and input into LDS
 #pragma unroll
@@ -221,8 +299,12 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
     const int i = tid + C::NT * q;
     if (i * 4 < wcount) reinterpret_cast<f32x4*>(As)[i] = wv[q];
   }
+  if constexpr (NHWC) {
+    xn.store(Xs, p.pW, ow1, n1, n2, seg2);
+  } else {
 #pragma unroll
-  for (int ic = 0; ic < C::IC; ++ic) xi[ic].store(Xs, ic, p.pW, ow1, n1, n2, seg2);
+    for (int ic = 0; ic < C::IC; ++ic) xi[ic].store(Xs, ic, p.pW, ow1, n1, n2, seg2);
+  }
   __syncthreads();
 
   // 4. all of K: wave w computes pixel blocks [0, PBH) (w < 8) or [PBH, NPB)
@@ -245,9 +327,28 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
   else
     stem_mma<C, 0, C::KSTEPS, C::NPB - C::PBH>(acc, Aw, Tj, Xs, boff);
 
-  // 5. + bias, NCHW store: lane (pixel m, group j) holds output channels
+  // 5. + bias, store: lane (pixel m, group j) holds output channels
   // 4j .. 4j+3 of the wave's 16
   const int npix = n1 + n2;
+  if constexpr (NHWC) {
+    // [B, OH, OW, OC]: the four channels of one pixel are one 16-byte
+    // store (OC % 4 == 0: they are all inside or all past OC)
+    const int oc0 = m0 + ocb * 16 + 4 * j;
+    if (oc0 >= p.OC) return;
+    f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.bias) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[r] = p.bias[oc0 + r];
+    }
+    float* obn = p.out + ((size_t)b * p.P + p0) * p.OC + oc0;
+#pragma unroll
+    for (int pb = 0; pb < C::PBH; ++pb) {
+      const int t = 16 * (pb0 + pb) + m;
+      if (pb < nb && (npix == C::BN || t < npix))
+        *reinterpret_cast<f32x4*>(obn + (size_t)t * p.OC) = acc[pb] + bv;
+    }
+    return;
+  }
   float* ob = p.out + (size_t)b * p.OC * p.P + p0;
   if (m0 + C::BM <= p.OC && npix == C::BN) {
     // A whole tile: the four bias values first, then stores without the
@@ -281,7 +382,7 @@ __global__ __launch_bounds__(C::NT) void conv_stem_kernel(StemArgs p) {
 
 typedef StemCfg<3, 7, 7, 4> Stem3x7x7S4;
 
-hipError_t launch_conv2d_stem(const ConvProblem& q, hipStream_t stream) {
+hipError_t launch_conv2d_stem(const ConvProblem& q, bool nhwc, hipStream_t stream) {
   typedef Stem3x7x7S4 C;
   static_assert(C::IC == kStemIC && C::KH == kStemK && C::KW == kStemK && C::S == kStemS &&
                     C::BM == kStemBM && C::BN == kStemBN && C::NT == 64 * kStemWaves,
@@ -303,7 +404,10 @@ hipError_t launch_conv2d_stem(const ConvProblem& q, hipStream_t stream) {
   a.x_elems = q.B * q.IC * q.H * q.W;
   a.w_elems = q.OC * C::K;
   const dim3 grid(q.B * a.tpi, (q.OC + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL(conv_stem_kernel<C>, grid, dim3(C::NT), 0, stream, a);
+  if (nhwc)
+    hipLaunchKernelGGL((conv_stem_kernel<C, true>), grid, dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((conv_stem_kernel<C, false>), grid, dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 

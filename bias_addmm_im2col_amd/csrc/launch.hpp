@@ -70,14 +70,18 @@ inline WinShape win_shape(const ConvProblem& q) {
 }
 hipError_t launch_conv2d_window(const ConvProblem& p, const WinPlan& plan, hipStream_t stream);
 // The 3-channel 7x7 stride-4 stem (plan_conv_stem): one pass over K per
-// block of 128 output channels x 144 output pixels.
-hipError_t launch_conv2d_stem(const ConvProblem& p, hipStream_t stream);
+// block of 128 output channels x 144 output pixels; NCHW, or channels-last
+// (nhwc: x [B,H,W,IC], w [OC,KH,KW,IC], out [B,OH,OW,OC], out 16-byte
+// aligned).
+hipError_t launch_conv2d_stem(const ConvProblem& p, bool nhwc, hipStream_t stream);
 hipError_t launch_conv2d(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_conv2d_direct(const ConvProblem& p, hipStream_t stream);
 hipError_t launch_sdpa(const SdpaProblem& p, hipStream_t stream);
 hipError_t launch_conv_transpose2d(const ConvTProblem& p, hipStream_t stream);
 // Channels-last conv (groups == 1): x [B,H,W,IC], w [OC,KH,KW,IC],
-// out [B,OH,OW,OC]; the addmm kernels with an im2col A operand.
+// out [B,OH,OW,OC]; the stem kernel where plan_conv_stem takes the shape
+// (input, weight and out 16-byte aligned), else the addmm kernels with an
+// im2col A operand.
 hipError_t launch_conv2d_nhwc(const ConvProblem& p, hipStream_t stream);
 
 }  // namespace baim

@@ -305,6 +305,26 @@ baim_status baim_conv2d_plan(int64_t B, int64_t IC, int64_t H, int64_t W,
                              int* bn, int* bk, int* waves, int* kgroups,
                              int* splits, int* stream_blocks);
 
+/*
+ * baim_conv2d_nhwc_plan: which kernel conv2d_nhwc_f32 runs for a
+ * channels-last conv of these sizes on 16-byte aligned input, weight and
+ * out.  The conv page's motivating case, a 3-channel patch-embed stem ("et_vk
+ * conv2d: route standard (groups==1) conv through an im2col tiled GEMM",
+ * Problem paragraph), has a kernel of its own in this layout as well.
+ * Arguments as conv2d_nhwc_f32's sizes.  Writes *kernel:
+ *   0  the addmm kernels with an im2col A operand;
+ *   3  the stem kernel for 3-channel 7x7 stride-4 convs (dilation 1,
+ *      OW >= 144, W % 4 == 0, OC % 4 == 0), as baim_conv2d_plan's kernel 3.
+ * BAIM_CONV_WIN="off" declines kernel 3, as in the op.  Returns the status
+ * conv2d_nhwc_f32 would return for these sizes (SHAPE, TOO_LARGE), or
+ * BAIM_ERR_NULL if kernel is NULL.  Host-only; touches no GPU.
+ */
+baim_status baim_conv2d_nhwc_plan(int64_t B, int64_t IC, int64_t H, int64_t W,
+                                  int64_t OC, int64_t KH, int64_t KW,
+                                  int64_t sH, int64_t sW, int64_t pH,
+                                  int64_t pW, int64_t dH, int64_t dW,
+                                  int* kernel);
+
 /* Text describing the last error returned on the calling thread ("" if the
  * last call succeeded).  The pointer stays valid until the next call on the
  * same thread. */

@@ -136,3 +136,43 @@ def test_stride2_convs_take_the_window_kernel(monkeypatch):
     assert plan(4, 256, 57, 57, 256, s=2)["stream_blocks"] == 0
     monkeypatch.setenv("BAIM_CONV_WIN", "2")
     assert plan(4, 256, 57, 57, 256, s=2)["splits"] == 2
+
+
+def nhwc_plan(B, H, W, IC, OC, K=7, s=4, p=3, d=1):
+    st, pl = _capi.conv2d_nhwc_plan(B, IC, H, W, OC, K, K, s, s, p, p, d, d)
+    assert st == 0, _capi.last_error()
+    return pl["kernel"]
+
+
+def test_channels_last_stem_routing(monkeypatch):
+    """conv2d_nhwc_f32 takes the stem kernel under the NCHW stem's
+    conditions, and the im2col addmm kernels otherwise."""
+    assert nhwc_plan(1, 768, 768, 3, 128) == 3
+    assert nhwc_plan(1, 580, 580, 3, 128) == 3      # OW = 145
+    assert nhwc_plan(1, 580, 572, 3, 128) == 0      # OW = 143 < 144
+    assert nhwc_plan(1, 768, 766, 3, 128) == 0      # W % 4 != 0
+    assert nhwc_plan(1, 768, 768, 3, 126) == 0      # OC % 4 != 0
+    assert nhwc_plan(1, 768, 768, 4, 128) == 0      # 4 channels
+    assert nhwc_plan(1, 768, 768, 3, 128, s=2) == 0
+    assert nhwc_plan(1, 768, 768, 3, 128, d=2) == 0
+    assert nhwc_plan(2, 21, 18, 16, 70, K=3, s=1, p=1) == 0
+    monkeypatch.setenv("BAIM_CONV_WIN", "off")
+    assert nhwc_plan(1, 768, 768, 3, 128) == 0
+
+
+def test_gpu_channels_last_stem_shapes_are_planned_onto_the_stem_kernel():
+    from tests.test_parity_conv_stem import SHAPES
+    for B, H, W, OC, pad, _ in SHAPES:
+        pH, pW = (pad, pad) if isinstance(pad, int) else pad
+        st, pl = _capi.conv2d_nhwc_plan(B, 3, H, W, OC, 7, 7, 4, 4, pH, pW, 1, 1)
+        assert st == 0 and pl["kernel"] == 3, (B, H, W, OC, pad)
+
+
+def test_channels_last_plan_rejects_like_the_op():
+    st, _ = _capi.conv2d_nhwc_plan(1, 4, 5, 5, 8, 7, 7, 1, 1, 0, 0, 1, 1)  # kernel larger than input
+    assert st == 2
+    st, _ = _capi.conv2d_nhwc_plan(0, 3, 768, 768, 128, 7, 7, 4, 4, 3, 3, 1, 1)
+    assert st == 2
+    import ctypes
+    assert _capi.lib().baim_conv2d_nhwc_plan(1, 3, 768, 768, 128, 7, 7, 4, 4, 3, 3, 1, 1,
+                                             ctypes.cast(None, ctypes.POINTER(ctypes.c_int))) == 1
