@@ -155,11 +155,14 @@ __global__ __launch_bounds__(256) void conv_dw_rows_kernel(ConvDirectArgs p, uin
   if (!live) return;
   const float bv = p.bias ? p.bias[oc] : 0.0f;
   float* o = p.out + (size_t)plane * p.OH * p.OW;
+  // the output is written once and not read back here: non-temporal
+  // stores (5.97 -> 5.42 us on [4,256,56,56]; four output rows per thread
+  // instead of two measured 6.6)
 #pragma unroll
   for (int oy = 0; oy < OR; ++oy)
     if (oh0 + oy < p.OH) {
       const f32x4 v = {acc[oy][0] + bv, acc[oy][1] + bv, acc[oy][2] + bv, acc[oy][3] + bv};
-      *reinterpret_cast<f32x4*>(o + (oh0 + oy) * p.OW + ow0) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o + (oh0 + oy) * p.OW + ow0));
     }
 }
 
