@@ -192,7 +192,8 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
   if (epi == EPI_STORE && m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
     // A whole tile: per 32-row block the bias values first, then stores
     // without tests (the grouped 3x3 conv with 8 groups of 32 channels:
-    // 42.4 -> 39.5 us).
+    // 42.4 -> 39.5 us), non-temporal since nothing reads them back (38.9 ->
+    // 37.8 us).
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       float bv[16];
@@ -204,7 +205,7 @@ __device__ __forceinline__ void conv_piece(const ConvArgs& p, float* smem, int m
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ocx = g * p.OCg + m0 + ws.wm0 + 32 * i + acc_row(r, lane);
-          p.out[obase[j] + (size_t)ocx * P] = acc.c[i][j][r] + bv[r];
+          __builtin_nontemporal_store(acc.c[i][j][r] + bv[r], &p.out[obase[j] + (size_t)ocx * P]);
         }
     }
     return;
