@@ -122,6 +122,8 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
     // A whole tile with self [N]: no bounds tests and no mode choice per
     // element (with them, the epilogue cost 3.7 us of the 4096 x 4096 x
     // 1024 down-projection and 3.3 us of the 2048 x 768 x 3072 FFN).
+    // Non-temporal: the output is not read back (FFN 80 -> 77 us; the
+    // 256x256 kernel's stores got slower that way and stay plain).
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -131,13 +133,14 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + ws.wm0 + 32 * i + acc_row(r, lane);
-          p.out[(size_t)m * p.N + n] = fmaf(p.alpha, acc.c[i][j][r], bs);
+          __builtin_nontemporal_store(fmaf(p.alpha, acc.c[i][j][r], bs), &p.out[(size_t)m * p.N + n]);
         }
       }
     return;
   }
   if (epi == EPI_STORE && p.self_mode == 2 && m0 + T::BM <= p.M && n0 + T::BN <= p.N) {
-    // the same with a full self (ragged-577 addmm 56.8 -> 55.6 us)
+    // the same with a full self (ragged-577 addmm 56.8 -> 55.6 us; 55.0
+    // -> 54.4 us with non-temporal stores)
 #pragma unroll
     for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -147,7 +150,7 @@ __device__ __forceinline__ void addmm_piece(const AddmmArgs& p, float* smem, int
         for (int r = 0; r < 16; ++r) {
           const size_t o = (size_t)(m0 + ws.wm0 + 32 * i + acc_row(r, lane)) * p.N + n;
           const float s = (kSelfAhead && self_ahead) ? sv[r] : p.self[o];
-          p.out[o] = fmaf(p.alpha, acc.c[i][j][r], p.beta * s);
+          __builtin_nontemporal_store(fmaf(p.alpha, acc.c[i][j][r], p.beta * s), &p.out[o]);
         }
       }
     return;
