@@ -178,7 +178,13 @@ class Case:
             self.x, self.w, self.bias = x.cuda(), w.cuda(), bias.cuda()
             OH, OW = c.out_hw()
             self.out = torch.empty((c.B, c.OC, OH, OW), dtype=torch.float32, device="cuda")
-            self.kernel = "baim::conv_transpose_kernel"
+            # the one-GEMM path takes kernel == stride, no padding, no output
+            # padding, 128 | H*W and 4 | (OC/groups)*KH*KW (aligned tensors);
+            # the rest run one GEMM per output phase
+            fused = ((c.KH, c.KW) == tuple(c.stride) and tuple(c.padding) == (0, 0)
+                     and tuple(c.output_padding) == (0, 0) and (c.H * c.W) % 128 == 0
+                     and (c.OC * c.KH * c.KW) % 4 == 0)
+            self.kernel = "baim::convt_fused_kernel" if fused else "baim::conv_transpose_kernel"
             self.run = lambda: baim.conv_transpose2d_f32(self.out, self.x, self.w, self.bias,
                                                          c.stride, c.padding, c.output_padding,
                                                          1, c.dilation)
