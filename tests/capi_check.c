@@ -223,6 +223,37 @@ static void test_sdpa(void) {
   free(q), free(k), free(v), free(mask), free(ref), free(err);
 }
 
+/* The host-only plan queries: the stem shape takes the stem kernel in both
+ * layouts, a NULL output pointer is refused. */
+static void test_plans(void) {
+  int bm = 0, bn = 0, bk = 0, waves = 0, kg = 0, splits = 0, sb = 0, kernel = -1;
+  check_status("baim_gemm_plan",
+               baim_gemm_plan(4096, 1024, 4096, &bm, &bn, &bk, &waves, &kg, &splits, &sb),
+               BAIM_OK);
+  if (bm < 32 || bn < 32 || waves < 4) {
+    printf("FAIL baim_gemm_plan: %d x %d, %d waves\n", bm, bn, waves);
+    ++failures;
+  }
+  check_status("baim_conv2d_plan",
+               baim_conv2d_plan(1, 3, 768, 768, 128, 7, 7, 4, 4, 3, 3, 1, 1, 1, &kernel, &bm, &bn,
+                                &bk, &waves, &kg, &splits, &sb),
+               BAIM_OK);
+  if (kernel != 3) {
+    printf("FAIL baim_conv2d_plan: stem shape planned on kernel %d\n", kernel);
+    ++failures;
+  }
+  kernel = -1;
+  check_status("baim_conv2d_nhwc_plan",
+               baim_conv2d_nhwc_plan(1, 3, 768, 768, 128, 7, 7, 4, 4, 3, 3, 1, 1, &kernel), BAIM_OK);
+  if (kernel != 3) {
+    printf("FAIL baim_conv2d_nhwc_plan: stem shape planned on kernel %d\n", kernel);
+    ++failures;
+  }
+  check_status("baim_conv2d_nhwc_plan NULL",
+               baim_conv2d_nhwc_plan(1, 3, 768, 768, 128, 7, 7, 4, 4, 3, 3, 1, 1, NULL),
+               BAIM_ERR_NULL);
+}
+
 int main(void) {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
@@ -233,6 +264,7 @@ int main(void) {
   test_addmm();
   test_convs();
   test_sdpa();
+  test_plans();
   if (failures) {
     printf("capi_check: %d FAILED\n", failures);
     return 1;
